@@ -45,6 +45,7 @@ def lib():
         L.orc_double_to_bf16.argtypes = [D]; L.orc_double_to_bf16.restype = ctypes.c_uint16
         L.orc_fp4_row_element.argtypes = [P, I]; L.orc_fp4_row_element.restype = D
         L.orc_fp4_table.argtypes = [P]; L.orc_fp4_table.restype = None
+        L.orc_fp4_decode_rows.argtypes = [P, I64, I64, P]; L.orc_fp4_decode_rows.restype = None
         L.orc_e4m3_table.argtypes = [P]; L.orc_e4m3_table.restype = None
         L.orc_build_idx.argtypes = [I, P, P, I, P, I64, I, P, I64, I, P, I64, P, I64]
         L.orc_build_idx.restype = I
@@ -111,12 +112,7 @@ def fp4_rows_decode(rows: torch.Tensor) -> np.ndarray:
     rows = _cpu(rows, torch.int32)
     n = rows.shape[0]
     out = np.zeros((n, 128), dtype=np.float64)
-    L = lib()
-    base = rows.data_ptr()
-    stride = rows.stride(0) * 4
-    for i in range(n):
-        for d in range(128):
-            out[i, d] = L.orc_fp4_row_element(ctypes.c_void_p(base + i * stride), d)
+    lib().orc_fp4_decode_rows(_p(rows), n, rows.stride(0), out.ctypes.data_as(ctypes.c_void_p))
     return out
 
 

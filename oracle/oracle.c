@@ -133,6 +133,14 @@ double orc_fp4_row_element(const int32_t *row, int d)
     return orc_bf16_to_double(orc_double_to_bf16(v));
 }
 
+/* Decode n packed rows (row_words words apart) into out[n][128]. */
+void orc_fp4_decode_rows(const int32_t *rows, int64_t n, int64_t row_words, double *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        for (int d = 0; d < 128; ++d)
+            out[i * 128 + d] = orc_fp4_row_element(rows + i * row_words, d);
+}
+
 /* The 256 x 256 dequant table: entry [code_byte][scale_byte][j] for the two
  * nibbles j = 0 (low), 1 (high) of code_byte, as bf16 bits. */
 void orc_fp4_table(uint16_t *out /* [256*256*2] */)

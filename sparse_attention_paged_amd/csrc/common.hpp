@@ -1,0 +1,53 @@
+// common.hpp -- device-side building blocks shared by the gfx950 kernels:
+// vector types, MFMA wrappers, wavefront shuffles and bf16 conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sap {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D = A * B + C on a 16x16 tile with a 32-deep reduction.  Lane l holds
+// A[m = l%16][k = 8(l/16) .. +7], B[k = 8(l/16) .. +7][n = l%16] and
+// D[m = 4(l/16) + i][n = l%16] for i = 0..3.
+__device__ __forceinline__ f32x4 mfma16x16x32(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// D = A * B + C on a 32x32 tile with a 16-deep reduction.  Lane l holds
+// A[m = l%32][k = 8(l/32) .. +7], B[k = 8(l/32) .. +7][n = l%32] and
+// D[m = 8(i/4) + 4(l/32) + i%4][n = l%32] for i = 0..15.
+__device__ __forceinline__ f32x16 mfma32x32x16(uint4 a, uint4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+__device__ __forceinline__ int shfl_xor(int v, int mask) { return __shfl_xor(v, mask, kWave); }
+
+// float -> bf16 bits, round to nearest even (hardware conversion)
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+    __bf16 b = (__bf16)x;
+    return (uint32_t)__builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return bf16_bits(lo) | (bf16_bits(hi) << 16);
+}
+
+// byte-select permute of two dwords: selector bytes 0-3 pick from `lo`,
+// 4-7 from `hi`
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace sap

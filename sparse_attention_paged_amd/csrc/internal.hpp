@@ -1,0 +1,86 @@
+// internal.hpp -- parameter blocks and launchers shared between the C-ABI
+// layer (sap_abi.hip) and the kernel translation units.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sap {
+
+constexpr int kAttnTile = 32;        // gathered columns per LDS tile
+constexpr int kAttnHeadsPerBlock = 64;
+
+struct AttnParams {
+    const uint16_t *q;               // bf16 [T, H, D]
+    int64_t q_st, q_sh;              // element strides
+    const uint8_t *win;              // pool bases and row strides (bytes)
+    const uint8_t *cmp;
+    int64_t win_rs, cmp_rs;
+    const float *win_scale, *cmp_scale;
+    const int32_t *idx;
+    int64_t idx_st;
+    int n_win, n_cols;
+    void *out;
+    int64_t out_st, out_sh;
+    int T, H;
+    float sm_scale_log2;             // sm_scale * log2(e)
+    int num_splits, cols_per_split;  // cols_per_split: multiple of kAttnTile
+    float *part_o;                   // [T, S, H, D] unnormalised partial outputs
+    float *part_ml;                  // [T, S, H, 2] running max (log2 domain), sum
+};
+
+// kv: 0 = bf16, 2 = e4m3.  out: 0 = bf16, 1 = f32.
+hipError_t launch_attn(const AttnParams &p, int D, int kv, int out_dtype, hipStream_t s);
+hipError_t launch_attn_merge(const AttnParams &p, int D, int out_dtype, hipStream_t s);
+
+struct IndexerParams {
+    const uint16_t *q;               // bf16 [B, Hi, 128]
+    int64_t q_sb;
+    const float *w;
+    int64_t w_sb;
+    const int32_t *pool;
+    int64_t row_words;
+    const int32_t *pt;               // may be null
+    int64_t pt_sb;
+    int page;
+    const int32_t *n_keys;           // may be null
+    float *logits;
+    int64_t logits_sb;
+    int B, Hi, N;
+    int tiles_per_wave;
+};
+hipError_t launch_indexer(const IndexerParams &p, hipStream_t s);
+
+struct TopkParams {
+    const float *x;
+    int64_t x_sb;
+    const int32_t *n_valid;
+    int B, N, k;
+    int32_t *out;
+    int64_t out_sb;
+    void *workspace;                 // 2 * topk_slot_bytes(B, N, k) bytes
+};
+size_t topk_slot_bytes(int B, int N, int k);   // one of the two ping-pong halves
+hipError_t launch_topk(const TopkParams &p, hipStream_t s);
+
+struct IdxBuildParams {
+    const int32_t *pos, *seq;
+    int T, n_win;
+    const int32_t *win_pt;
+    int64_t win_pt_sb;
+    int page;
+    const int32_t *cmp_logical;
+    int64_t cmp_logical_st;
+    int n_cmp;
+    const int32_t *cmp_pt;
+    int64_t cmp_pt_sb;
+    int32_t *idx;
+    int64_t idx_st;
+};
+hipError_t launch_build_idx(const IdxBuildParams &p, hipStream_t s);
+
+hipError_t launch_debug_e4m3(uint16_t *out, float *fold, hipStream_t s);
+hipError_t launch_debug_fp4(uint16_t *out, hipStream_t s);
+
+}  // namespace sap

@@ -1,0 +1,277 @@
+// sap_abi.hip -- the C ABI declared in include/sap.h: argument validation
+// (every check runs on the host before any HIP call, so a rejected call
+// launches nothing and touches no device), split planning, workspace sizing
+// and kernel dispatch onto the caller's stream.
+#include "sap.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.hpp"
+
+namespace {
+
+inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+inline int dtype_size(int dt) { return dt == SAP_BF16 ? 2 : dt == SAP_F32 ? 4 : dt == SAP_FP8_E4M3 ? 1 : 0; }
+
+struct SplitPlan {
+    int splits;
+    int cols_per_split;
+};
+
+// Splitting a token's columns buys parallelism for decode, where a few tokens
+// would otherwise occupy a few CUs; each split costs a partial output of H*D
+// floats, so prefill-sized batches keep one split.
+SplitPlan plan_splits(int T, int H, int n_cols, int requested)
+{
+    const int tiles = n_cols > 0 ? (n_cols + sap::kAttnTile - 1) / sap::kAttnTile : 1;
+    int s;
+    if (requested >= 1) {
+        s = requested;
+    } else {
+        const int hb = (H + sap::kAttnHeadsPerBlock - 1) / sap::kAttnHeadsPerBlock;
+        const int64_t wgs = (int64_t)T * hb;
+        s = wgs >= 128 ? 1 : (int)((160 + wgs - 1) / wgs);
+    }
+    if (s > tiles) s = tiles;
+    if (s < 1) s = 1;
+    const int tiles_per = (tiles + s - 1) / s;
+    SplitPlan p;
+    p.cols_per_split = tiles_per * sap::kAttnTile;
+    p.splits = n_cols > 0 ? (n_cols + p.cols_per_split - 1) / p.cols_per_split : 1;
+    return p;
+}
+
+size_t attn_ws_bytes(int T, int H, int D, const SplitPlan &sp)
+{
+    if (sp.splits <= 1) return 0;
+    const size_t slots = (size_t)T * sp.splits * H;
+    return align256(slots * D * 4) + align256(slots * 2 * 4);
+}
+
+inline int launched(hipError_t e) { return e == hipSuccess ? SAP_OK : SAP_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int sap_version(void) { return 100; }
+
+const char *sap_status_string(int status)
+{
+    switch (status) {
+    case SAP_OK: return "ok";
+    case SAP_ERR_NULL: return "a required pointer is NULL";
+    case SAP_ERR_ALIGN: return "a base address or row stride breaks the alignment contract";
+    case SAP_ERR_SHAPE: return "a size, stride or count is out of range";
+    case SAP_ERR_DTYPE: return "unsupported element type";
+    case SAP_ERR_WORKSPACE: return "workspace missing or too small";
+    case SAP_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int sap_build_sparse_idx(const int32_t *pos, const int32_t *seq, int T, int n_win,
+                         const int32_t *win_pt, int64_t win_pt_stride, int page,
+                         const int32_t *cmp_logical, int64_t cmp_logical_stride, int n_cmp,
+                         const int32_t *cmp_pt, int64_t cmp_pt_stride,
+                         int32_t *idx, int64_t idx_stride, sap_stream_t stream)
+{
+    if (T < 0 || n_win < 0 || n_cmp < 0 || page <= 0) return SAP_ERR_SHAPE;
+    if ((int64_t)n_win + n_cmp > (1 << 20)) return SAP_ERR_SHAPE;
+    if (T == 0 || n_win + n_cmp == 0) return SAP_OK;
+    if (!pos || !seq || !idx) return SAP_ERR_NULL;
+    if (n_win > 0 && !win_pt) return SAP_ERR_NULL;
+    if (n_cmp > 0 && (!cmp_logical || !cmp_pt)) return SAP_ERR_NULL;
+    if (idx_stride < n_win + n_cmp || win_pt_stride < 0 || cmp_pt_stride < 0) return SAP_ERR_SHAPE;
+    if (n_cmp > 0 && cmp_logical_stride < n_cmp) return SAP_ERR_SHAPE;
+    sap::IdxBuildParams p{};
+    p.pos = pos;
+    p.seq = seq;
+    p.T = T;
+    p.n_win = n_win;
+    p.win_pt = win_pt;
+    p.win_pt_sb = win_pt_stride;
+    p.page = page;
+    p.cmp_logical = cmp_logical;
+    p.cmp_logical_st = cmp_logical_stride;
+    p.n_cmp = n_cmp;
+    p.cmp_pt = cmp_pt;
+    p.cmp_pt_sb = cmp_pt_stride;
+    p.idx = idx;
+    p.idx_st = idx_stride;
+    return launched(sap::launch_build_idx(p, (hipStream_t)stream));
+}
+
+int sap_sparse_attn_num_splits(int T, int H, int D, int n_cols, int num_splits)
+{
+    (void)D;
+    if (T < 0 || H < 1 || n_cols < 0 || num_splits < 0) return SAP_ERR_SHAPE;
+    return plan_splits(T, H, n_cols, num_splits).splits;
+}
+
+size_t sap_sparse_attn_workspace_bytes(int T, int H, int D, int n_cols, int num_splits)
+{
+    if (T <= 0 || H < 1 || D < 1 || n_cols < 0 || num_splits < 0) return 0;
+    return attn_ws_bytes(T, H, D, plan_splits(T, H, n_cols, num_splits));
+}
+
+int sap_sparse_attn_paged(const void *q, sap_dtype q_dtype, int64_t q_stride_t, int64_t q_stride_h,
+                          const void *win_pool, int64_t win_row_stride_bytes,
+                          const void *cmp_pool, int64_t cmp_row_stride_bytes,
+                          sap_dtype kv_dtype,
+                          const int32_t *idx, int64_t idx_stride, int n_win, int n_cmp,
+                          const float *win_scale, const float *cmp_scale,
+                          void *out, sap_dtype out_dtype, int64_t out_stride_t, int64_t out_stride_h,
+                          int T, int H, int D, float sm_scale, int num_splits,
+                          void *workspace, size_t workspace_bytes, sap_stream_t stream)
+{
+    if (T < 0 || H < 1 || n_win < 0 || n_cmp < 0 || num_splits < 0) return SAP_ERR_SHAPE;
+    if (D != 64 && D != 128 && D != 256 && D != 512) return SAP_ERR_SHAPE;
+    const int C = n_win + n_cmp;
+    if (C > 65536) return SAP_ERR_SHAPE;
+    if (q_dtype != SAP_BF16) return SAP_ERR_DTYPE;
+    if (kv_dtype != SAP_BF16 && kv_dtype != SAP_FP8_E4M3) return SAP_ERR_DTYPE;
+    if (out_dtype != SAP_F32 && out_dtype != SAP_BF16) return SAP_ERR_DTYPE;
+    if (T == 0) return SAP_OK;
+    if (!q || !out) return SAP_ERR_NULL;
+    if (C > 0 && !idx) return SAP_ERR_NULL;
+    if (n_win > 0 && !win_pool) return SAP_ERR_NULL;
+    if (n_cmp > 0 && !cmp_pool) return SAP_ERR_NULL;
+    if (kv_dtype == SAP_FP8_E4M3 && ((n_win > 0 && !win_scale) || (n_cmp > 0 && !cmp_scale))) return SAP_ERR_NULL;
+    if (C > 0 && idx_stride < C) return SAP_ERR_SHAPE;
+    if (q_stride_t < 0 || q_stride_h < 0 || out_stride_t < 0 || out_stride_h < 0) return SAP_ERR_SHAPE;
+    const int kvb = dtype_size(kv_dtype), ob = dtype_size(out_dtype);
+    // 16-byte vector loads and stores of q, out and pool rows
+    if (!aligned(q, 16) || (q_stride_t * 2) % 16 || (q_stride_h * 2) % 16) return SAP_ERR_ALIGN;
+    if (!aligned(out, 16) || (out_stride_t * ob) % 16 || (out_stride_h * ob) % 16) return SAP_ERR_ALIGN;
+    if (n_win > 0) {
+        if (!aligned(win_pool, 16) || win_row_stride_bytes % 16) return SAP_ERR_ALIGN;
+        if (win_row_stride_bytes < (int64_t)D * kvb) return SAP_ERR_SHAPE;
+    }
+    if (n_cmp > 0) {
+        if (!aligned(cmp_pool, 16) || cmp_row_stride_bytes % 16) return SAP_ERR_ALIGN;
+        if (cmp_row_stride_bytes < (int64_t)D * kvb) return SAP_ERR_SHAPE;
+    }
+    const SplitPlan sp = plan_splits(T, H, C, num_splits);
+    if ((int64_t)T * sp.splits >= (int64_t)1 << 31) return SAP_ERR_SHAPE;
+    const size_t need = attn_ws_bytes(T, H, D, sp);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return SAP_ERR_WORKSPACE;
+
+    sap::AttnParams p{};
+    p.q = (const uint16_t *)q;
+    p.q_st = q_stride_t;
+    p.q_sh = q_stride_h;
+    p.win = (const uint8_t *)win_pool;
+    p.cmp = (const uint8_t *)(n_cmp > 0 ? cmp_pool : win_pool);
+    p.win_rs = win_row_stride_bytes;
+    p.cmp_rs = n_cmp > 0 ? cmp_row_stride_bytes : win_row_stride_bytes;
+    p.win_scale = win_scale;
+    p.cmp_scale = cmp_scale;
+    p.idx = idx;
+    p.idx_st = idx_stride;
+    p.n_win = n_win;
+    p.n_cols = C;
+    p.out = out;
+    p.out_st = out_stride_t;
+    p.out_sh = out_stride_h;
+    p.T = T;
+    p.H = H;
+    p.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+    p.num_splits = sp.splits;
+    p.cols_per_split = sp.cols_per_split;
+    if (sp.splits > 1) {
+        const size_t slots = (size_t)T * sp.splits * H;
+        p.part_o = (float *)workspace;
+        p.part_ml = (float *)((uint8_t *)workspace + align256(slots * D * 4));
+    }
+    const int kv = kv_dtype == SAP_FP8_E4M3 ? 2 : 0;
+    const int od = out_dtype == SAP_F32 ? 1 : 0;
+    hipError_t e = sap::launch_attn(p, D, kv, od, (hipStream_t)stream);
+    if (e == hipSuccess && sp.splits > 1) e = sap::launch_attn_merge(p, D, od, (hipStream_t)stream);
+    return launched(e);
+}
+
+int sap_indexer_logits_packed(const void *q, int64_t q_stride_b,
+                              const float *w, int64_t w_stride_b,
+                              const int32_t *key_pool, int64_t key_row_words,
+                              const int32_t *page_table, int64_t pt_stride_b, int page,
+                              const int32_t *n_keys,
+                              float *logits, int64_t logits_stride_b,
+                              int B, int Hi, int D, int N, sap_stream_t stream)
+{
+    if (B < 0 || N < 0 || Hi < 1 || Hi > 32 || D != 128) return SAP_ERR_SHAPE;
+    if (key_row_words < 17) return SAP_ERR_SHAPE;
+    if (page_table && page < 1) return SAP_ERR_SHAPE;
+    if (B == 0 || N == 0) return SAP_OK;
+    if (!q || !w || !key_pool || !logits) return SAP_ERR_NULL;
+    if (q_stride_b < 0 || w_stride_b < 0 || pt_stride_b < 0 || logits_stride_b < N) return SAP_ERR_SHAPE;
+    if (!aligned(key_pool, 4)) return SAP_ERR_ALIGN;
+    if (!aligned(q, 16) || (q_stride_b * 2) % 16) return SAP_ERR_ALIGN;
+    if (!aligned(w, 4) || !aligned(logits, 4)) return SAP_ERR_ALIGN;
+    sap::IndexerParams p{};
+    p.q = (const uint16_t *)q;
+    p.q_sb = q_stride_b;
+    p.w = w;
+    p.w_sb = w_stride_b;
+    p.pool = key_pool;
+    p.row_words = key_row_words;
+    p.pt = page_table;
+    p.pt_sb = pt_stride_b;
+    p.page = page_table ? page : 1;
+    p.n_keys = n_keys;
+    p.logits = logits;
+    p.logits_sb = logits_stride_b;
+    p.B = B;
+    p.Hi = Hi;
+    p.N = N;
+    const int64_t tiles = ((int64_t)N + 63) / 64 * B;
+    p.tiles_per_wave = (int)((tiles + 4095) / 4096);
+    if (p.tiles_per_wave < 1) p.tiles_per_wave = 1;
+    return launched(sap::launch_indexer(p, (hipStream_t)stream));
+}
+
+size_t sap_topk_workspace_bytes(int B, int N, int k)
+{
+    if (B <= 0 || N <= 0 || k < 1 || k > 4096) return 0;
+    return 2 * sap::topk_slot_bytes(B, N, k);
+}
+
+int sap_topk_select(const float *logits, int64_t stride_b, const int32_t *n_valid,
+                    int B, int N, int k, int32_t *out_idx, int64_t out_stride_b,
+                    void *workspace, size_t workspace_bytes, sap_stream_t stream)
+{
+    if (B < 0 || N < 0 || k < 1 || k > 4096) return SAP_ERR_SHAPE;
+    if (B == 0) return SAP_OK;
+    if (!out_idx || (N > 0 && !logits)) return SAP_ERR_NULL;
+    if (out_stride_b < k || (N > 0 && stride_b < N)) return SAP_ERR_SHAPE;
+    if (!aligned(out_idx, 4) || (logits && !aligned(logits, 4))) return SAP_ERR_ALIGN;
+    const size_t need = sap_topk_workspace_bytes(B, N, k);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return SAP_ERR_WORKSPACE;
+    sap::TopkParams p{};
+    p.x = logits;
+    p.x_sb = stride_b;
+    p.n_valid = n_valid;
+    p.B = B;
+    p.N = N;
+    p.k = k;
+    p.out = out_idx;
+    p.out_sb = out_stride_b;
+    p.workspace = workspace;
+    return launched(sap::launch_topk(p, (hipStream_t)stream));
+}
+
+int sap_debug_e4m3_table(uint16_t *out, float *fold_factor, sap_stream_t stream)
+{
+    if (!out || !fold_factor) return SAP_ERR_NULL;
+    return launched(sap::launch_debug_e4m3(out, fold_factor, (hipStream_t)stream));
+}
+
+int sap_debug_fp4_table(uint16_t *out, sap_stream_t stream)
+{
+    if (!out) return SAP_ERR_NULL;
+    return launched(sap::launch_debug_fp4(out, (hipStream_t)stream));
+}
+
+}  // extern "C"

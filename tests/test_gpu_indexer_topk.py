@@ -1,0 +1,160 @@
+"""GPU parity of the fp4 indexer logits and the exact top-k selection, and
+the small end-to-end chain indexer -> top-k -> index build -> attention.
+
+The indexer reads fp4_e8m0_b32 key rows ('perf(kernel): read dsv41 indexer
+key rows as int32 words', Changes; Kernel time: 32 index heads, head_dim
+128, decode at contexts of 32768 and 131072, B 1 and 4).
+
+Logit tolerance: each head's dot product sums 128 exact bf16 x bf16
+products in fp32 and the head sum adds 32 fp32 terms, so the rounding error
+is below (128 + 32) * 2^-24 < 1e-5 of M = sum_h |w_h| sum_d |q_hd k_d|.
+Top-k is compared bit for bit when both sides select from the same fp32
+logits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_paged_amd as sap
+import workloads as W
+from gpu_helpers import assert_attn_close, dev, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _magnitude(case, rows_sel=None):
+    """M[b, n] = sum_h |w_bh| sum_d |q_bhd k_nd| with keys decoded by the oracle."""
+    B, N = case.q.shape[0], case.N
+    M = np.zeros((B, N))
+    for b in range(B):
+        prow = (case.page_table[b].to(torch.int64).repeat_interleave(case.page) * case.page
+                + torch.arange(case.page).repeat(case.page_table.shape[1]))[:N]
+        k = np.abs(oracle.fp4_rows_decode(case.key_pool[prow]))            # [N, 128]
+        q = np.abs(case.q[b].to(torch.float64).numpy())                     # [Hi, 128]
+        w = np.abs(case.w[b].to(torch.float64).numpy())
+        M[b] = (q @ k.T * w[:, None]).sum(0)
+    return M
+
+
+def _check_logits(got, ref, M, label):
+    g = got.cpu().to(torch.float64).numpy()
+    r = ref.numpy()
+    inf = np.isinf(r)
+    assert np.array_equal(np.isinf(g), inf) and (g[inf] < 0).all(), f"{label}: -inf pattern"
+    err = np.abs(g[~inf] - r[~inf])
+    bound = 1e-5 * M[~inf] + 1e-30
+    worst = float((err / bound).max()) if err.size else 0.0
+    say(f"  {label}: worst error / bound = {worst:.3f}")
+    assert worst <= 1.0, label
+
+
+def _gpu_logits(case):
+    out = sap.indexer_logits_packed(dev(case.q), dev(case.w), dev(case.key_pool), dev(case.page_table), case.page,
+                                    case.N, n_keys=dev(case.n_keys))
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("B,N,n_keys", [(1, 8192, None), (4, 2000, [2000, 1999, 1000, 1]), (2, 333, [333, 0])])
+def test_indexer_logits_small(B, N, n_keys):
+    need_gpu()
+    case = W.indexer_case(B=B, N=N, seed=W.SEED_BASE + 500 + B + N, n_keys=n_keys)
+    got = _gpu_logits(case)
+    ref = oracle.case_indexer(case)
+    _check_logits(got, ref, _magnitude(case), f"indexer B{B} N{N}")
+
+
+def test_indexer_logits_context_131072_b1():
+    need_gpu()
+    case = W.indexer_case(B=1, N=131072)
+    got = _gpu_logits(case)
+    ref = oracle.case_indexer(case)
+    _check_logits(got, ref, _magnitude(case), "indexer B1 N131072")
+
+
+def test_indexer_extreme_scales_and_strides():
+    # scale bytes across the whole range (the table test covers the decode;
+    # here the rows go through the kernel), rows with extra words, no page table
+    need_gpu()
+    g = W.make_generator(W.SEED_BASE + 520)
+    B, N = 2, 256
+    rows = W.fp4_key_rows(B * N, g, exp_lo=100, exp_hi=150, row_words=20)
+    q = (torch.randn((B, 32, 128), generator=g)).to(torch.bfloat16)
+    w = torch.rand((B, 32), generator=g)
+    got = sap.indexer_logits_packed(dev(q), dev(w), dev(rows), None, 64, N)
+    torch.cuda.synchronize()
+    ref = oracle.indexer_logits(q, w, rows, None, 64, None, N)
+    k = np.abs(oracle.fp4_rows_decode(rows)).reshape(B, N, 128)
+    M = np.stack([(np.abs(q[b].double().numpy()) @ k[b].T * w[b].double().numpy()[:, None]).sum(0)
+                  for b in range(B)])
+    _check_logits(got, ref, M, "indexer strided rows, no page table")
+    # fewer than 32 heads
+    got = sap.indexer_logits_packed(dev(q[:, :7].contiguous()), dev(w[:, :7].contiguous()), dev(rows), None, 64, N)
+    torch.cuda.synchronize()
+    ref = oracle.indexer_logits(q[:, :7], w[:, :7], rows, None, 64, None, N)
+    _check_logits(got, ref, M, "indexer 7 heads")
+
+
+@pytest.mark.parametrize("B,N,k", [(1, 131072, 512), (4, 131072, 512), (1, 8192, 512), (3, 4096, 512),
+                                   (2, 1000, 512), (2, 70000, 2048), (1, 100000, 1), (2, 50000, 300)])
+def test_topk_same_logits_bit_exact(B, N, k):
+    need_gpu()
+    g = torch.Generator().manual_seed(N + k + B)
+    x = torch.randn((B, N), generator=g)
+    if B > 1:
+        x[1] = torch.round(x[1] * 3) / 3             # heavy ties
+    x[0, ::11] = float("-inf")
+    nv = torch.tensor([N - (b * 977) % max(N, 1) for b in range(B)], dtype=torch.int32).clamp(min=0)
+    got = sap.topk_select(dev(x), k, n_valid=dev(nv))
+    torch.cuda.synchronize()
+    ref = oracle.topk(x, k, nv)
+    assert torch.equal(got.cpu(), ref), f"B{B} N{N} k{k}"
+
+
+def test_topk_on_indexer_logits():
+    need_gpu()
+    case = W.indexer_case(B=4, N=131072, seed=W.SEED_BASE + 530)
+    logits = _gpu_logits(case)
+    got = sap.topk_select(logits, 512)
+    torch.cuda.synchronize()
+    assert torch.equal(got.cpu(), oracle.topk(logits.cpu(), 512))
+
+
+def test_chain_indexer_topk_attention_small():
+    """Small-scale chain: 256 query tokens, 64 compressed entries with packed
+    128-d index keys, 32 index heads -> top-32 -> index build -> attention
+    with 8 heads, head_dim 64, window 16, r = 4."""
+    need_gpu()
+    case = W.tiny_case()
+    g = W.make_generator(W.SEED_BASE + 540)
+    T, n_c = case.T, case.cmp_pool.shape[0]
+    keys = W.fp4_key_rows(n_c, g)                                   # index key of each compressed row
+    qi = torch.randn((T, 32, 128), generator=g).to(torch.bfloat16)
+    wi = torch.rand((T, 32), generator=g)
+    n_vis = torch.div(case.pos.to(torch.int64) + 4, 4, rounding_mode="floor").to(torch.int32)
+    # every token scores the same key pool (page-table row stride 0), up to its causal count
+    pt = case.cmp_pt.expand(T, -1)
+    logits = sap.indexer_logits_packed(dev(qi), dev(wi), dev(keys), dev(pt), case.page, n_c, n_keys=dev(n_vis))
+    torch.cuda.synchronize()
+    ref_logits = oracle.indexer_logits(qi, wi, keys, pt, case.page, n_vis, n_c)
+    prow = (case.cmp_pt[0].to(torch.int64).repeat_interleave(case.page) * case.page
+            + torch.arange(case.page).repeat(case.cmp_pt.shape[1]))[:n_c]
+    k = np.abs(oracle.fp4_rows_decode(keys[prow]))
+    M = (np.abs(qi.double().numpy()) @ k.T * np.abs(wi.double().numpy())[:, :, None]).sum(1)
+    _check_logits(logits, ref_logits, M, "chain logits")
+    sel = sap.topk_select(logits, 32)
+    torch.cuda.synchronize()
+    assert torch.equal(sel.cpu(), oracle.topk(logits.cpu(), 32))
+    # logical entries chosen by the indexer become the compressed columns
+    case.cmp_logical = sel.cpu()
+    q = case.q.to(torch.bfloat16)
+    wp, cp = case.win_pool.to(torch.bfloat16), case.cmp_pool.to(torch.bfloat16)
+    idx = sap.build_sparse_idx(dev(case.pos), dev(case.seq), case.n_win, dev(case.win_pt), case.page,
+                               dev(case.cmp_logical), dev(case.cmp_pt))
+    out = sap.sparse_attn_paged(dev(q), dev(wp), dev(cp), idx, case.n_win, case.sm_scale)
+    torch.cuda.synchronize()
+    oidx = oracle.case_idx(case)
+    assert torch.equal(idx.cpu(), oidx)
+    ref = oracle.sparse_attn(q, wp, cp, oidx, case.n_win, case.sm_scale)
+    assert_attn_close(out, ref, "chain")
