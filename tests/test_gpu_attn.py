@@ -75,10 +75,13 @@ def test_decode_bf16(B, ratio):
     for splits in (0, 1, 2, 5):
         outs[splits] = gpu_attn(case, idx=gidx, num_splits=splits)
         assert_attn_close(outs[splits], ref, f"splits={splits} (runs {sap.sparse_attn_num_splits(case.T, 64, 512, idx.shape[1], splits)})")
-    # the split merge is exact algebra: results agree to fp32 rounding
+    # The merge is exact algebra, but each split rounds its softmax weights to
+    # bf16 relative to its own running max, so split counts agree with each
+    # other only within the same bf16-weight budget as with the oracle.
     for s in (0, 2, 5):
-        d = (outs[s] - outs[1]).abs().max().item()
-        assert d <= 1e-5, (s, d)
+        d = (outs[s] - outs[1]).double()
+        rel = (d.norm() / outs[1].double().norm()).item()
+        assert d.abs().max().item() <= 1e-2 and rel <= 2e-3, (s, rel)
 
 
 def test_decode_fp8_b8():
