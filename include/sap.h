@@ -169,8 +169,9 @@ int sap_indexer_logits_packed(const void *q, int64_t q_stride_b,
  * indices are written in ascending order, padded with -1.
  *
  * logits: [B, N] fp32 (row stride stride_b).  out_idx: [B, k] int32 (row
- * stride out_stride_b).  workspace: >= sap_topk_workspace_bytes(B, N, k)
- * bytes, 256-byte aligned.
+ * stride out_stride_b).  workspace: sap_topk_workspace_bytes(B, N, k) bytes
+ * (currently 0: one workgroup selects one row entirely in LDS; the argument
+ * is kept so a larger scheme can be adopted without an ABI change).
  * Limits: 1 <= k <= 4096, 0 <= N < 2^31.
  * Errors: SAP_ERR_NULL, SAP_ERR_SHAPE, SAP_ERR_WORKSPACE, SAP_ERR_LAUNCH.
  * ------------------------------------------------------------------------- */

@@ -9,20 +9,28 @@
 // folded into the softmax weights for PV; the softmax denominator sums the
 // unscaled weights ("Perf/kv fp8 read path", What this changes).
 //
-// One workgroup (4 waves) handles one token, a range of its columns and up to
-// 64 heads; wave w owns heads 16w .. 16w+15.  Per tile of 32 columns:
-//  1. gather: 32 rows are fetched with 16-byte loads (one wave instruction
-//     reads one full 1 KiB bf16 row), written to LDS as a row-major K tile and,
-//     after an 8x8 register transpose, as a V^T tile (columns contiguous per
-//     head_dim element).  The next tile's loads are in flight while the
-//     current tile computes; row indices are fetched one tile earlier still.
-//  2. S^T = K Q^T on MFMA 16x16x32 bf16 (M = columns, N = 16 heads, K = D):
-//     each lane ends up with 8 columns of one head.
-//  3. online softmax per head in the log2 domain (max over the lane's 8
-//     columns, then across the 4 lane groups with two xor shuffles).
+// One workgroup = 4 waves = up to 64 heads of one token over a range of its
+// columns.  Wave (hh, dh) owns heads 32hh .. 32hh+31 (two 16-head MFMA tiles,
+// so each K or V fragment read from LDS feeds two MFMAs) and head_dim half
+// dh.  Per tile of 32 columns:
+//  1. gather: each 16-byte chunk of the 32 rows goes straight from HBM into
+//     LDS (global_load_lds_dwordx4; at D = 512 one wave instruction moves one
+//     1 KiB row), XOR-swizzled per row.  The next tile is in flight while the
+//     current one computes (two LDS arrays); e4m3 rows go through registers
+//     and are widened to bf16 on the way.
+//  2. S^T = K Q^T on MFMA 16x16x32 bf16 (M = columns, N = heads) over the
+//     wave's half of head_dim; the two halves swap fp32 partial scores
+//     through LDS and add them (a + b on one side, b + a on the other: the
+//     same bits), so both waves hold the full scores of their 32 heads.
+//  3. online softmax per head in the log2 domain; the running max is only
+//     raised (and O rescaled) when a tile's max exceeds it by more than 8, so
+//     the weights stay <= 2^8 and the rescale is rare.
 //  4. O^T += V^T P^T on MFMA 16x16x32 bf16 (M = head_dim, N = heads, K = 32
-//     columns); P^T is already in the B-operand layout, so P never goes
-//     through LDS.  e4m3 pools feed P as a hi + lo pair of bf16 terms.
+//     columns) for the wave's head_dim half.  P^T leaves step 3 already in the
+//     B-operand layout; the V^T A-operand is read from the same row-major
+//     tile with ds_read_b64_tr_b16 (within 16 lanes, lane i receives element
+//     i%4 of the 8 bytes addressed by lanes i/4 + 4r, r = 0..3).  e4m3 pools
+//     feed P as a hi + lo pair of bf16 terms.
 // With one split per token the output is normalised and stored; with several
 // splits each workgroup stores (unnormalised O, running max, sum) and the
 // merge kernel combines them in split order.
@@ -33,43 +41,98 @@
 namespace sap {
 namespace {
 
+constexpr int kThreads = 256;          // 4 waves
+constexpr float kRescaleSlack = 8.0f;  // log2 units
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
 template <int D>
 struct AttnShape {
-    static constexpr int CH = D / 8;                            // 16-byte chunks per bf16 row
-    static constexpr int KT_BYTES = kAttnTile * D * 2;          // K tile, row-major
-    static constexpr int VT_BYTES = D * kAttnTile * 2;          // V^T tile
-    static constexpr int META_BYTES = 2 * kAttnTile * 4;        // column bias + column scale
-    static constexpr int BUF_BYTES = KT_BYTES + VT_BYTES + META_BYTES;
-    static constexpr int GATHER_THREADS = (kAttnTile / 8) * CH; // one 8x8 block per thread
-    static_assert(GATHER_THREADS <= 256, "tile too large for the workgroup");
+    static constexpr int CH = D / 8;                    // 16-byte chunks per bf16 row
+    static constexpr int RPI = 64 / CH;                 // rows per 1 KiB wave instruction
+    static constexpr int NQ = D / 64;                   // gather instructions per wave per tile
+    static constexpr int SK = D / 64;                   // S k-steps per wave (its head_dim half)
+    static constexpr int PM = D / 32;                   // PV head_dim tiles per wave
+    static constexpr int KT_BYTES = kAttnTile * D * 2;  // K tile, row-major (= 1 KiB * D / 32)
+    static constexpr int BUF_BYTES = KT_BYTES;
 };
 
-// K tile: row rho (0..31) at rho * 2D bytes; 16-byte chunk j stored at
-// position j ^ kswz(rho).  The S^T A-operand reads rows
-// {0,1,2,3,8,9,10,11} (+4) with one chunk per 8-lane phase; kswz maps them to
-// 8 distinct bank groups.
+// K tile row rho (0..31) holds 16-byte chunk j at position j ^ kswz(rho): the
+// S^T A-operand reads rows {0-3, 8-11} (+4) of one chunk per 8-lane phase and
+// kswz sends them to 8 distinct bank groups.
 __device__ __forceinline__ int kswz(int rho) { return (rho & 3) | ((rho & 8) >> 1); }
-template <int D>
-__device__ __forceinline__ int kt_off(int rho, int chunk) { return rho * (2 * D) + 16 * (chunk ^ kswz(rho)); }
-
-// V^T tile: head_dim element d owns 64 bytes (32 columns); 16-byte column
-// chunk kc stored at position kc ^ vswz(d).  Reads take 8 consecutive d per
-// phase (distinct via d & 1 and vswz); writes take d = 8j + e for 8
-// consecutive j (2-way at worst).
-__device__ __forceinline__ int vswz(int d) { return ((d >> 1) ^ (d >> 3)) & 3; }
-__device__ __forceinline__ int vt_off(int d, int kc) { return d * 64 + 16 * (kc ^ vswz(d)); }
 
 template <int KV> struct RawRow;
 template <> struct RawRow<0> { using T = uint4; };   // 8 bf16
 template <> struct RawRow<2> { using T = uint2; };   // 8 e4m3 codes
 
+__device__ __forceinline__ uint4 lds_b128(const uint8_t *p) { return *(const uint4 *)p; }
+__device__ __forceinline__ uint2 lds_tr16(const uint8_t *p)
+{
+    v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4i16 __attribute__((address_space(3))) *)p);
+    return __builtin_bit_cast(uint2, r);
+}
+
+// max over the four lanes l, l^16, l^32, l^48 with the gfx950 row-swap
+// permutes (VALU, no LDS round trip)
+__device__ __forceinline__ float group4_max(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// sum over the same four lanes
+__device__ __forceinline__ float group4_sum(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// v *= a for an accumulator tile held in AGPRs, one element at a time through
+// one temporary VGPR (the rescale is rare; this keeps it from needing a VGPR
+// copy of the whole accumulator)
+__device__ __forceinline__ void agpr_scale(f32x4 &v, float a)
+{
+    float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3], tmp;
+    asm volatile("v_accvgpr_read_b32 %4, %0\n\t"
+                 "v_mul_f32 %4, %4, %5\n\t"
+                 "v_accvgpr_write_b32 %0, %4\n\t"
+                 "v_accvgpr_read_b32 %4, %1\n\t"
+                 "v_mul_f32 %4, %4, %5\n\t"
+                 "v_accvgpr_write_b32 %1, %4\n\t"
+                 "v_accvgpr_read_b32 %4, %2\n\t"
+                 "v_mul_f32 %4, %4, %5\n\t"
+                 "v_accvgpr_write_b32 %2, %4\n\t"
+                 "v_accvgpr_read_b32 %4, %3\n\t"
+                 "v_mul_f32 %4, %4, %5\n\t"
+                 "v_accvgpr_write_b32 %3, %4"
+                 : "+a"(x0), "+a"(x1), "+a"(x2), "+a"(x3), "=&v"(tmp)
+                 : "v"(a));
+    v = f32x4{x0, x1, x2, x3};
+}
+
 template <int D, int KV, int OUT>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void attn_kernel(AttnParams p)
 {
     using SH = AttnShape<D>;
     using Raw = typename RawRow<KV>::T;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * SH::BUF_BYTES];
+    // two distinct arrays (not halves of one) so the compiler can tell the
+    // in-flight gather into one buffer from the reads of the other
+    __shared__ __attribute__((aligned(1024))) uint8_t bufA[SH::BUF_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t bufB[SH::BUF_BYTES];
+    // per-column bias (0 or -inf) and dequant scale of each buffer, kept out of
+    // the gather targets so writing them never waits on an in-flight gather
+    __shared__ float metaA[2 * kAttnTile], metaB[2 * kAttnTile];
+    __shared__ __attribute__((aligned(16))) float4 xch[4][4][64];   // [wave][j][lane] partial scores
 
     // XCD-aware order: consecutive logical blocks (one token's splits, then
     // neighbouring tokens, which share window rows) stay on one XCD.
@@ -86,217 +149,310 @@ void attn_kernel(AttnParams p)
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-    const int head = blockIdx.y * kAttnHeadsPerBlock + wave * 16 + l16;
-    const bool head_ok = head < p.H;
+    const int hh = wave >> 1, dh = wave & 1;
+    const int hbase = blockIdx.y * kAttnHeadsPerBlock + hh * 32;
 
-    // Q as the B operand of S^T: k-step s holds q[t, head, 32s + 8g .. +7].
-    uint4 qf[D / 32];
-    {
-        const uint16_t *qrow = p.q + (int64_t)t * p.q_st + (int64_t)(head_ok ? head : 0) * p.q_sh;
+    // Q as the B operand of S^T over this wave's head_dim half:
+    // qf[nt][s] = q[t, hbase + 16nt + l16, 32(dh*SK + s) + 8g .. +7]
+    uint4 qf[2][SH::SK];
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s)
-            qf[s] = head_ok ? *(const uint4 *)(qrow + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0);
+    for (int nt = 0; nt < 2; ++nt) {
+        const int head = hbase + 16 * nt + l16;
+        const bool ok = head < p.H;
+        const uint16_t *qrow = p.q + (int64_t)t * p.q_st + (int64_t)(ok ? head : 0) * p.q_sh;
+#pragma unroll
+        for (int s = 0; s < SH::SK; ++s)
+            qf[nt][s] = ok ? *(const uint4 *)(qrow + 32 * (dh * SH::SK + s) + 8 * g) : make_uint4(0, 0, 0, 0);
     }
+    // finite data that invalid columns load instead of a pool row (their
+    // scores are masked to -inf and their weights are 0)
+    const uint8_t *safe_src = (const uint8_t *)(p.q + (int64_t)t * p.q_st);
 
-    // gather role: row block gv (rows 8gv .. 8gv+7 of a tile), chunk gj
-    const bool gthr = tid < SH::GATHER_THREADS;
-    const int gv = tid / SH::CH;
-    const int gj = tid - gv * SH::CH;
+    // gather role: instruction q of this wave covers tile rows
+    // 8*wave + q*RPI .. + RPI-1; this lane reads row grow(q), chunk slot gpos
     const int32_t *idx_row = p.idx + (int64_t)t * p.idx_st;
-
-    int ridx[8];     // row indices, one tile ahead of the row loads
-    Raw raw[8];      // row data of the next tile to be written to LDS
-    float rsc[8];    // their dequant scales (e4m3)
-    bool rok[8];
+    const int gpos = lane % SH::CH;
+    auto grow = [&](int q) { return 8 * wave + q * SH::RPI + lane / SH::CH; };
+    int ridx[SH::NQ];      // row indices of the next tile to be issued
+    Raw raw[SH::NQ];       // e4m3 only: codes of the next tile, widened when written
+    float rsc[SH::NQ];
 
     auto load_idx = [&](int tile) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = c_begin + tile * kAttnTile + 8 * gv + i;
-            ridx[i] = (gthr && tile < n_tiles && c < c_end) ? idx_row[c] : -1;
+        for (int q = 0; q < SH::NQ; ++q) {
+            const int c = c_begin + tile * kAttnTile + grow(q);
+            ridx[q] = (tile < n_tiles && c < c_end) ? idx_row[c] : -1;
         }
     };
-    auto load_rows = [&](int tile) {
+    // issue the tile whose indices sit in ridx into buffer `bf`
+    auto issue = [&](uint8_t *bf, float *meta, int tile) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = c_begin + tile * kAttnTile + 8 * gv + i;
-            const int r = ridx[i];
-            rok[i] = r >= 0;
-            if (r >= 0) {
-                const bool w = c < p.n_win;
-                const uint8_t *base = w ? p.win : p.cmp;
-                const int64_t rs = w ? p.win_rs : p.cmp_rs;
-                raw[i] = *(const Raw *)(base + (int64_t)r * rs + (int64_t)gj * sizeof(Raw));
-                if constexpr (KV == 2) rsc[i] = (w ? p.win_scale : p.cmp_scale)[r];
-                else rsc[i] = 1.0f;
+        for (int q = 0; q < SH::NQ; ++q) {
+            const int rho = grow(q);
+            const int c = c_begin + tile * kAttnTile + rho;
+            // one row per instruction: the index is wave-uniform, use an SGPR
+            const int r = SH::RPI == 1 ? __builtin_amdgcn_readfirstlane(ridx[q]) : ridx[q];
+            const bool w = c < p.n_win;
+            const uint8_t *base = w ? p.win : p.cmp;
+            const int64_t rs = w ? p.win_rs : p.cmp_rs;
+            const int j = gpos ^ kswz(rho);
+            if constexpr (KV == 0) {
+                const uint8_t *src = r >= 0 ? base + (int64_t)r * rs + 16 * j : safe_src + 16 * gpos;
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)src,
+                    (__attribute__((address_space(3))) void *)(bf + (8 * wave + q * SH::RPI) * 2 * D), 16, 0, 0);
             } else {
-                raw[i] = Raw{};
-                rsc[i] = 0.0f;
+                // unused columns: load the stand-in bytes but keep zero codes,
+                // since arbitrary bytes read as e4m3 may be NaN encodings
+                const uint8_t *src = r >= 0 ? base + (int64_t)r * rs + 8 * j : safe_src + 8 * gpos;
+                const Raw v = *(const Raw *)src;
+                raw[q] = r >= 0 ? v : Raw{0u, 0u};
+                rsc[q] = r >= 0 ? (w ? p.win_scale : p.cmp_scale)[r] : 0.0f;
             }
+            if (gpos == 0) meta[rho] = r >= 0 ? 0.0f : -INFINITY;
         }
     };
-    auto write_tile = [&](uint8_t *buf) {
-        if (!gthr) return;
-        uint8_t *kt = buf;
-        uint8_t *vt = buf + SH::KT_BYTES;
-        float *meta = (float *)(buf + SH::KT_BYTES + SH::VT_BYTES);
-        uint4 row[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if constexpr (KV == 2) row[i] = e4m3x8_to_bf16x8(raw[i]);
-            else row[i] = raw[i];
-            *(uint4 *)(kt + kt_off<D>(8 * gv + i, gj)) = row[i];
-        }
-        // 8x8 transpose: element e of row i -> slot i of head_dim row 8gj + e
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            uint4 v;
-            const int dw = e >> 1;
-            auto pick = [&](const uint4 &u) { return dw == 0 ? u.x : dw == 1 ? u.y : dw == 2 ? u.z : u.w; };
-            v.x = perm(pick(row[1]), pick(row[0]), sel);
-            v.y = perm(pick(row[3]), pick(row[2]), sel);
-            v.z = perm(pick(row[5]), pick(row[4]), sel);
-            v.w = perm(pick(row[7]), pick(row[6]), sel);
-            *(uint4 *)(vt + vt_off(8 * gj + e, gv)) = v;
-        }
-        if (gj == 0) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                meta[8 * gv + i] = rok[i] ? 0.0f : -INFINITY;
-                meta[kAttnTile + 8 * gv + i] = rsc[i];
-            }
-        }
-    };
-
-    f32x4 acc[D / 16];
-#pragma unroll
-    for (int m = 0; m < D / 16; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;
-
-    auto compute = [&](const uint8_t *buf) {
-        const uint8_t *kt = buf;
-        const uint8_t *vt = buf + SH::KT_BYTES;
-        const float *meta = (const float *)(buf + SH::KT_BYTES + SH::VT_BYTES);
-        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        const int rho0 = 8 * (l16 >> 2) + (l16 & 3);
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const uint4 a = *(const uint4 *)(kt + kt_off<D>(rho0 + 4 * mt, 4 * s + g));
-                sacc[mt] = mfma16x16x32(a, qf[s], sacc[mt]);
-            }
-        }
-        // this lane: head `head`, columns rho = 8g + 4mt + i
-        float x[8], csc[8];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rho = 8 * g + 4 * mt + i;
-                float v = sacc[mt][i] * p.sm_scale_log2;
-                if constexpr (KV == 2) {
-                    csc[4 * mt + i] = meta[kAttnTile + rho];
-                    v *= csc[4 * mt + i];
-                }
-                v += meta[rho];
-                x[4 * mt + i] = v;
-                tmax = fmaxf(tmax, v);
-            }
-        tmax = fmaxf(tmax, shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const bool none = (m_new == -INFINITY);
-        const float alpha = none ? 1.0f : fast_exp2(m_run - m_new);
-        const float msub = none ? 0.0f : m_new;
-        float pr[8], psum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            pr[i] = fast_exp2(x[i] - msub);
-            psum += pr[i];
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int m = 0; m < D / 16; ++m) acc[m] *= alpha;
-
-        uint4 pb, pl;
+    // e4m3: widen the registers of the issued tile into the buffer (after the
+    // current tile's compute, so the loads had that long to arrive)
+    auto land = [&](uint8_t *bf, float *meta) {
         if constexpr (KV == 2) {
-            float hi[8], lo[8];
+            float *scl = meta + kAttnTile;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float pp = pr[i] * csc[i];
-                const uint32_t hb = bf16_bits(pp);
-                hi[i] = pp;
-                lo[i] = pp - __uint_as_float(hb << 16);
+            for (int q = 0; q < SH::NQ; ++q) {
+                *(uint4 *)(bf + (8 * wave + q * SH::RPI) * 2 * D + 16 * lane) = e4m3x8_to_bf16x8(raw[q]);
+                if (gpos == 0) scl[grow(q)] = rsc[q];
             }
-            pb = make_uint4(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]),
-                            pack_bf16x2(hi[4], hi[5]), pack_bf16x2(hi[6], hi[7]));
-            pl = make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
-                            pack_bf16x2(lo[4], lo[5]), pack_bf16x2(lo[6], lo[7]));
-        } else {
-            pb = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                            pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
-            pl = pb;
-        }
-#pragma unroll
-        for (int md = 0; md < D / 16; ++md) {
-            const int d = 16 * md + l16;
-            const uint4 a = *(const uint4 *)(vt + vt_off(d, g));
-            acc[md] = mfma16x16x32(a, pb, acc[md]);
-            if constexpr (KV == 2) acc[md] = mfma16x16x32(a, pl, acc[md]);
         }
     };
+
+    f32x4 acc[SH::PM][2];
+#pragma unroll
+    for (int m = 0; m < SH::PM; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
+
+    auto compute = [&](const uint8_t *bf, const float *meta) {
+        const float *bias = meta;
+        const float *scl = meta + kAttnTile;
+        // --- S^T partial over this wave's head_dim half; rows
+        //     a(mt, m) = 8(m>>2) + 4mt + (m&3) of the tile
+        f32x4 sacc[2][2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) sacc[mt][0] = sacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+            const int rho0 = 8 * (l16 >> 2) + (l16 & 3);
+            const uint8_t *k0 = bf + rho0 * 2 * D, *k1 = bf + (rho0 + 4) * 2 * D;
+            const int ks0 = kswz(rho0), ks1 = kswz(rho0 + 4);
+            auto kfrag = [&](int s, int mt) {
+                const int chunk = 4 * (dh * SH::SK + s) + g;
+                return mt ? lds_b128(k1 + 16 * (chunk ^ ks1)) : lds_b128(k0 + 16 * (chunk ^ ks0));
+            };
+            uint4 f0[3], f1[3];   // fragments for k-steps s, s+1, s+2 (ring)
+            f0[0] = kfrag(0, 0);
+            f1[0] = kfrag(0, 1);
+            if (SH::SK > 1) {
+                f0[1] = kfrag(1, 0);
+                f1[1] = kfrag(1, 1);
+            }
+#pragma unroll
+            for (int s = 0; s < SH::SK; ++s) {
+                if (s + 2 < SH::SK) {
+                    f0[(s + 2) % 3] = kfrag(s + 2, 0);
+                    f1[(s + 2) % 3] = kfrag(s + 2, 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                sacc[0][0] = mfma16x16x32(f0[s % 3], qf[0][s], sacc[0][0]);
+                sacc[0][1] = mfma16x16x32(f0[s % 3], qf[1][s], sacc[0][1]);
+                sacc[1][0] = mfma16x16x32(f1[s % 3], qf[0][s], sacc[1][0]);
+                sacc[1][1] = mfma16x16x32(f1[s % 3], qf[1][s], sacc[1][1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // --- swap partial scores with the other head_dim half
+        {
+            float4 *mine = xch[wave][0];
+            mine[0 * 64 + lane] = make_float4(sacc[0][0][0], sacc[0][0][1], sacc[0][0][2], sacc[0][0][3]);
+            mine[1 * 64 + lane] = make_float4(sacc[0][1][0], sacc[0][1][1], sacc[0][1][2], sacc[0][1][3]);
+            mine[2 * 64 + lane] = make_float4(sacc[1][0][0], sacc[1][0][1], sacc[1][0][2], sacc[1][0][3]);
+            mine[3 * 64 + lane] = make_float4(sacc[1][1][0], sacc[1][1][1], sacc[1][1][2], sacc[1][1][3]);
+            __syncthreads();
+            const float4 *other = xch[wave ^ 1][0];
+            float4 o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = other[j * 64 + lane];
+            // dh 0 adds mine + other, dh 1 adds other + mine: identical sums
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                f32x4 &sv = sacc[j >> 1][j & 1];
+                const f32x4 ov = f32x4{o[j].x, o[j].y, o[j].z, o[j].w};
+                sv = dh == 0 ? sv + ov : ov + sv;
+            }
+        }
+        // --- softmax; this lane: head hbase + 16nt + l16, columns 8g + k (k = 4mt + i)
+        float bb[8], csc[8];
+        {
+            const float4 b0 = *(const float4 *)(bias + 8 * g), b1 = *(const float4 *)(bias + 8 * g + 4);
+            bb[0] = b0.x; bb[1] = b0.y; bb[2] = b0.z; bb[3] = b0.w;
+            bb[4] = b1.x; bb[5] = b1.y; bb[6] = b1.z; bb[7] = b1.w;
+            if constexpr (KV == 2) {
+                const float4 s0 = *(const float4 *)(scl + 8 * g), s1 = *(const float4 *)(scl + 8 * g + 4);
+                csc[0] = s0.x; csc[1] = s0.y; csc[2] = s0.z; csc[3] = s0.w;
+                csc[4] = s1.x; csc[5] = s1.y; csc[6] = s1.z; csc[7] = s1.w;
+            }
+        }
+        // scores in log2 units; recomputed from sacc where needed instead of kept
+        auto score = [&](int nt, int k) {
+            float v = sacc[k >> 2][nt][k & 3] * p.sm_scale_log2;
+            if constexpr (KV == 2) v *= csc[k];
+            return v + bb[k];
+        };
+        float tmax[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            tmax[nt] = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) tmax[nt] = fmaxf(tmax[nt], score(nt, k));
+        }
+        tmax[0] = group4_max(tmax[0]);
+        tmax[1] = group4_max(tmax[1]);
+        const bool raise0 = tmax[0] > m_run[0] + kRescaleSlack;
+        const bool raise1 = tmax[1] > m_run[1] + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(raise0 || raise1) != 0) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const bool raise = nt ? raise1 : raise0;
+                const float m_new = raise ? tmax[nt] : m_run[nt];
+                const float alpha = raise ? fast_exp2(m_run[nt] - m_new) : 1.0f;
+                m_run[nt] = m_new;
+                l_run[nt] *= alpha;
+#pragma unroll
+                for (int m = 0; m < SH::PM; ++m) agpr_scale(acc[m][nt], alpha);
+            }
+        }
+        uint4 pb[2], pl[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const float msub = m_run[nt] == -INFINITY ? 0.0f : m_run[nt];
+            float pr[8], psum = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                pr[k] = fast_exp2(score(nt, k) - msub);
+                psum += pr[k];
+            }
+            l_run[nt] += psum;
+            if constexpr (KV == 2) {
+                float hi[8], lo[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float pp = pr[k] * csc[k];
+                    hi[k] = pp;
+                    lo[k] = pp - __uint_as_float(bf16_bits(pp) << 16);
+                }
+                pb[nt] = make_uint4(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]),
+                                    pack_bf16x2(hi[4], hi[5]), pack_bf16x2(hi[6], hi[7]));
+                pl[nt] = make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                                    pack_bf16x2(lo[4], lo[5]), pack_bf16x2(lo[6], lo[7]));
+            } else {
+                pb[nt] = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                                    pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
+                pl[nt] = pb[nt];
+            }
+        }
+        // --- O^T += V^T P^T over this wave's head_dim half: A-operand rows
+        //     8g + 4h + (l16>>2), head_dim 16md + 4(l16&3)
+        {
+            const int trow0 = 8 * g + (l16 >> 2);
+            const uint8_t *va0 = bf + trow0 * 2 * D, *va1 = bf + (trow0 + 4) * 2 * D;
+            const int vs0 = kswz(trow0), vs1 = kswz(trow0 + 4);
+            const int dsub = 4 * (l16 & 3);
+            auto vfrag = [&](int m) {
+                const int d = 16 * (dh * SH::PM + m) + dsub;
+                const uint2 v0 = lds_tr16(va0 + 16 * ((d >> 3) ^ vs0) + 2 * (d & 7));
+                const uint2 v1 = lds_tr16(va1 + 16 * ((d >> 3) ^ vs1) + 2 * (d & 7));
+                return make_uint4(v0.x, v0.y, v1.x, v1.y);
+            };
+            uint4 vr[3];
+            vr[0] = vfrag(0);
+            if (SH::PM > 1) vr[1] = vfrag(1);
+#pragma unroll
+            for (int m = 0; m < SH::PM; ++m) {
+                if (m + 2 < SH::PM) vr[(m + 2) % 3] = vfrag(m + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                const uint4 a = vr[m % 3];
+                acc[m][0] = mfma16x16x32(a, pb[0], acc[m][0]);
+                acc[m][1] = mfma16x16x32(a, pb[1], acc[m][1]);
+                if constexpr (KV == 2) {
+                    acc[m][0] = mfma16x16x32(a, pl[0], acc[m][0]);
+                    acc[m][1] = mfma16x16x32(a, pl[1], acc[m][1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+
+    // wait until this wave's gathers for the next tile have landed in LDS
+    auto wait_gather = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
     if (n_tiles > 0) {
         load_idx(0);
-        load_rows(0);
+        issue(bufA, metaA, 0);
+        land(bufA, metaA);
         load_idx(1);
-        write_tile(smem);
+        wait_gather();
         __syncthreads();
-        load_rows(1);
-        load_idx(2);
-        for (int it = 0; it < n_tiles; ++it) {
-            compute(smem + (it & 1) * SH::BUF_BYTES);
+        for (int it = 0; it < n_tiles; it += 2) {
+            // tile it is in bufA; tile it+1 goes to bufB
             if (it + 1 < n_tiles) {
-                write_tile(smem + ((it + 1) & 1) * SH::BUF_BYTES);
-                load_rows(it + 2);
+                issue(bufB, metaB, it + 1);
+                load_idx(it + 2);
+            }
+            compute(bufA, metaA);
+            if (it + 1 < n_tiles) land(bufB, metaB);
+            wait_gather();
+            __syncthreads();
+            if (it + 1 >= n_tiles) break;
+            // tile it+1 is in bufB; tile it+2 goes to bufA
+            if (it + 2 < n_tiles) {
+                issue(bufA, metaA, it + 2);
                 load_idx(it + 3);
             }
+            compute(bufB, metaB);
+            if (it + 2 < n_tiles) land(bufA, metaA);
+            wait_gather();
             __syncthreads();
         }
     }
 
-    float l_tot = l_run + shfl_xor(l_run, 16);
-    l_tot += shfl_xor(l_tot, 32);
-    if (!head_ok) return;
-
-    if (p.num_splits == 1) {
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        if constexpr (OUT == 1) {
-            float *o = (float *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh;
 #pragma unroll
-            for (int md = 0; md < D / 16; ++md) {
-                const f32x4 v = acc[md] * inv;
-                *(float4 *)(o + 16 * md + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+    for (int nt = 0; nt < 2; ++nt) {
+        const int head = hbase + 16 * nt + l16;
+        const float l_tot = group4_sum(l_run[nt]);
+        if (head >= p.H) continue;
+        const int d0 = 16 * dh * SH::PM + 4 * g;
+        if (p.num_splits == 1) {
+            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+            if constexpr (OUT == 1) {
+                float *o = (float *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d0;
+#pragma unroll
+                for (int m = 0; m < SH::PM; ++m) {
+                    const f32x4 v = acc[m][nt] * inv;
+                    *(float4 *)(o + 16 * m) = make_float4(v[0], v[1], v[2], v[3]);
+                }
+            } else {
+                uint16_t *o = (uint16_t *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d0;
+#pragma unroll
+                for (int m = 0; m < SH::PM; ++m) {
+                    const f32x4 v = acc[m][nt] * inv;
+                    *(uint2 *)(o + 16 * m) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                }
             }
         } else {
-            uint16_t *o = (uint16_t *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh;
+            const int64_t slot = ((int64_t)t * p.num_splits + split) * p.H + head;
+            float *o = p.part_o + slot * D + d0;
 #pragma unroll
-            for (int md = 0; md < D / 16; ++md) {
-                const f32x4 v = acc[md] * inv;
-                *(uint2 *)(o + 16 * md + 4 * g) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-            }
+            for (int m = 0; m < SH::PM; ++m)
+                *(float4 *)(o + 16 * m) = make_float4(acc[m][nt][0], acc[m][nt][1], acc[m][nt][2], acc[m][nt][3]);
+            if (g == 0 && dh == 0) *(float2 *)(p.part_ml + slot * 2) = make_float2(m_run[nt], l_tot);
         }
-    } else {
-        const int64_t slot = ((int64_t)t * p.num_splits + split) * p.H + head;
-        float *o = p.part_o + slot * D;
-#pragma unroll
-        for (int md = 0; md < D / 16; ++md)
-            *(float4 *)(o + 16 * md + 4 * g) = make_float4(acc[md][0], acc[md][1], acc[md][2], acc[md][3]);
-        if (g == 0) *(float2 *)(p.part_ml + slot * 2) = make_float2(m_run, l_tot);
     }
 }
 
@@ -337,7 +493,7 @@ template <int D, int KV, int OUT>
 hipError_t launch_attn_t(const AttnParams &p, hipStream_t s)
 {
     const dim3 grid((unsigned)(p.T * p.num_splits), (unsigned)((p.H + kAttnHeadsPerBlock - 1) / kAttnHeadsPerBlock));
-    hipLaunchKernelGGL((attn_kernel<D, KV, OUT>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_kernel<D, KV, OUT>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

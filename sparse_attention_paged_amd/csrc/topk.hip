@@ -6,26 +6,35 @@
 // with -1 (the index top-k of "perf(kernel): keep 16-byte kv loads in dsv4
 // sparse attention and unroll gated pool", Kernel time).
 //
-// Values become order-preserving 32-bit keys (0 = not a candidate).  One
-// workgroup selects the top-k of one segment with a 4-pass, 8-bit radix
-// select over keys held in registers (LDS histograms, one wave scanning the
-// 256 bins), then takes the keys above the threshold plus the first
-// threshold-equal keys in index order (block prefix sums keep index order,
-// which is also the tie-break).  Pass 1 cuts each row into 4096-entry
-// segments and writes each segment's survivors (key, index) to a slot of k
-// entries; later passes merge groups of slots the same way until one slot is
-// left, which writes the final index list.  The top-k of a union is always
-// inside the union of the parts' top-k under the same total order, so every
-// pass is exact.
+// One 1024-thread workgroup per row.  Values become order-preserving 32-bit
+// keys (0 = not a candidate).
+//  1. Threshold estimate: a strided sample of up to 4096 keys gives, by radix
+//     select, a key tau expected to have about 2k row entries at or above it
+//     (skipped when the whole row fits the candidate buffer).
+//  2. The row is streamed through registers in coalesced chunks; entries with
+//     key >= tau are compacted into an LDS candidate buffer.
+//  3. If tau was too high (fewer than k survivors) or the buffer overflowed,
+//     the exact answer is computed by radix select over the whole row
+//     streamed from memory -- slower, never wrong.
+//  4. Radix select (4 passes of 8 bits, 16 sub-histograms so equal digits do
+//     not serialise on one LDS word) finds the k-th largest key T; if more
+//     entries equal T than are needed, a second radix select over their
+//     indices keeps the lowest ones.
+//  5. The selected indices (<= k) are sorted in LDS by a bitonic network and
+//     written out, padded with -1.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace sap {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRowSeg = 4096;            // pass-1 segment (16 per thread)
-constexpr int kMergeSeg = 16384;         // later passes (64 per thread)
+constexpr int kT = 1024;                 // threads per workgroup
+constexpr int kWaves = kT / kWave;
+constexpr int kCap = 8192;               // LDS candidate capacity
+constexpr int kSample = 4096;
+constexpr int kChunkPer = 16;            // keys per thread per streamed chunk
+constexpr int kChunk = kT * kChunkPer;
+constexpr int kMaxK = 4096;
 
 __device__ __forceinline__ uint32_t order_key(float v)
 {
@@ -34,264 +43,266 @@ __device__ __forceinline__ uint32_t order_key(float v)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // >= 0x00800000 otherwise
 }
 
-struct PassParams {
-    int B, k;
-    // pass 1 input: a row of floats
-    const float *x;
-    int64_t x_sb;
-    const int32_t *n_valid;
-    int N;
-    // later-pass input: slots of k (key, index) pairs with counts
-    const uint32_t *in_key;
-    const int32_t *in_idx;
-    const int32_t *in_cnt;
-    int in_slots, slots_per_wg;
-    // output: either slots or the final list
-    uint32_t *out_key;
-    int32_t *out_idx;
-    int32_t *out_cnt;
-    int out_slots;
-    int32_t *final_out;
-    int64_t final_sb;
+struct Smem {
+    uint32_t hist[16 * 256];
+    uint32_t tot[256];
+    uint32_t cand_key[kCap];
+    int32_t cand_idx[kCap];
+    int32_t sel[kMaxK];
+    int red[kWaves];
+    int misc[8];
 };
 
-__device__ __forceinline__ int wave_incl_scan(int x, int lane)
+__device__ __forceinline__ int block_sum(int v, Smem &s)
 {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    if (lane == 0) s.red[wave] = v;
+    __syncthreads();
+    int t = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t += s.red[w];
+    __syncthreads();
+    return t;
+}
+
+__device__ __forceinline__ int block_excl_scan(int v, Smem &s, int &total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
         const int y = __shfl_up(x, off, kWave);
         if (lane >= off) x += y;
     }
-    return x;
-}
-
-// exclusive prefix over the block in thread order; `total` gets the sum
-__device__ __forceinline__ int block_excl_scan(int v, int *sh, int &total)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int inc = wave_incl_scan(v, lane);
-    if (lane == 63) sh[wave] = inc;
+    if (lane == 63) s.red[wave] = x;
     __syncthreads();
     int base = 0;
     total = 0;
 #pragma unroll
-    for (int w = 0; w < kThreads / kWave; ++w) {
-        const int s = sh[w];
-        if (w < wave) base += s;
-        total += s;
+    for (int w = 0; w < kWaves; ++w) {
+        const int r = s.red[w];
+        base += (w < wave) ? r : 0;
+        total += r;
     }
     __syncthreads();
-    return base + inc - v;
+    return base + x - v;
 }
 
-template <int PER, bool FROM_ROW>
-__global__ __launch_bounds__(kThreads) void topk_pass_kernel(PassParams p)
+// Radix select over the keys a visitor presents: returns the key T of the
+// kk-th largest nonzero key and how many entries equal to T belong to the
+// top kk.  `visit(f)` calls f(key) for every key this thread holds.
+template <class Visit>
+__device__ uint32_t radix_kth(Visit visit, int kk, Smem &s, int &need_eq)
 {
-    __shared__ uint32_t hist[256];
-    __shared__ int sh[8];
-    const int b = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-
-    // this thread's contiguous run of segment positions [tid*PER, tid*PER+PER)
-    uint32_t key[PER];
-    int32_t ind[PER];
-    if constexpr (FROM_ROW) {
-        int nv = p.n_valid ? p.n_valid[b] : p.N;
-        nv = min(max(nv, 0), p.N);
-        const int64_t base = (int64_t)seg * (kThreads * PER);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t prefix = 0u, mask = 0u;
+    int rem = kk;
+    uint32_t *myh = s.hist + (lane & 15) * 256;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 16 * 256; i += kT) s.hist[i] = 0u;
+        __syncthreads();
+        visit([&](uint32_t key) {
+            if (key != 0u && (key & mask) == prefix) atomicAdd(&myh[(key >> shift) & 255u], 1u);
+        });
+        __syncthreads();
+        if (tid < 256) {
+            uint32_t t = 0;
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int64_t i = base + (int64_t)tid * PER + j;
-            ind[j] = (int32_t)i;
-            key[j] = i < nv ? order_key(p.x[(int64_t)b * p.x_sb + i]) : 0u;
+            for (int j = 0; j < 16; ++j) t += s.hist[j * 256 + tid];
+            s.tot[tid] = t;
         }
-    } else {
-        const int s0 = seg * p.slots_per_wg;
+        __syncthreads();
+        if (wave == 0) {
+            const int c = (int)(s.tot[4 * lane] + s.tot[4 * lane + 1] + s.tot[4 * lane + 2] + s.tot[4 * lane + 3]);
+            int x = c;   // suffix sum: entries in bins >= 4*lane
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int pos = tid * PER + j;
-            const int s = s0 + pos / p.k;
-            const int e = pos - (pos / p.k) * p.k;
-            key[j] = 0u;
-            ind[j] = -1;
-            if (s < p.in_slots && s < s0 + p.slots_per_wg) {
-                const int64_t slot = (int64_t)b * p.in_slots + s;
-                if (e < p.in_cnt[slot]) {
-                    key[j] = p.in_key[slot * p.k + e];
-                    ind[j] = p.in_idx[slot * p.k + e];
+            for (int off = 1; off < kWave; off <<= 1) {
+                const int y = __shfl_down(x, off, kWave);
+                if (lane + off < kWave) x += y;
+            }
+            if (x >= rem && x - c < rem) {
+                int above = x - c, bin = 4 * lane;
+                for (int bb = 4 * lane + 3; bb >= 4 * lane; --bb) {
+                    if (above + (int)s.tot[bb] >= rem) { bin = bb; break; }
+                    above += (int)s.tot[bb];
                 }
+                s.misc[0] = bin;
+                s.misc[1] = above;
             }
         }
+        __syncthreads();
+        prefix |= (uint32_t)s.misc[0] << shift;
+        mask |= 255u << shift;
+        rem -= s.misc[1];
+        __syncthreads();
     }
+    need_eq = rem;
+    return prefix;
+}
 
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) cnt += key[j] != 0u;
-    int n_cand;
-    (void)block_excl_scan(cnt, sh, n_cand);
-    const int kk = min(p.k, n_cand);
-
-    uint32_t T = 0xFFFFFFFFu;
-    int need_eq = 0;
-    if (kk > 0) {
-        uint32_t prefix = 0u, mask = 0u;
-        int rem = kk;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            hist[tid] = 0u;
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < PER; ++j)
-                if (key[j] != 0u && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 255u], 1u);
-            __syncthreads();
-            if (wave == 0) {
-                const int c = (int)(hist[4 * lane] + hist[4 * lane + 1] + hist[4 * lane + 2] + hist[4 * lane + 3]);
-                // suffix sum over lanes: entries in bins >= 4*lane
-                int x = c;
-#pragma unroll
-                for (int off = 1; off < kWave; off <<= 1) {
-                    const int y = __shfl_down(x, off, kWave);
-                    if (lane + off < kWave) x += y;
-                }
-                if (x >= rem && x - c < rem) {
-                    int above = x - c;
-                    int bin = 4 * lane;
-                    for (int bb = 4 * lane + 3; bb >= 4 * lane; --bb) {
-                        if (above + (int)hist[bb] >= rem) { bin = bb; break; }
-                        above += (int)hist[bb];
-                    }
-                    sh[4] = bin;
-                    sh[5] = above;
-                }
+// Ascending bitonic sort of s.sel[0 .. n) (n <= kMaxK), padding with INT_MAX.
+__device__ void sort_sel(Smem &s, int n)
+{
+    int m = 1;
+    while (m < n) m <<= 1;
+    for (int i = n + threadIdx.x; i < m; i += kT) s.sel[i] = 0x7FFFFFFF;
+    __syncthreads();
+    for (int size = 2; size <= m; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = threadIdx.x; i < m / 2; i += kT) {
+                const int lo = 2 * i - (i & (stride - 1));
+                const int hi = lo + stride;
+                const bool up = ((lo & size) == 0);
+                const int a = s.sel[lo], b = s.sel[hi];
+                if ((a > b) == up) { s.sel[lo] = b; s.sel[hi] = a; }
             }
             __syncthreads();
-            const int bin = sh[4];
-            rem -= sh[5];
-            prefix |= (uint32_t)bin << shift;
-            mask |= 255u << shift;
-            __syncthreads();
         }
-        T = prefix;
-        need_eq = rem;
+    }
+}
+
+__global__ __launch_bounds__(kT) void topk_row_kernel(TopkParams p)
+{
+    __shared__ Smem s;
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const float *x = p.x + (int64_t)b * p.x_sb;
+    int nv = p.n_valid ? p.n_valid[b] : p.N;
+    nv = min(max(nv, 0), p.N);
+    const int k = p.k;
+
+    // 1. threshold estimate
+    uint32_t tau = 1u;
+    if (nv > kCap) {
+        const int S = kSample;
+        const int want = min(S, (int)(((int64_t)2 * k * S + nv - 1) / nv) + 4);
+        uint32_t sk[kSample / kT];
+#pragma unroll
+        for (int j = 0; j < kSample / kT; ++j) {
+            const int si = j * kT + tid;
+            sk[j] = order_key(x[(int64_t)si * nv / S]);
+        }
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < kSample / kT; ++j) cnt += sk[j] != 0u;
+        const int ns = block_sum(cnt, s);
+        if (ns >= want) {
+            int ne;
+            tau = radix_kth([&](auto f) {
+#pragma unroll
+                for (int j = 0; j < kSample / kT; ++j) f(sk[j]);
+            }, want, s, ne);
+        }
     }
 
-    int gt = 0, eq = 0;
+    // 2. stream the row, compact entries with key >= tau
+    int n_c = 0;            // candidates kept (block-uniform)
+    bool overflow = false;
+    for (int base = 0; base < nv; base += kChunk) {
+        uint32_t kv[kChunkPer];
+        int mine = 0;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        gt += (kk > 0 && key[j] > T);
-        eq += (kk > 0 && key[j] == T);
-    }
-    int tot;
-    const int eq_before = block_excl_scan(eq, sh, tot);
-    const int take_eq = max(0, min(eq, need_eq - eq_before));
-    int n_out;
-    int pos = block_excl_scan(gt + take_eq, sh, n_out);
-
-    if (p.final_out) {
-        int32_t *o = p.final_out + (int64_t)b * p.final_sb;
-        int seen = 0;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const bool sel = kk > 0 && (key[j] > T || (key[j] == T && seen++ < take_eq));
-            if (sel) o[pos++] = ind[j];
+        for (int j = 0; j < kChunkPer; ++j) {
+            const int i = base + j * kT + tid;
+            kv[j] = i < nv ? order_key(x[i]) : 0u;
+            mine += kv[j] != 0u && kv[j] >= tau;
         }
-        for (int i = n_out + tid; i < p.k; i += kThreads) o[i] = -1;
-    } else {
-        const int64_t slot = (int64_t)b * p.out_slots + seg;
-        uint32_t *ok = p.out_key + slot * p.k;
-        int32_t *oi = p.out_idx + slot * p.k;
-        int seen = 0;
+        int tot;
+        int pos = n_c + block_excl_scan(mine, s, tot);
+        if (n_c + tot > kCap) {
+            overflow = true;
+            break;
+        }
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const bool sel = kk > 0 && (key[j] > T || (key[j] == T && seen++ < take_eq));
-            if (sel) {
-                ok[pos] = key[j];
-                oi[pos] = ind[j];
+        for (int j = 0; j < kChunkPer; ++j) {
+            if (kv[j] != 0u && kv[j] >= tau) {
+                s.cand_key[pos] = kv[j];
+                s.cand_idx[pos] = base + j * kT + tid;
                 ++pos;
             }
         }
-        if (tid == 0) p.out_cnt[slot] = n_out;
+        n_c += tot;
     }
+    __syncthreads();
+
+    // 3./4. exact k-th key over the candidates (or the whole row)
+    const bool whole = overflow || (tau > 1u && n_c < k);
+    int kk;
+    uint32_t T;
+    int need_eq;
+    if (!whole) {
+        kk = min(k, n_c);
+        T = kk > 0 ? radix_kth([&](auto f) {
+                for (int i = tid; i < n_c; i += kT) f(s.cand_key[i]);
+            }, kk, s, need_eq) : 0xFFFFFFFFu;
+    } else {
+        int cnt = 0;
+        for (int i = tid; i < nv; i += kT) cnt += order_key(x[i]) != 0u;
+        kk = min(k, block_sum(cnt, s));
+        T = kk > 0 ? radix_kth([&](auto f) {
+                for (int i = tid; i < nv; i += kT) f(order_key(x[i]));
+            }, kk, s, need_eq) : 0xFFFFFFFFu;
+    }
+
+    // ties at T: keep the need_eq lowest indices
+    uint32_t imax = 0x7FFFFFFFu;
+    if (kk > 0) {
+        int eq = 0;
+        if (!whole) {
+            for (int i = tid; i < n_c; i += kT) eq += s.cand_key[i] == T;
+        } else {
+            for (int i = tid; i < nv; i += kT) eq += order_key(x[i]) == T;
+        }
+        const int n_eq = block_sum(eq, s);
+        if (n_eq > need_eq) {
+            int one;
+            uint32_t t2;
+            if (!whole) {
+                t2 = radix_kth([&](auto f) {
+                    for (int i = tid; i < n_c; i += kT) f(s.cand_key[i] == T ? ~(uint32_t)s.cand_idx[i] : 0u);
+                }, need_eq, s, one);
+            } else {
+                t2 = radix_kth([&](auto f) {
+                    for (int i = tid; i < nv; i += kT) f(order_key(x[i]) == T ? ~(uint32_t)i : 0u);
+                }, need_eq, s, one);
+            }
+            imax = ~t2;
+        }
+    }
+
+    // 5. collect, sort, write
+    if (tid == 0) s.misc[2] = 0;
+    __syncthreads();
+    if (kk > 0) {
+        auto take = [&](uint32_t key, int idx) {
+            if (key > T || (key == T && (uint32_t)idx <= imax)) {
+                const int at = atomicAdd(&s.misc[2], 1);
+                if (at < kMaxK) s.sel[at] = idx;
+            }
+        };
+        if (!whole) {
+            for (int i = tid; i < n_c; i += kT) take(s.cand_key[i], s.cand_idx[i]);
+        } else {
+            for (int i = tid; i < nv; i += kT) take(order_key(x[i]), i);
+        }
+    }
+    __syncthreads();
+    const int n_sel = min(s.misc[2], kk);
+    sort_sel(s, n_sel);
+    int32_t *o = p.out + (int64_t)b * p.out_sb;
+    for (int i = tid; i < k; i += kT) o[i] = i < n_sel ? s.sel[i] : -1;
 }
 
 }  // namespace
 
-// Workspace: two slot buffers sized for pass 1 (ceil(N/4096) slots per row).
-size_t topk_slot_bytes(int B, int N, int k)
-{
-    const int64_t slots = N > kRowSeg ? (N + kRowSeg - 1) / kRowSeg : 0;
-    const int64_t per = (int64_t)B * slots * ((int64_t)k * 8 + 4);
-    return (size_t)((per + 255) / 256 * 256);
-}
+size_t topk_slot_bytes(int, int, int) { return 0; }
 
-hipError_t launch_topk(const TopkParams &tp, hipStream_t s)
+hipError_t launch_topk(const TopkParams &p, hipStream_t st)
 {
-    if (tp.B == 0) return hipSuccess;
-    PassParams p{};
-    p.B = tp.B;
-    p.k = tp.k;
-    p.x = tp.x;
-    p.x_sb = tp.x_sb;
-    p.n_valid = tp.n_valid;
-    p.N = tp.N;
-    const int slots1 = tp.N > kRowSeg ? (tp.N + kRowSeg - 1) / kRowSeg : 1;
-    if (slots1 == 1) {
-        p.final_out = tp.out;
-        p.final_sb = tp.out_sb;
-        hipLaunchKernelGGL((topk_pass_kernel<kRowSeg / kThreads, true>), dim3(1, tp.B), dim3(kThreads), 0, s, p);
-        return hipGetLastError();
-    }
-    // ping-pong slot buffers inside the workspace
-    const size_t half = topk_slot_bytes(tp.B, tp.N, tp.k);
-    uint8_t *buf[2] = {(uint8_t *)tp.workspace, (uint8_t *)tp.workspace + half};
-    struct Slots { uint32_t *key; int32_t *idx; int32_t *cnt; };
-    auto carve = [&](uint8_t *base, int slots) {
-        Slots r;
-        r.key = (uint32_t *)base;
-        r.idx = (int32_t *)(base + (size_t)tp.B * slots * tp.k * 4);
-        r.cnt = (int32_t *)(base + (size_t)tp.B * slots * tp.k * 8);
-        return r;
-    };
-    {
-        const Slots o = carve(buf[0], slots1);
-        p.out_key = o.key;
-        p.out_idx = o.idx;
-        p.out_cnt = o.cnt;
-    }
-    p.out_slots = slots1;
-    hipLaunchKernelGGL((topk_pass_kernel<kRowSeg / kThreads, true>), dim3(slots1, tp.B), dim3(kThreads), 0, s, p);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-
-    int in_slots = slots1, cur = 0;
-    const int spw = kMergeSeg / tp.k;                 // slots merged per workgroup (>= 4)
-    while (true) {
-        PassParams q{};
-        q.B = tp.B;
-        q.k = tp.k;
-        const Slots in = carve(buf[cur], in_slots);
-        q.in_key = in.key;
-        q.in_idx = in.idx;
-        q.in_cnt = in.cnt;
-        q.in_slots = in_slots;
-        q.slots_per_wg = spw;
-        const int out_slots = (in_slots + spw - 1) / spw;
-        if (out_slots == 1) {
-            q.final_out = tp.out;
-            q.final_sb = tp.out_sb;
-        } else {
-            const Slots o = carve(buf[cur ^ 1], out_slots);
-            q.out_key = o.key;
-            q.out_idx = o.idx;
-            q.out_cnt = o.cnt;
-            q.out_slots = out_slots;
-        }
-        hipLaunchKernelGGL((topk_pass_kernel<kMergeSeg / kThreads, false>), dim3(out_slots, tp.B), dim3(kThreads), 0,
-                           s, q);
-        err = hipGetLastError();
-        if (err != hipSuccess || out_slots == 1) return err;
-        in_slots = out_slots;
-        cur ^= 1;
-    }
+    if (p.B == 0) return hipSuccess;
+    hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)p.B), dim3(kT), 0, st, p);
+    return hipGetLastError();
 }
 
 }  // namespace sap

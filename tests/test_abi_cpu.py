@@ -114,12 +114,11 @@ def test_indexer_argument_checks(L):
 
 def test_topk_argument_checks(L):
     ws = L.sap_topk_workspace_bytes
-    assert ws(1, 4096, 512) == 0                      # one segment: no workspace
-    assert ws(1, 131072, 512) > 0
-    assert ws(1, 131072, 512) % 512 == 0
+    assert ws(1, 4096, 512) == 0                      # one workgroup per row: no workspace
+    assert ws(4, 131072, 512) == 0
 
     def call(**kw):
-        a = dict(x=A, sb=131072, nv=None, B=1, N=131072, k=512, out=A, osb=512, ws=A, wsb=ws(1, 131072, 512))
+        a = dict(x=A, sb=131072, nv=None, B=1, N=131072, k=512, out=A, osb=512, ws=None, wsb=0)
         a.update(kw)
         return L.sap_topk_select(a["x"], a["sb"], a["nv"], a["B"], a["N"], a["k"], a["out"], a["osb"],
                                  a["ws"], a["wsb"], None)
@@ -128,8 +127,8 @@ def test_topk_argument_checks(L):
     assert call(k=5000) == ESHAPE
     assert call(osb=100) == ESHAPE
     assert call(out=None) == ENULL
-    assert call(ws=None) == EWS
-    assert call(wsb=10) == EWS
+    assert call(x=None) == ENULL
+    assert call(sb=100) == ESHAPE
 
 
 def test_index_build_argument_checks(L):

@@ -215,17 +215,17 @@ def test_ratio0_alias_and_row_offset_views():
 
 
 def test_bf16_output():
-    # A bf16 output adds one rounding (relative error <= 2^-9 per element) on
-    # top of the fp32-output bar, so the rel-L2 bound grows by 2^-9.
+    # A bf16 output adds one rounding (at most half an ulp, <= 2^-9 |x|) on
+    # top of the fp32-output bar: rel-L2 grows by 2^-9 and max-abs by
+    # 2^-9 max|ref| (tokens with one or two columns output a row itself).
     need_gpu()
-    case = W.decode_case(B=8, ratio=4, seed=W.SEED_BASE + 90)
-    ref = oracle.case_attn(case)
-    out = gpu_attn(case, out_dtype=torch.bfloat16)
-    assert out.dtype == torch.bfloat16
-    assert_attn_close(out.float(), ref, "bf16 out", rel_l2=2e-3 + 2.0 ** -9)
-    pcase = W.prefill_case(T=300, ratio=4, seed=W.SEED_BASE + 91)
-    out = gpu_attn(pcase, out_dtype=torch.bfloat16, num_splits=1)
-    assert_attn_close(out.float(), oracle.case_attn(pcase), "bf16 out prefill", rel_l2=2e-3 + 2.0 ** -9)
+    for case, splits in ((W.decode_case(B=8, ratio=4, seed=W.SEED_BASE + 90), 0),
+                         (W.prefill_case(T=300, ratio=4, seed=W.SEED_BASE + 91), 1)):
+        ref = oracle.case_attn(case)
+        out = gpu_attn(case, out_dtype=torch.bfloat16, num_splits=splits)
+        assert out.dtype == torch.bfloat16
+        bound = 1e-2 + 2.0 ** -9 * ref.abs().max().item()
+        assert_attn_close(out.float(), ref, f"bf16 out {case.name}", max_abs=bound, rel_l2=2e-3 + 2.0 ** -9)
 
 
 def test_determinism_sha256():
