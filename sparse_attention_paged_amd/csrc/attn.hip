@@ -10,27 +10,34 @@
 // unscaled weights ("Perf/kv fp8 read path", What this changes).
 //
 // One workgroup = 4 waves = up to 64 heads of one token over a range of its
-// columns.  Wave (hh, dh) owns heads 32hh .. 32hh+31 (two 16-head MFMA tiles,
-// so each K or V fragment read from LDS feeds two MFMAs) and head_dim half
-// dh.  Per tile of 32 columns:
-//  1. gather: each 16-byte chunk of the 32 rows goes straight from HBM into
-//     LDS (global_load_lds_dwordx4; at D = 512 one wave instruction moves one
-//     1 KiB row), XOR-swizzled per row.  The next tile is in flight while the
-//     current one computes (two LDS arrays); e4m3 rows go through registers
-//     and are widened to bf16 on the way.
-//  2. S^T = K Q^T on MFMA 16x16x32 bf16 (M = columns, N = heads) over the
-//     wave's half of head_dim; the two halves swap fp32 partial scores
-//     through LDS and add them (a + b on one side, b + a on the other: the
-//     same bits), so both waves hold the full scores of their 32 heads.
-//  3. online softmax per head in the log2 domain; the running max is only
-//     raised (and O rescaled) when a tile's max exceeds it by more than 8, so
-//     the weights stay <= 2^8 and the rescale is rare.
-//  4. O^T += V^T P^T on MFMA 16x16x32 bf16 (M = head_dim, N = heads, K = 32
-//     columns) for the wave's head_dim half.  P^T leaves step 3 already in the
-//     B-operand layout; the V^T A-operand is read from the same row-major
-//     tile with ds_read_b64_tr_b16 (within 16 lanes, lane i receives element
-//     i%4 of the 8 bytes addressed by lanes i/4 + 4r, r = 0..3).  e4m3 pools
-//     feed P as a hi + lo pair of bf16 terms.
+// columns, taken in tiles of 32 columns.  The split of work between the waves
+// is chosen so that every operand a wave reads from LDS feeds four MFMAs
+// (64 heads as the MFMA N dimension) and every score is exponentiated once:
+//  - gather: each wave moves 8 of the tile's 32 rows straight from HBM into
+//    LDS (global_load_lds_dwordx4, 16 bytes per lane; one wave instruction
+//    moves one 1 KiB row at D = 512), chunk-swizzled per row.  Three LDS
+//    tiles rotate, so tile t+2 is in flight while tile t computes.  e4m3 rows
+//    go through registers and are widened to bf16 on the way.
+//  - S^T = K Q^T on MFMA 16x16x32 bf16 (M = columns, N = heads): wave
+//    (dq, ch) = (w & 1, w >> 1) takes columns 16ch .. 16ch+15, all 64 heads,
+//    head_dim half dq.  The two head_dim halves of a column half add their
+//    partial scores through LDS: each keeps the 32 heads whose softmax it
+//    owns (32dq .. 32dq+31) and receives the partner's partial for them.
+//  - online softmax in the log2 domain over the owned 32 heads x 16 columns
+//    (8 scores per lane).  The running max only moves when a tile's max
+//    exceeds it by more than 8 (so weights stay <= 2^8): each wave computes P
+//    against the current max and publishes its tile max; if any head of the
+//    workgroup needs a larger max (first tile, rare later), all waves agree on
+//    the new maxima, rescale and recompute.
+//  - O^T += V^T P^T on MFMA 16x16x32 bf16 (M = head_dim, N = heads, K = the
+//    32 columns): wave w owns head_dim quarter w for all 64 heads.  P^T is
+//    read back from LDS in the B-operand layout; the V^T A-operand is read
+//    from the row-major tile with ds_read_b64_tr_b16 (within 16 lanes, lane i
+//    receives element i%4 of the 8 bytes addressed by lanes i/4 + 4r,
+//    r = 0..3).  e4m3 pools feed P as a hi + lo pair of bf16 terms.
+// The PV reduction index kk = 8g + 4c + i stands for tile column
+// 16c + 4g + i, which lets each lane take its own 4 weights of column half c
+// straight from the softmax layout.
 // With one split per token the output is normalised and stored; with several
 // splits each workgroup stores (unnormalised O, running max, sum) and the
 // merge kernel combines them in split order.
@@ -38,11 +45,14 @@
 #include "formats.hpp"
 #include "internal.hpp"
 
+#include <type_traits>
+
 namespace sap {
 namespace {
 
 constexpr int kThreads = 256;          // 4 waves
-constexpr float kRescaleSlack = 8.0f;  // log2 units
+constexpr float kRescaleSlack = 32.0f; // log2 units: weights stay <= 2^32
+constexpr int kIdxChunk = 2048;        // columns whose row indices are staged in LDS at a time
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
@@ -51,16 +61,17 @@ struct AttnShape {
     static constexpr int CH = D / 8;                    // 16-byte chunks per bf16 row
     static constexpr int RPI = 64 / CH;                 // rows per 1 KiB wave instruction
     static constexpr int NQ = D / 64;                   // gather instructions per wave per tile
-    static constexpr int SK = D / 64;                   // S k-steps per wave (its head_dim half)
-    static constexpr int PM = D / 32;                   // PV head_dim tiles per wave
-    static constexpr int KT_BYTES = kAttnTile * D * 2;  // K tile, row-major (= 1 KiB * D / 32)
-    static constexpr int BUF_BYTES = KT_BYTES;
+    static constexpr int SK = D / 64;                   // S k-steps (32 deep) over a head_dim half
+    static constexpr int PM = D / 64;                   // PV m-tiles (16 rows) over a head_dim quarter
+    static constexpr int TILE_BYTES = kAttnTile * D * 2;
 };
 
-// K tile row rho (0..31) holds 16-byte chunk j at position j ^ kswz(rho): the
-// S^T A-operand reads rows {0-3, 8-11} (+4) of one chunk per 8-lane phase and
-// kswz sends them to 8 distinct bank groups.
-__device__ __forceinline__ int kswz(int rho) { return (rho & 3) | ((rho & 8) >> 1); }
+// Tile row rho holds 16-byte chunk j at position j ^ rswz(rho).  rswz maps
+// rows 0..7 to 8 distinct values (the S reads: 8 lanes, 8 rows, one chunk)
+// and rows 4a .. 4a+3 to 4 distinct even-or-odd pairs (the transposed PV
+// reads: 4 rows x 2 adjacent chunks), so both read patterns are free of LDS
+// bank conflicts.
+__device__ __forceinline__ int rswz(int rho) { return ((rho & 3) << 1) | ((rho >> 2) & 1); }
 
 template <int KV> struct RawRow;
 template <> struct RawRow<0> { using T = uint4; };   // 8 bf16
@@ -119,20 +130,50 @@ __device__ __forceinline__ void agpr_scale(f32x4 &v, float a)
     v = f32x4{x0, x1, x2, x3};
 }
 
+// wait until at most N vector memory instructions of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+// 16 bytes per lane from global memory straight into LDS at lds_addr + 16 *
+// lane (global_load_lds_dwordx4).  Issued from inline assembly, so the
+// compiler neither tracks nor waits for it: the caller waits with wait_vm<N>()
+// and publishes the tile with a barrier.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_addr)
+{
+    const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr);   // wave-uniform by construction
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(m) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void *p)
+{
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+
 template <int D, int KV, int OUT>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void attn_kernel(AttnParams p)
 {
     using SH = AttnShape<D>;
     using Raw = typename RawRow<KV>::T;
-    // two distinct arrays (not halves of one) so the compiler can tell the
-    // in-flight gather into one buffer from the reads of the other
-    __shared__ __attribute__((aligned(1024))) uint8_t bufA[SH::BUF_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t bufB[SH::BUF_BYTES];
-    // per-column bias (0 or -inf) and dequant scale of each buffer, kept out of
-    // the gather targets so writing them never waits on an in-flight gather
-    __shared__ float metaA[2 * kAttnTile], metaB[2 * kAttnTile];
-    __shared__ __attribute__((aligned(16))) float4 xch[4][4][64];   // [wave][j][lane] partial scores
+    constexpr int NP = KV == 2 ? 2 : 1;   // P terms per weight (e4m3: hi + lo)
+    // rotating tiles (bf16: 4, the gathers of tile t+3 are issued while tile
+    // t computes; e4m3: 3, rows pass through registers), each tile's
+    // per-column bias (0 or -inf) and dequant scale, and the row indices of
+    // the current chunk of columns
+    constexpr int DEPTH = KV == 0 ? 4 : 3;
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles[DEPTH][SH::TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) float metas[DEPTH][2 * kAttnTile];
+    __shared__ int sidx[kIdxChunk];
+    __shared__ float4 xs[4][2][64];          // partial scores for the partner wave
+    // bf16 P by [term][dq][nt][ch][lane]: the two column halves of one head
+    // tile sit 512 bytes apart, so a lane reads its B operand with one
+    // ds_read2_b64
+    __shared__ uint2 xp[NP][2][2][2][64];
+    __shared__ uint2 xq[NP][2][2][2][64];    // the same after a max change
+    __shared__ float xm[4][32];              // tile max of each owned head
+    __shared__ float xl[4][32];              // softmax sums at the end
+    __shared__ int xf[4];                    // bit 0: a first max, bit 1: a larger max
 
     // XCD-aware order: consecutive logical blocks (one token's splits, then
     // neighbouring tokens, which share window rows) stay on one XCD.
@@ -145,303 +186,415 @@ void attn_kernel(AttnParams p)
     const int split = lb - t * p.num_splits;
     const int c_begin = split * p.cols_per_split;
     const int c_end = min(p.n_cols, c_begin + p.cols_per_split);
-    const int n_tiles = c_end > c_begin ? (c_end - c_begin + kAttnTile - 1) / kAttnTile : 0;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-    const int hh = wave >> 1, dh = wave & 1;
-    const int hbase = blockIdx.y * kAttnHeadsPerBlock + hh * 32;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    const int dq = w & 1, ch = w >> 1;
+    const int hbase = blockIdx.y * kAttnHeadsPerBlock;
 
-    // Q as the B operand of S^T over this wave's head_dim half:
-    // qf[nt][s] = q[t, hbase + 16nt + l16, 32(dh*SK + s) + 8g .. +7]
-    uint4 qf[2][SH::SK];
+    // Q as the B operand of S^T over head_dim half dq:
+    // qf[j][s] = q[t, hbase + 16j + l16, D/2*dq + 32s + 8g .. +7]
+    uint4 qf[4][SH::SK];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int head = hbase + 16 * nt + l16;
+    for (int j = 0; j < 4; ++j) {
+        const int head = hbase + 16 * j + l16;
         const bool ok = head < p.H;
-        const uint16_t *qrow = p.q + (int64_t)t * p.q_st + (int64_t)(ok ? head : 0) * p.q_sh;
+        const uint16_t *qrow = p.q + (int64_t)t * p.q_st + (int64_t)(ok ? head : 0) * p.q_sh + (D / 2) * dq;
 #pragma unroll
         for (int s = 0; s < SH::SK; ++s)
-            qf[nt][s] = ok ? *(const uint4 *)(qrow + 32 * (dh * SH::SK + s) + 8 * g) : make_uint4(0, 0, 0, 0);
+            qf[j][s] = ok ? *(const uint4 *)(qrow + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0);
     }
     // finite data that invalid columns load instead of a pool row (their
     // scores are masked to -inf and their weights are 0)
     const uint8_t *safe_src = (const uint8_t *)(p.q + (int64_t)t * p.q_st);
 
+    // kernel arguments the lambdas below use, as plain scalars (capturing the
+    // argument struct by reference would place it in scratch memory)
+    const uint8_t *const win_pool = p.win, *const cmp_pool = p.cmp;
+    const int64_t win_rs = p.win_rs, cmp_rs = p.cmp_rs;
+    const float *const win_scale = p.win_scale, *const cmp_scale = p.cmp_scale;
+    const int n_win = p.n_win;
+    const float sl2 = p.sm_scale_log2;
+
     // gather role: instruction q of this wave covers tile rows
-    // 8*wave + q*RPI .. + RPI-1; this lane reads row grow(q), chunk slot gpos
+    // 8w + q*RPI .. + RPI-1; this lane reads row grow(q), chunk slot gpos
     const int32_t *idx_row = p.idx + (int64_t)t * p.idx_st;
     const int gpos = lane % SH::CH;
-    auto grow = [&](int q) { return 8 * wave + q * SH::RPI + lane / SH::CH; };
-    int ridx[SH::NQ];      // row indices of the next tile to be issued
-    Raw raw[SH::NQ];       // e4m3 only: codes of the next tile, widened when written
+    auto grow = [&](int q) __attribute__((always_inline)) { return 8 * w + q * SH::RPI + lane / SH::CH; };
+    Raw raw[SH::NQ];       // e4m3 only: codes of the issued tile, widened when landed
     float rsc[SH::NQ];
+    int cc = c_begin;      // first column of the current chunk
+    int n_tiles = 0;       // tiles of the current chunk
 
-    auto load_idx = [&](int tile) {
-#pragma unroll
-        for (int q = 0; q < SH::NQ; ++q) {
-            const int c = c_begin + tile * kAttnTile + grow(q);
-            ridx[q] = (tile < n_tiles && c < c_end) ? idx_row[c] : -1;
+    // issue gather instruction q of tile `tile` (of the current chunk) into
+    // buffer `bf`; the row index comes from the staged chunk
+    auto issue_row = [&](uint8_t *bf, float *meta, int tile, int q) __attribute__((always_inline)) {
+        const int rho = grow(q);
+        const int c = cc + tile * kAttnTile + rho;
+        const int ri = sidx[tile * kAttnTile + rho];
+        // one row per instruction: the index is wave-uniform, use an SGPR
+        const int r = SH::RPI == 1 ? __builtin_amdgcn_readfirstlane(ri) : ri;
+        const bool win = c < n_win;
+        const uint8_t *base = win ? win_pool : cmp_pool;
+        const int64_t rs = win ? win_rs : cmp_rs;
+        const int j = gpos ^ rswz(rho);
+        if constexpr (KV == 0) {
+            const uint8_t *src = r >= 0 ? base + (int64_t)r * rs + 16 * j : safe_src + 16 * gpos;
+            dma16(src, lds_offset(bf + (8 * w + q * SH::RPI) * 2 * D));
+        } else {
+            // unused columns: load the stand-in bytes but keep zero codes,
+            // since arbitrary bytes read as e4m3 may be NaN encodings
+            const uint8_t *src = r >= 0 ? base + (int64_t)r * rs + 8 * j : safe_src + 8 * gpos;
+            const Raw v = *(const Raw *)src;
+            raw[q] = r >= 0 ? v : Raw{0u, 0u};
+            rsc[q] = r >= 0 ? (win ? win_scale : cmp_scale)[r] : 0.0f;
         }
+        if (gpos == 0) meta[rho] = r >= 0 ? 0.0f : -INFINITY;
     };
-    // issue the tile whose indices sit in ridx into buffer `bf`
-    auto issue = [&](uint8_t *bf, float *meta, int tile) {
+    auto issue = [&](uint8_t *bf, float *meta, int tile) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < SH::NQ; ++q) {
-            const int rho = grow(q);
-            const int c = c_begin + tile * kAttnTile + rho;
-            // one row per instruction: the index is wave-uniform, use an SGPR
-            const int r = SH::RPI == 1 ? __builtin_amdgcn_readfirstlane(ridx[q]) : ridx[q];
-            const bool w = c < p.n_win;
-            const uint8_t *base = w ? p.win : p.cmp;
-            const int64_t rs = w ? p.win_rs : p.cmp_rs;
-            const int j = gpos ^ kswz(rho);
-            if constexpr (KV == 0) {
-                const uint8_t *src = r >= 0 ? base + (int64_t)r * rs + 16 * j : safe_src + 16 * gpos;
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)src,
-                    (__attribute__((address_space(3))) void *)(bf + (8 * wave + q * SH::RPI) * 2 * D), 16, 0, 0);
-            } else {
-                // unused columns: load the stand-in bytes but keep zero codes,
-                // since arbitrary bytes read as e4m3 may be NaN encodings
-                const uint8_t *src = r >= 0 ? base + (int64_t)r * rs + 8 * j : safe_src + 8 * gpos;
-                const Raw v = *(const Raw *)src;
-                raw[q] = r >= 0 ? v : Raw{0u, 0u};
-                rsc[q] = r >= 0 ? (w ? p.win_scale : p.cmp_scale)[r] : 0.0f;
-            }
-            if (gpos == 0) meta[rho] = r >= 0 ? 0.0f : -INFINITY;
-        }
+        for (int q = 0; q < SH::NQ; ++q) issue_row(bf, meta, tile, q);
     };
-    // e4m3: widen the registers of the issued tile into the buffer (after the
-    // current tile's compute, so the loads had that long to arrive)
-    auto land = [&](uint8_t *bf, float *meta) {
+    // e4m3: widen the registers of the issued tile into its buffer
+    auto land = [&](uint8_t *bf, float *meta) __attribute__((always_inline)) {
         if constexpr (KV == 2) {
             float *scl = meta + kAttnTile;
 #pragma unroll
             for (int q = 0; q < SH::NQ; ++q) {
-                *(uint4 *)(bf + (8 * wave + q * SH::RPI) * 2 * D + 16 * lane) = e4m3x8_to_bf16x8(raw[q]);
+                *(uint4 *)(bf + (8 * w + q * SH::RPI) * 2 * D + 16 * lane) = e4m3x8_to_bf16x8(raw[q]);
                 if (gpos == 0) scl[grow(q)] = rsc[q];
             }
         }
     };
 
-    f32x4 acc[SH::PM][2];
+    // O^T accumulators: acc[m][j] = O^T[d = D/4*w + 16m + 4g + i][head 16j + l16]
+    f32x4 acc[SH::PM][4];
 #pragma unroll
-    for (int m = 0; m < SH::PM; ++m) acc[m][0] = acc[m][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
+    for (int m = 0; m < SH::PM; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // running max of heads 16j + l16 (identical in every wave), and the sum
+    // over this lane's columns of the owned heads 32dq + 16nt + l16
+    float m_run[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    float l_run[2] = {0.0f, 0.0f};
 
-    auto compute = [&](const uint8_t *bf, const float *meta) {
-        const float *bias = meta;
-        const float *scl = meta + kAttnTile;
-        // --- S^T partial over this wave's head_dim half; rows
-        //     a(mt, m) = 8(m>>2) + 4mt + (m&3) of the tile
-        f32x4 sacc[2][2];
+    // LDS byte offsets within a tile.  S reads chunk (D/16)dq + 4s + g of row
+    // 16ch + l16; PV reads rows 16h + 4g + l16/4 at head_dim D/4*w + 16m +
+    // 4(l16%4).  The swizzle only touches the low 3 chunk bits, so each read
+    // is one of a few per-lane bases plus a constant.
+    int kb[2];
+    {
+        const int rho = 16 * ch + l16, sw = rswz(rho);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) sacc[mt][0] = sacc[mt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        {
-            const int rho0 = 8 * (l16 >> 2) + (l16 & 3);
-            const uint8_t *k0 = bf + rho0 * 2 * D, *k1 = bf + (rho0 + 4) * 2 * D;
-            const int ks0 = kswz(rho0), ks1 = kswz(rho0 + 4);
-            auto kfrag = [&](int s, int mt) {
-                const int chunk = 4 * (dh * SH::SK + s) + g;
-                return mt ? lds_b128(k1 + 16 * (chunk ^ ks1)) : lds_b128(k0 + 16 * (chunk ^ ks0));
-            };
-            uint4 f0[3], f1[3];   // fragments for k-steps s, s+1, s+2 (ring)
-            f0[0] = kfrag(0, 0);
-            f1[0] = kfrag(0, 1);
-            if (SH::SK > 1) {
-                f0[1] = kfrag(1, 0);
-                f1[1] = kfrag(1, 1);
+        for (int e = 0; e < 2; ++e) kb[e] = rho * 2 * D + 16 * (((D / 16) * dq + 4 * e + g) ^ sw);
+    }
+    constexpr int VB = SH::PM < 4 ? SH::PM : 4;
+    int vb[2][VB];
+    {
+        const int dsub = 4 * (l16 & 3);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = 16 * h + 4 * g + (l16 >> 2), vs = rswz(r);
+#pragma unroll
+            for (int mm = 0; mm < VB; ++mm) {
+                const int d = (D / 4) * w + 16 * mm + dsub;
+                vb[h][mm] = r * 2 * D + 16 * ((d >> 3) ^ vs) + 2 * (d & 7);
             }
-#pragma unroll
-            for (int s = 0; s < SH::SK; ++s) {
-                if (s + 2 < SH::SK) {
-                    f0[(s + 2) % 3] = kfrag(s + 2, 0);
-                    f1[(s + 2) % 3] = kfrag(s + 2, 1);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                sacc[0][0] = mfma16x16x32(f0[s % 3], qf[0][s], sacc[0][0]);
-                sacc[0][1] = mfma16x16x32(f0[s % 3], qf[1][s], sacc[0][1]);
-                sacc[1][0] = mfma16x16x32(f1[s % 3], qf[0][s], sacc[1][0]);
-                sacc[1][1] = mfma16x16x32(f1[s % 3], qf[1][s], sacc[1][1]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        // --- swap partial scores with the other head_dim half
-        {
-            float4 *mine = xch[wave][0];
-            mine[0 * 64 + lane] = make_float4(sacc[0][0][0], sacc[0][0][1], sacc[0][0][2], sacc[0][0][3]);
-            mine[1 * 64 + lane] = make_float4(sacc[0][1][0], sacc[0][1][1], sacc[0][1][2], sacc[0][1][3]);
-            mine[2 * 64 + lane] = make_float4(sacc[1][0][0], sacc[1][0][1], sacc[1][0][2], sacc[1][0][3]);
-            mine[3 * 64 + lane] = make_float4(sacc[1][1][0], sacc[1][1][1], sacc[1][1][2], sacc[1][1][3]);
-            __syncthreads();
-            const float4 *other = xch[wave ^ 1][0];
-            float4 o[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = other[j * 64 + lane];
-            // dh 0 adds mine + other, dh 1 adds other + mine: identical sums
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                f32x4 &sv = sacc[j >> 1][j & 1];
-                const f32x4 ov = f32x4{o[j].x, o[j].y, o[j].z, o[j].w};
-                sv = dh == 0 ? sv + ov : ov + sv;
-            }
-        }
-        // --- softmax; this lane: head hbase + 16nt + l16, columns 8g + k (k = 4mt + i)
-        float bb[8], csc[8];
-        {
-            const float4 b0 = *(const float4 *)(bias + 8 * g), b1 = *(const float4 *)(bias + 8 * g + 4);
-            bb[0] = b0.x; bb[1] = b0.y; bb[2] = b0.z; bb[3] = b0.w;
-            bb[4] = b1.x; bb[5] = b1.y; bb[6] = b1.z; bb[7] = b1.w;
-            if constexpr (KV == 2) {
-                const float4 s0 = *(const float4 *)(scl + 8 * g), s1 = *(const float4 *)(scl + 8 * g + 4);
-                csc[0] = s0.x; csc[1] = s0.y; csc[2] = s0.z; csc[3] = s0.w;
-                csc[4] = s1.x; csc[5] = s1.y; csc[6] = s1.z; csc[7] = s1.w;
-            }
-        }
-        // scores in log2 units; recomputed from sacc where needed instead of kept
-        auto score = [&](int nt, int k) {
-            float v = sacc[k >> 2][nt][k & 3] * p.sm_scale_log2;
-            if constexpr (KV == 2) v *= csc[k];
-            return v + bb[k];
-        };
-        float tmax[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            tmax[nt] = -INFINITY;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) tmax[nt] = fmaxf(tmax[nt], score(nt, k));
-        }
-        tmax[0] = group4_max(tmax[0]);
-        tmax[1] = group4_max(tmax[1]);
-        const bool raise0 = tmax[0] > m_run[0] + kRescaleSlack;
-        const bool raise1 = tmax[1] > m_run[1] + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(raise0 || raise1) != 0) {
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const bool raise = nt ? raise1 : raise0;
-                const float m_new = raise ? tmax[nt] : m_run[nt];
-                const float alpha = raise ? fast_exp2(m_run[nt] - m_new) : 1.0f;
-                m_run[nt] = m_new;
-                l_run[nt] *= alpha;
-#pragma unroll
-                for (int m = 0; m < SH::PM; ++m) agpr_scale(acc[m][nt], alpha);
-            }
-        }
-        uint4 pb[2], pl[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const float msub = m_run[nt] == -INFINITY ? 0.0f : m_run[nt];
-            float pr[8], psum = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                pr[k] = fast_exp2(score(nt, k) - msub);
-                psum += pr[k];
-            }
-            l_run[nt] += psum;
-            if constexpr (KV == 2) {
-                float hi[8], lo[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const float pp = pr[k] * csc[k];
-                    hi[k] = pp;
-                    lo[k] = pp - __uint_as_float(bf16_bits(pp) << 16);
-                }
-                pb[nt] = make_uint4(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]),
-                                    pack_bf16x2(hi[4], hi[5]), pack_bf16x2(hi[6], hi[7]));
-                pl[nt] = make_uint4(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
-                                    pack_bf16x2(lo[4], lo[5]), pack_bf16x2(lo[6], lo[7]));
-            } else {
-                pb[nt] = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                                    pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
-                pl[nt] = pb[nt];
-            }
-        }
-        // --- O^T += V^T P^T over this wave's head_dim half: A-operand rows
-        //     8g + 4h + (l16>>2), head_dim 16md + 4(l16&3)
-        {
-            const int trow0 = 8 * g + (l16 >> 2);
-            const uint8_t *va0 = bf + trow0 * 2 * D, *va1 = bf + (trow0 + 4) * 2 * D;
-            const int vs0 = kswz(trow0), vs1 = kswz(trow0 + 4);
-            const int dsub = 4 * (l16 & 3);
-            auto vfrag = [&](int m) {
-                const int d = 16 * (dh * SH::PM + m) + dsub;
-                const uint2 v0 = lds_tr16(va0 + 16 * ((d >> 3) ^ vs0) + 2 * (d & 7));
-                const uint2 v1 = lds_tr16(va1 + 16 * ((d >> 3) ^ vs1) + 2 * (d & 7));
-                return make_uint4(v0.x, v0.y, v1.x, v1.y);
-            };
-            uint4 vr[3];
-            vr[0] = vfrag(0);
-            if (SH::PM > 1) vr[1] = vfrag(1);
-#pragma unroll
-            for (int m = 0; m < SH::PM; ++m) {
-                if (m + 2 < SH::PM) vr[(m + 2) % 3] = vfrag(m + 2);
-                __builtin_amdgcn_sched_barrier(0);
-                const uint4 a = vr[m % 3];
-                acc[m][0] = mfma16x16x32(a, pb[0], acc[m][0]);
-                acc[m][1] = mfma16x16x32(a, pb[1], acc[m][1]);
-                if constexpr (KV == 2) {
-                    acc[m][0] = mfma16x16x32(a, pl[0], acc[m][0]);
-                    acc[m][1] = mfma16x16x32(a, pl[1], acc[m][1]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-    };
-
-    // wait until this wave's gathers for the next tile have landed in LDS
-    auto wait_gather = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-
-    if (n_tiles > 0) {
-        load_idx(0);
-        issue(bufA, metaA, 0);
-        land(bufA, metaA);
-        load_idx(1);
-        wait_gather();
-        __syncthreads();
-        for (int it = 0; it < n_tiles; it += 2) {
-            // tile it is in bufA; tile it+1 goes to bufB
-            if (it + 1 < n_tiles) {
-                issue(bufB, metaB, it + 1);
-                load_idx(it + 2);
-            }
-            compute(bufA, metaA);
-            if (it + 1 < n_tiles) land(bufB, metaB);
-            wait_gather();
-            __syncthreads();
-            if (it + 1 >= n_tiles) break;
-            // tile it+1 is in bufB; tile it+2 goes to bufA
-            if (it + 2 < n_tiles) {
-                issue(bufA, metaA, it + 2);
-                load_idx(it + 3);
-            }
-            compute(bufB, metaB);
-            if (it + 2 < n_tiles) land(bufA, metaA);
-            wait_gather();
-            __syncthreads();
         }
     }
 
+    // --- S^T over head_dim half dq for columns 16ch .. 16ch+15:
+    //     sacc[j] = S^T[col 16ch + 4g + i][head 16j + l16] (partial)
+    auto s_part = [&](const uint8_t *bf, f32x4 (&sacc)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto kfrag = [&](int s) __attribute__((always_inline)) { return lds_b128(bf + kb[s & 1] + 128 * (s >> 1)); };
+        uint4 f[3];
+        f[0] = kfrag(0);
+        if (SH::SK > 1) f[1] = kfrag(1);
+#pragma unroll
+        for (int s = 0; s < SH::SK; ++s) {
+            if (s + 2 < SH::SK) f[(s + 2) % 3] = kfrag(s + 2);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sacc[j] = mfma16x16x32(f[s % 3], qf[j][s], sacc[j]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // weights of the owned heads against the current max: per head tile nt,
+    // 4 columns packed as bf16 (and the lo terms for e4m3)
+    auto weights = [&](const float (&x)[2][4], const float (&csc)[4], float (&pr)[2][4], uint2 (&hi)[2],
+                       uint2 (&lo)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const float mr = dq ? m_run[2 + nt] : m_run[nt];
+            const float msub = mr == -INFINITY ? 0.0f : mr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pr[nt][i] = fast_exp2(x[nt][i] - msub);
+            if constexpr (KV == 2) {
+                float a[4], b[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    a[i] = pr[nt][i] * csc[i];
+                    b[i] = a[i] - __uint_as_float(bf16_bits(a[i]) << 16);
+                }
+                hi[nt] = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+                lo[nt] = make_uint2(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
+            } else {
+                hi[nt] = make_uint2(pack_bf16x2(pr[nt][0], pr[nt][1]), pack_bf16x2(pr[nt][2], pr[nt][3]));
+            }
+        }
+    };
+    auto put_p = [&](uint2 (*px)[2][2][2][64], const uint2 (&hi)[2], const uint2 (&lo)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            px[0][dq][nt][ch][lane] = hi[nt];
+            if constexpr (KV == 2) px[NP - 1][dq][nt][ch][lane] = lo[nt];
+        }
+    };
+
+    // --- O^T += V^T P^T for head_dim quarter w; P^T of head tile j comes from
+    //     the owners (j/2, ch = 0) and (j/2, ch = 1)
+    auto pv = [&](const uint8_t *bf, const uint2 (*px)[2][2][2][64], int dma_tile, uint8_t *nb3, float *nm3) __attribute__((always_inline)) {
+        uint4 pb[NP][4];
+#pragma unroll
+        for (int e = 0; e < NP; ++e)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint2 a = px[e][j >> 1][j & 1][0][lane], b = px[e][j >> 1][j & 1][1][lane];
+                pb[e][j] = make_uint4(a.x, a.y, b.x, b.y);
+            }
+        auto vfrag = [&](int m) __attribute__((always_inline)) {
+            const uint2 v0 = lds_tr16(bf + vb[0][m & 3] + 128 * (m >> 2));
+            const uint2 v1 = lds_tr16(bf + vb[1][m & 3] + 128 * (m >> 2));
+            return make_uint4(v0.x, v0.y, v1.x, v1.y);
+        };
+        uint4 vr[3];
+        vr[0] = vfrag(0);
+        if (SH::PM > 1) vr[1] = vfrag(1);
+#pragma unroll
+        for (int m = 0; m < SH::PM; ++m) {
+            if (m + 2 < SH::PM) vr[(m + 2) % 3] = vfrag(m + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            const uint4 a = vr[m % 3];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[m][j] = mfma16x16x32(a, pb[0][j], acc[m][j]);
+            if constexpr (KV == 2) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[m][j] = mfma16x16x32(a, pb[1][j], acc[m][j]);
+            }
+            // bf16: one gather instruction of tile t+3 per m-step, so the
+            // memory pipeline fills while the MFMAs run (NQ == PM)
+            if constexpr (KV == 0) {
+                if (dma_tile < n_tiles) issue_row(nb3, nm3, dma_tile, m);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // softmax inputs of the current tile, kept between the two halves of a step
+    struct Soft {
+        float x[2][4], csc[4], pr[2][4];
+    };
+
+    // first half of a tile: S, partial-score exchange, gather of tile t+2,
+    // weights against the current max and their publication.  Returns the
+    // workgroup's combined flags (bit 0: some head sees its first valid
+    // column, bit 1: some head's max grows by more than the slack).
+    auto front = [&](int tile, const uint8_t *cb, const float *cm, uint8_t *nb1, float *nm1, uint8_t *nb2,
+                     float *nm2, Soft &st) __attribute__((always_inline)) {
+        f32x4 sacc[4];
+        s_part(cb, sacc);
+        // send the partner's heads, keep mine (register arrays are only
+        // indexed by constants; the wave-uniform choice is a select)
+        f32x4 mine[2], theirs[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            mine[nt] = dq ? sacc[2 + nt] : sacc[nt];
+            theirs[nt] = dq ? sacc[nt] : sacc[2 + nt];
+        }
+        xs[w][0][lane] = make_float4(theirs[0][0], theirs[0][1], theirs[0][2], theirs[0][3]);
+        xs[w][1][lane] = make_float4(theirs[1][0], theirs[1][1], theirs[1][2], theirs[1][3]);
+        if constexpr (KV == 0) {
+            // tile t+1 has landed; the gathers of tile t+2 may stay in flight
+            if (tile + 2 < n_tiles) wait_vm<SH::NQ>();
+            else wait_vm<0>();
+            __syncthreads();
+        } else {
+            // tile t+1 arrived in registers: widen it into its buffer, then
+            // start tile t+2
+            wait_vm<0>();
+            if (tile + 1 < n_tiles) land(nb1, nm1);
+            __syncthreads();
+            if (tile + 2 < n_tiles) issue(nb2, nm2, tile + 2);
+        }
+        // --- softmax of heads 32dq + 16nt + l16, columns 16ch + 4g + i
+        {
+            const float4 o0 = xs[w ^ 1][0][lane], o1 = xs[w ^ 1][1][lane];
+            const float4 b4 = *(const float4 *)(cm + 16 * ch + 4 * g);
+            const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+            if constexpr (KV == 2) {
+                const float4 s4 = *(const float4 *)(cm + kAttnTile + 16 * ch + 4 * g);
+                st.csc[0] = s4.x; st.csc[1] = s4.y; st.csc[2] = s4.z; st.csc[3] = s4.w;
+            }
+            const float ov[2][4] = {{o0.x, o0.y, o0.z, o0.w}, {o1.x, o1.y, o1.z, o1.w}};
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v = (mine[nt][i] + ov[nt][i]) * sl2;
+                    if constexpr (KV == 2) v *= st.csc[i];
+                    st.x[nt][i] = v + bb[i];
+                }
+        }
+        float tmax[2];
+        int flag = 0;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            tmax[nt] = group4_max(fmaxf(fmaxf(st.x[nt][0], st.x[nt][1]), fmaxf(st.x[nt][2], st.x[nt][3])));
+            const float mr = dq ? m_run[2 + nt] : m_run[nt];
+            if (mr == -INFINITY) flag |= tmax[nt] > -INFINITY ? 1 : 0;
+            else flag |= tmax[nt] > mr + kRescaleSlack ? 2 : 0;
+        }
+        uint2 phi[2], plo[2];
+        weights(st.x, st.csc, st.pr, phi, plo);
+        put_p(xp, phi, plo);
+        if (g == 0) {
+            xm[w][l16] = tmax[0];
+            xm[w][16 + l16] = tmax[1];
+        }
+        const int wf = (__builtin_amdgcn_ballot_w64((flag & 1) != 0) ? 1 : 0) |
+                       (__builtin_amdgcn_ballot_w64((flag & 2) != 0) ? 2 : 0);
+        if (lane == 0) xf[w] = wf;
+        __syncthreads();
+        return __builtin_amdgcn_readfirstlane(xf[0] | xf[1] | xf[2] | xf[3]);
+    };
+
+    // second half: agree on new maxima if any head needs one (RESCALE: also
+    // from a finite max, which rescales O and the sums), then PV
+    auto back = [&](auto rescale_tag, int any, const uint8_t *cb, Soft &st, int dma_tile, uint8_t *nb3, float *nm3) __attribute__((always_inline)) {
+        constexpr bool RESCALE = decltype(rescale_tag)::value;
+        if (any) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float mt = fmaxf(xm[j >> 1][16 * (j & 1) + l16], xm[(j >> 1) + 2][16 * (j & 1) + l16]);
+                const float mr = m_run[j];
+                if constexpr (RESCALE) {
+                    const bool up = mt > mr + kRescaleSlack;   // also from -inf
+                    const float m_new = up ? mt : mr;
+                    const float alpha = up ? fast_exp2(mr - m_new) : 1.0f;
+                    m_run[j] = m_new;
+                    if (__builtin_amdgcn_ballot_w64(up && mr != -INFINITY) != 0) {
+#pragma unroll
+                        for (int m = 0; m < SH::PM; ++m) acc[m][j] *= alpha;
+                    }
+                    if ((j >> 1) == dq) l_run[j & 1] *= alpha;
+                } else {
+                    // only first maxima here: O and the sums of such a head
+                    // are still zero, nothing to rescale
+                    if (mr == -INFINITY && mt > -INFINITY) m_run[j] = mt;
+                }
+            }
+            uint2 phi[2], plo[2];
+            weights(st.x, st.csc, st.pr, phi, plo);
+            put_p(xq, phi, plo);
+            __syncthreads();
+        }
+        pv(cb, any ? xq : xp, dma_tile, nb3, nm3);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) l_run[nt] += (st.pr[nt][0] + st.pr[nt][1]) + (st.pr[nt][2] + st.pr[nt][3]);
+    };
+
+    using Fast = std::integral_constant<bool, false>;
+    using Slow = std::integral_constant<bool, true>;
+    // columns are taken in chunks whose row indices are staged in LDS
+    for (; cc < c_end; cc += kIdxChunk) {
+        const int cn = min(c_end - cc, kIdxChunk);
+        n_tiles = (cn + kAttnTile - 1) / kAttnTile;
+        __syncthreads();   // the previous chunk's indices are no longer read
+        for (int i = tid; i < n_tiles * kAttnTile; i += kThreads) sidx[i] = i < cn ? idx_row[cc + i] : -1;
+        // a wait the compiler sees: Q and the index loads are complete, so no
+        // wait for them is left inside the tile loops (s_waitcnt vmcnt(0))
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        // prologue: the first DEPTH-1 tiles
+        issue(tiles[0], metas[0], 0);
+        if constexpr (KV == 2) {
+            wait_vm<0>();
+            land(tiles[0], metas[0]);
+        }
+        if (n_tiles > 1) issue(tiles[1], metas[1], 1);
+        if constexpr (KV == 0) {
+            if (n_tiles > 2) issue(tiles[2], metas[2], 2);
+            wait_vm<0>();
+        }
+        __syncthreads();
+        int bi[DEPTH];
+#pragma unroll
+        for (int k = 0; k < DEPTH; ++k) bi[k] = k;
+        auto rotate = [&]() __attribute__((always_inline)) {
+            const int b0 = bi[0];
+#pragma unroll
+            for (int k = 0; k + 1 < DEPTH; ++k) bi[k] = bi[k + 1];
+            bi[DEPTH - 1] = b0;
+        };
+        auto fr = [&](int it, Soft &st) __attribute__((always_inline)) {
+            return front(it, tiles[bi[0]], metas[bi[0]], tiles[bi[1]], metas[bi[1]], tiles[bi[2]], metas[bi[2]], st);
+        };
+        auto bk = [&](auto tag, int any, int it, Soft &st) __attribute__((always_inline)) {
+            back(tag, any, tiles[bi[0]], st, it + 3, tiles[bi[DEPTH - 1]], metas[bi[DEPTH - 1]]);
+        };
+        Soft st;
+        int it = 0, any = 0;
+        // fast loop: no rescale of O in its body (a max that grows by more
+        // than the slack is rare and leaves for the loop below)
+        for (; it < n_tiles; ++it) {
+            any = fr(it, st);
+            if (any & 2) break;
+            bk(Fast{}, any, it, st);
+            rotate();
+        }
+        if (it < n_tiles) {
+            bk(Slow{}, any, it, st);
+            rotate();
+            for (++it; it < n_tiles; ++it) {
+                any = fr(it, st);
+                bk(Slow{}, any, it, st);
+                rotate();
+            }
+        }
+    }
+
+    // softmax sums: owners reduce over their columns, everyone adds the two
+    // column halves of each head in a fixed order
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-        const int head = hbase + 16 * nt + l16;
-        const float l_tot = group4_sum(l_run[nt]);
+        const float ls = group4_sum(l_run[nt]);
+        if (g == 0) xl[w][16 * nt + l16] = ls;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int head = hbase + 16 * j + l16;
+        const float l_tot = xl[j >> 1][16 * (j & 1) + l16] + xl[(j >> 1) + 2][16 * (j & 1) + l16];
         if (head >= p.H) continue;
-        const int d0 = 16 * dh * SH::PM + 4 * g;
+        const int d0 = (D / 4) * w + 4 * g;
         if (p.num_splits == 1) {
             const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
             if constexpr (OUT == 1) {
                 float *o = (float *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d0;
 #pragma unroll
                 for (int m = 0; m < SH::PM; ++m) {
-                    const f32x4 v = acc[m][nt] * inv;
+                    const f32x4 v = acc[m][j] * inv;
                     *(float4 *)(o + 16 * m) = make_float4(v[0], v[1], v[2], v[3]);
                 }
             } else {
                 uint16_t *o = (uint16_t *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d0;
 #pragma unroll
                 for (int m = 0; m < SH::PM; ++m) {
-                    const f32x4 v = acc[m][nt] * inv;
+                    const f32x4 v = acc[m][j] * inv;
                     *(uint2 *)(o + 16 * m) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 }
             }
@@ -450,8 +603,8 @@ void attn_kernel(AttnParams p)
             float *o = p.part_o + slot * D + d0;
 #pragma unroll
             for (int m = 0; m < SH::PM; ++m)
-                *(float4 *)(o + 16 * m) = make_float4(acc[m][nt][0], acc[m][nt][1], acc[m][nt][2], acc[m][nt][3]);
-            if (g == 0 && dh == 0) *(float2 *)(p.part_ml + slot * 2) = make_float2(m_run[nt], l_tot);
+                *(float4 *)(o + 16 * m) = make_float4(acc[m][j][0], acc[m][j][1], acc[m][j][2], acc[m][j][3]);
+            if (g == 0 && w == 0) *(float2 *)(p.part_ml + slot * 2) = make_float2(m_run[j], l_tot);
         }
     }
 }

@@ -38,8 +38,11 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
     __bf16 b = (__bf16)x;
     return (uint32_t)__builtin_bit_cast(uint16_t, b);
 }
+// two floats -> packed bf16 pair (lo in bits 0-15), one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return bf16_bits(lo) | (bf16_bits(hi) << 16);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 b = __builtin_convertvector((f32x2{lo, hi}), bf16x2);
+    return __builtin_bit_cast(uint32_t, b);
 }
 
 // byte-select permute of two dwords: selector bytes 0-3 pick from `lo`,
