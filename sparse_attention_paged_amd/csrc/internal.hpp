@@ -59,9 +59,9 @@ struct TopkParams {
     int B, N, k;
     int32_t *out;
     int64_t out_sb;
-    void *workspace;                 // 2 * topk_slot_bytes(B, N, k) bytes
+    void *workspace;                 // topk_workspace_bytes(B, N, k) bytes
 };
-size_t topk_slot_bytes(int B, int N, int k);   // one of the two ping-pong halves
+size_t topk_workspace_bytes(int B, int N, int k);
 hipError_t launch_topk(const TopkParams &p, hipStream_t s);
 
 struct IdxBuildParams {

@@ -235,7 +235,7 @@ int sap_indexer_logits_packed(const void *q, int64_t q_stride_b,
 size_t sap_topk_workspace_bytes(int B, int N, int k)
 {
     if (B <= 0 || N <= 0 || k < 1 || k > 4096) return 0;
-    return 2 * sap::topk_slot_bytes(B, N, k);
+    return sap::topk_workspace_bytes(B, N, k);
 }
 
 int sap_topk_select(const float *logits, int64_t stride_b, const int32_t *n_valid,

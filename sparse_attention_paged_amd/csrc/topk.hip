@@ -6,34 +6,39 @@
 // with -1 (the index top-k of "perf(kernel): keep 16-byte kv loads in dsv4
 // sparse attention and unroll gated pool", Kernel time).
 //
-// One 1024-thread workgroup per row.  Values become order-preserving 32-bit
-// keys (0 = not a candidate).
-//  1. Threshold estimate: a strided sample of up to 4096 keys gives, by radix
-//     select, a key tau expected to have about 2k row entries at or above it
-//     (skipped when the whole row fits the candidate buffer).
-//  2. The row is streamed through registers in coalesced chunks; entries with
-//     key >= tau are compacted into an LDS candidate buffer.
-//  3. If tau was too high (fewer than k survivors) or the buffer overflowed,
-//     the exact answer is computed by radix select over the whole row
-//     streamed from memory -- slower, never wrong.
-//  4. Radix select (4 passes of 8 bits, 16 sub-histograms so equal digits do
-//     not serialise on one LDS word) finds the k-th largest key T; if more
-//     entries equal T than are needed, a second radix select over their
-//     indices keeps the lowest ones.
-//  5. The selected indices (<= k) are sorted in LDS by a bitonic network and
-//     written out, padded with -1.
+// Values become order-preserving 32-bit keys (0 = not a candidate).  The
+// selection core runs in one 512-thread workgroup on keys held in registers,
+// each thread owning a contiguous run of positions:
+//  - radix select finds the prefix of the k-th largest key.  It starts below
+//    the bits every candidate shares (found by AND/OR reductions), takes 8
+//    bits per pass with one private LDS histogram per wave (no atomics shared
+//    between waves), and stops as soon as the bin holding the k-th key is
+//    taken whole;
+//  - the selected positions are written through one order-preserving block
+//    scan of (greater, equal) counts, so the output is already in ascending
+//    index order -- no sort.
+// Wave-level scans and reductions use DPP row shifts and broadcasts.
+// Rows of up to 16384 entries are selected directly.  Longer rows take two
+// launches: a filter launch where each workgroup derives the same threshold
+// from a fixed strided sample of the row and compacts the keys of its 4096
+// positions at or above it into its own slot, then a select launch that
+// gathers the slots (in position order) and runs the core on them.  If the
+// sample's threshold was too high (fewer than k keys at or above it) or a
+// slot overflowed, the select launch falls back to radix select over the row
+// streamed from memory -- slower, never wrong.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace sap {
 namespace {
 
-constexpr int kT = 1024;                 // threads per workgroup
-constexpr int kWaves = kT / kWave;
-constexpr int kCap = 8192;               // LDS candidate capacity
-constexpr int kSample = 4096;
-constexpr int kChunkPer = 16;            // keys per thread per streamed chunk
-constexpr int kChunk = kT * kChunkPer;
+constexpr int kT = 512;                  // threads per workgroup
+constexpr int kW = kT / kWave;           // waves per workgroup
+constexpr int kDirectMax = 16384;        // rows selected in one launch (32 keys per thread)
+constexpr int kChunk = 4096;             // positions per filter workgroup (8 keys per thread)
+constexpr int kSlotCap = 2048;           // candidates one filter workgroup may keep
+constexpr int kMaxChunks = 4096;         // two-launch path: N <= kChunk * kMaxChunks
+constexpr int kSample = 4096;            // strided sample that sets the filter threshold
 constexpr int kMaxK = 4096;
 
 __device__ __forceinline__ uint32_t order_key(float v)
@@ -43,265 +48,452 @@ __device__ __forceinline__ uint32_t order_key(float v)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // >= 0x00800000 otherwise
 }
 
-struct Smem {
-    uint32_t hist[16 * 256];
+struct Shared {
+    uint32_t hist[kW][256];
     uint32_t tot[256];
-    uint32_t cand_key[kCap];
-    int32_t cand_idx[kCap];
-    int32_t sel[kMaxK];
-    int red[kWaves];
-    int misc[8];
+    int red[2 * kW];
+    int misc[4];
 };
 
-__device__ __forceinline__ int block_sum(int v, Smem &s)
+// exclusive prefix sum over the workgroup in thread order; total to all
+__device__ int block_excl_scan(int v, Shared &s, int &total)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-    if (lane == 0) s.red[wave] = v;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int x = wave_incl_sum(v);
+    if (lane == 63) s.red[w] = x;
     __syncthreads();
-    int t = 0;
+    int base = 0, t = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) t += s.red[w];
-    __syncthreads();
-    return t;
-}
-
-__device__ __forceinline__ int block_excl_scan(int v, Smem &s, int &total)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) s.red[wave] = x;
-    __syncthreads();
-    int base = 0;
-    total = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        const int r = s.red[w];
-        base += (w < wave) ? r : 0;
-        total += r;
+    for (int i = 0; i < kW; ++i) {
+        const int r = s.red[i];
+        base += i < w ? r : 0;
+        t += r;
     }
     __syncthreads();
+    total = t;
     return base + x - v;
 }
 
-// Radix select over the keys a visitor presents: returns the key T of the
-// kk-th largest nonzero key and how many entries equal to T belong to the
-// top kk.  `visit(f)` calls f(key) for every key this thread holds.
-template <class Visit>
-__device__ uint32_t radix_kth(Visit visit, int kk, Smem &s, int &need_eq)
+__device__ void block_and_or(uint32_t &a, uint32_t &o, Shared &s)
 {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t prefix = 0u, mask = 0u;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    a = wave_last(wave_scan_dpp(a, ~0u, [](uint32_t x, uint32_t y) { return x & y; }));
+    o = wave_last(wave_scan_dpp(o, 0u, [](uint32_t x, uint32_t y) { return x | y; }));
+    if (lane == 0) {
+        s.red[w] = (int)a;
+        s.red[kW + w] = (int)o;
+    }
+    __syncthreads();
+    a = ~0u;
+    o = 0u;
+#pragma unroll
+    for (int i = 0; i < kW; ++i) {
+        a &= (uint32_t)s.red[i];
+        o |= (uint32_t)s.red[kW + i];
+    }
+    __syncthreads();
+}
+
+// Outcome of a radix select: keys with (key & M) > P are selected; of the
+// cnt_eq keys with (key & M) == P, the rem with the lowest positions are.
+struct Sel {
+    uint32_t P, M;
+    int rem;
+};
+
+// Radix select of the kk-th largest nonzero key (1 <= kk <= number of
+// nonzero keys).  for_each(f) calls f(key) for every key of the row.
+template <class ForEach>
+__device__ Sel radix_select(ForEach for_each, int kk, Shared &s)
+{
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    uint32_t a = ~0u, o = 0u;
+    for_each([&](uint32_t key) {
+        if (key) {
+            a &= key;
+            o |= key;
+        }
+    });
+    block_and_or(a, o, s);
+    const uint32_t diff = a ^ o;
+    if (diff == 0u) return Sel{a, ~0u, kk};   // every candidate has the same key
+    int hb = 31 - __builtin_clz(diff);
+    uint32_t M = ~((2u << hb) - 1u);          // hb == 31: 2u << 31 == 0, M == 0
+    uint32_t P = a & M;
     int rem = kk;
-    uint32_t *myh = s.hist + (lane & 15) * 256;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 16 * 256; i += kT) s.hist[i] = 0u;
-        __syncthreads();
-        visit([&](uint32_t key) {
-            if (key != 0u && (key & mask) == prefix) atomicAdd(&myh[(key >> shift) & 255u], 1u);
+    uint32_t *h = s.hist[w];
+    for (;;) {
+        const int lo = hb >= 7 ? hb - 7 : 0;
+        const uint32_t dm = (1u << (hb - lo + 1)) - 1u;
+        // this wave's histogram: cleared and filled by the wave alone (its
+        // LDS operations stay in order), read by all after the barrier
+        for (int i = lane; i < 256; i += kWave) h[i] = 0u;
+        for_each([&](uint32_t key) {
+            if (key && (key & M) == P) atomicAdd(&h[(key >> lo) & dm], 1u);
         });
         __syncthreads();
         if (tid < 256) {
             uint32_t t = 0;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) t += s.hist[j * 256 + tid];
+            for (int i = 0; i < kW; ++i) t += s.hist[i][tid];
             s.tot[tid] = t;
         }
         __syncthreads();
-        if (wave == 0) {
-            const int c = (int)(s.tot[4 * lane] + s.tot[4 * lane + 1] + s.tot[4 * lane + 2] + s.tot[4 * lane + 3]);
-            int x = c;   // suffix sum: entries in bins >= 4*lane
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) {
-                const int y = __shfl_down(x, off, kWave);
-                if (lane + off < kWave) x += y;
-            }
+        if (w == 0) {
+            // lane l covers bins 4l .. 4l+3; x = keys in bins >= 4l
+            const int c0 = (int)s.tot[4 * lane], c1 = (int)s.tot[4 * lane + 1];
+            const int c2 = (int)s.tot[4 * lane + 2], c3 = (int)s.tot[4 * lane + 3];
+            const int c = c0 + c1 + c2 + c3;
+            const int pre = wave_incl_sum(c);                      // bins < 4l+4
+            const int x = (int)wave_last((uint32_t)pre) - pre + c;   // bins >= 4l
             if (x >= rem && x - c < rem) {
-                int above = x - c, bin = 4 * lane;
-                for (int bb = 4 * lane + 3; bb >= 4 * lane; --bb) {
-                    if (above + (int)s.tot[bb] >= rem) { bin = bb; break; }
-                    above += (int)s.tot[bb];
+                int above = x - c, d = 4 * lane;
+                const int cb[4] = {c0, c1, c2, c3};
+#pragma unroll
+                for (int bb = 3; bb >= 0; --bb) {
+                    if (above + cb[bb] >= rem) {
+                        d = 4 * lane + bb;
+                        break;
+                    }
+                    above += cb[bb];
                 }
-                s.misc[0] = bin;
+                s.misc[0] = d;
                 s.misc[1] = above;
+                s.misc[2] = (int)s.tot[d];
             }
         }
         __syncthreads();
-        prefix |= (uint32_t)s.misc[0] << shift;
-        mask |= 255u << shift;
+        const int d = s.misc[0];
         rem -= s.misc[1];
-        __syncthreads();
+        const int cd = s.misc[2];
+        P |= (uint32_t)d << lo;
+        M |= dm << lo;
+        if (cd == rem || lo == 0) return Sel{P, M, rem};
+        hb = lo - 1;
     }
-    need_eq = rem;
-    return prefix;
 }
 
-// Ascending bitonic sort of s.sel[0 .. n) (n <= kMaxK), padding with INT_MAX.
-__device__ void sort_sel(Smem &s, int n)
+__device__ __forceinline__ bool sel_gt(uint32_t key, const Sel &q) { return key && (key & q.M) > q.P; }
+__device__ __forceinline__ bool sel_eq(uint32_t key, const Sel &q) { return key && (key & q.M) == q.P; }
+
+// Writes the selected positions of a block of KPT keys per thread in
+// position order: a selected key's slot is the number of greater keys before
+// it plus min(equal keys before it, rem).  One scan of both counts (16 bits
+// each) gives both.  gt_seen / eq_seen carry the counts of earlier blocks.
+template <int KPT, class IdxOf>
+__device__ void emit_block(const uint32_t (&key)[KPT], IdxOf idx_of, const Sel &q, int32_t *out, int &gt_seen,
+                           int &eq_seen, Shared &s)
 {
-    int m = 1;
-    while (m < n) m <<= 1;
-    for (int i = n + threadIdx.x; i < m; i += kT) s.sel[i] = 0x7FFFFFFF;
-    __syncthreads();
-    for (int size = 2; size <= m; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < m / 2; i += kT) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const bool up = ((lo & size) == 0);
-                const int a = s.sel[lo], b = s.sel[hi];
-                if ((a > b) == up) { s.sel[lo] = b; s.sel[hi] = a; }
-            }
-            __syncthreads();
+    int n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        n_gt += sel_gt(key[j], q);
+        n_eq += sel_eq(key[j], q);
+    }
+    int tot;
+    const int before = block_excl_scan(n_gt | (n_eq << 16), s, tot);
+    int g = gt_seen + (before & 0xFFFF), e = eq_seen + (before >> 16);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        if (sel_gt(key[j], q)) {
+            out[g + min(e, q.rem)] = idx_of(j);
+            ++g;
+        } else if (sel_eq(key[j], q)) {
+            if (e < q.rem) out[g + e] = idx_of(j);
+            ++e;
         }
     }
+    gt_seen += tot & 0xFFFF;
+    eq_seen += tot >> 16;
 }
 
-__global__ __launch_bounds__(kT) void topk_row_kernel(TopkParams p)
+__device__ void pad_out(int32_t *out, int from, int k)
 {
-    __shared__ Smem s;
-    const int b = blockIdx.x, tid = threadIdx.x;
+    for (int i = from + (int)threadIdx.x; i < k; i += kT) out[i] = -1;
+}
+
+// KPT consecutive keys of positions base + tid*KPT .. from row x (n valid)
+template <int KPT>
+__device__ void load_keys(const float *x, int64_t base, int n, uint32_t (&key)[KPT])
+{
+    const int64_t p0 = base + (int64_t)threadIdx.x * KPT;
+    const bool vec = ((reinterpret_cast<uintptr_t>(x) & 15u) == 0u) && (KPT % 4 == 0);
+    if (vec && p0 + KPT <= n) {
+#pragma unroll
+        for (int j = 0; j < KPT; j += 4) {
+            const float4 v = *(const float4 *)(x + p0 + j);
+            key[j] = order_key(v.x);
+            key[j + 1] = order_key(v.y);
+            key[j + 2] = order_key(v.z);
+            key[j + 3] = order_key(v.w);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) key[j] = p0 + j < n ? order_key(x[p0 + j]) : 0u;
+    }
+}
+
+// the whole row streamed from memory: every pass reads it again
+__device__ void select_streaming(const float *x, int nv, int k, int32_t *out, Shared &s)
+{
+    constexpr int KPT = 8;
+    constexpr int BLK = kT * KPT;
+    auto for_each = [&](auto f) {
+        for (int base = 0; base < nv; base += BLK) {
+            uint32_t key[KPT];
+            load_keys<KPT>(x, base, nv, key);
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) f(key[j]);
+        }
+    };
+    int nz = 0;
+    for_each([&](uint32_t key) { nz += key != 0u; });
+    int valid;
+    block_excl_scan(nz, s, valid);
+    const int kk = min(k, valid);
+    int gt_seen = 0, eq_seen = 0;
+    if (kk > 0) {
+        const Sel q = radix_select(for_each, kk, s);
+        for (int base = 0; base < nv; base += BLK) {
+            uint32_t key[KPT];
+            load_keys<KPT>(x, base, nv, key);
+            const int p0 = base + (int)threadIdx.x * KPT;
+            emit_block<KPT>(key, [&](int j) { return p0 + j; }, q, out, gt_seen, eq_seen, s);
+        }
+    }
+    pad_out(out, kk, k);
+}
+
+// rows of at most kT * KPT positions, keys in registers
+template <int KPT>
+__global__ __launch_bounds__(kT) void topk_direct_kernel(TopkParams p)
+{
+    __shared__ Shared s;
+    const int b = blockIdx.x;
+    const float *x = p.x + (int64_t)b * p.x_sb;
+    int32_t *out = p.out + (int64_t)b * p.out_sb;
+    int nv = p.n_valid ? p.n_valid[b] : p.N;
+    nv = min(max(nv, 0), p.N);
+    uint32_t key[KPT];
+    load_keys<KPT>(x, 0, nv, key);
+    int nz = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) nz += key[j] != 0u;
+    int valid;
+    block_excl_scan(nz, s, valid);
+    const int kk = min(p.k, valid);
+    int gt_seen = 0, eq_seen = 0;
+    if (kk > 0) {
+        auto for_each = [&](auto f) {
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) f(key[j]);
+        };
+        const Sel q = radix_select(for_each, kk, s);
+        const int p0 = (int)threadIdx.x * KPT;
+        emit_block<KPT>(key, [&](int j) { return p0 + j; }, q, out, gt_seen, eq_seen, s);
+    }
+    pad_out(out, kk, p.k);
+}
+
+// workspace of the two-launch path, per row: chunk counts, the sample
+// threshold, and per chunk kSlotCap keys and positions
+struct TopkWs {
+    int *count;        // [B][nch]
+    uint32_t *tau;     // [B]
+    uint32_t *key;     // [B][nch][kSlotCap]
+    int32_t *pos;      // [B][nch][kSlotCap]
+};
+
+__host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+__host__ __device__ inline TopkWs topk_ws(void *base, int B, int nch)
+{
+    uint8_t *p = (uint8_t *)base;
+    TopkWs w;
+    w.count = (int *)p;
+    p += align256((size_t)B * nch * 4);
+    w.tau = (uint32_t *)p;
+    p += align256((size_t)B * 4);
+    w.key = (uint32_t *)p;
+    p += align256((size_t)B * nch * kSlotCap * 4);
+    w.pos = (int32_t *)p;
+    return w;
+}
+
+__host__ __device__ inline size_t topk_ws_size(int B, int nch)
+{
+    return align256((size_t)B * nch * 4) + align256((size_t)B * 4) + 2 * align256((size_t)B * nch * kSlotCap * 4);
+}
+
+// filter launch: grid (chunks, B)
+__global__ __launch_bounds__(kT) void topk_filter_kernel(TopkParams p, int nch)
+{
+    __shared__ Shared s;
+    const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const float *x = p.x + (int64_t)b * p.x_sb;
     int nv = p.n_valid ? p.n_valid[b] : p.N;
     nv = min(max(nv, 0), p.N);
-    const int k = p.k;
+    const TopkWs ws = topk_ws(p.workspace, p.B, nch);
 
-    // 1. threshold estimate
+    // threshold from the fixed strided sample (identical in every chunk)
     uint32_t tau = 1u;
-    if (nv > kCap) {
-        const int S = kSample;
-        const int want = min(S, (int)(((int64_t)2 * k * S + nv - 1) / nv) + 4);
-        uint32_t sk[kSample / kT];
+    if (nv > kSample) {
+        constexpr int SPT = kSample / kT;
+        uint32_t sk[SPT];
 #pragma unroll
-        for (int j = 0; j < kSample / kT; ++j) {
-            const int si = j * kT + tid;
-            sk[j] = order_key(x[(int64_t)si * nv / S]);
-        }
-        int cnt = 0;
+        for (int j = 0; j < SPT; ++j) sk[j] = order_key(x[(int64_t)(tid * SPT + j) * nv / kSample]);
+        int nz = 0;
 #pragma unroll
-        for (int j = 0; j < kSample / kT; ++j) cnt += sk[j] != 0u;
-        const int ns = block_sum(cnt, s);
+        for (int j = 0; j < SPT; ++j) nz += sk[j] != 0u;
+        int ns;
+        block_excl_scan(nz, s, ns);
+        const int want = min(kSample, (int)(((int64_t)2 * p.k * kSample + nv - 1) / nv) + 16);
         if (ns >= want) {
-            int ne;
-            tau = radix_kth([&](auto f) {
+            auto for_each = [&](auto f) {
 #pragma unroll
-                for (int j = 0; j < kSample / kT; ++j) f(sk[j]);
-            }, want, s, ne);
+                for (int j = 0; j < SPT; ++j) f(sk[j]);
+            };
+            tau = radix_select(for_each, want, s).P;   // low bits zero: key >= tau <=> prefix >= P
+            if (tau == 0u) tau = 1u;
         }
     }
+    if (c == 0 && tid == 0) ws.tau[b] = tau;
 
-    // 2. stream the row, compact entries with key >= tau
-    int n_c = 0;            // candidates kept (block-uniform)
-    bool overflow = false;
-    for (int base = 0; base < nv; base += kChunk) {
-        uint32_t kv[kChunkPer];
-        int mine = 0;
+    constexpr int KPT = kChunk / kT;
+    uint32_t key[KPT];
+    const int64_t base = (int64_t)c * kChunk;
+    load_keys<KPT>(x, base, nv, key);
+    int n = 0;
 #pragma unroll
-        for (int j = 0; j < kChunkPer; ++j) {
-            const int i = base + j * kT + tid;
-            kv[j] = i < nv ? order_key(x[i]) : 0u;
-            mine += kv[j] != 0u && kv[j] >= tau;
-        }
-        int tot;
-        int pos = n_c + block_excl_scan(mine, s, tot);
-        if (n_c + tot > kCap) {
-            overflow = true;
-            break;
-        }
+    for (int j = 0; j < KPT; ++j) {
+        key[j] = key[j] >= tau ? key[j] : 0u;
+        n += key[j] != 0u;
+    }
+    int total;
+    int o = block_excl_scan(n, s, total);
+    const size_t slot = ((size_t)b * nch + c) * kSlotCap;
+    if (total <= kSlotCap) {
 #pragma unroll
-        for (int j = 0; j < kChunkPer; ++j) {
-            if (kv[j] != 0u && kv[j] >= tau) {
-                s.cand_key[pos] = kv[j];
-                s.cand_idx[pos] = base + j * kT + tid;
-                ++pos;
+        for (int j = 0; j < KPT; ++j)
+            if (key[j]) {
+                ws.key[slot + o] = key[j];
+                ws.pos[slot + o] = (int32_t)(base + tid * KPT + j);
+                ++o;
             }
-        }
-        n_c += tot;
     }
-    __syncthreads();
-
-    // 3./4. exact k-th key over the candidates (or the whole row)
-    const bool whole = overflow || (tau > 1u && n_c < k);
-    int kk;
-    uint32_t T;
-    int need_eq;
-    if (!whole) {
-        kk = min(k, n_c);
-        T = kk > 0 ? radix_kth([&](auto f) {
-                for (int i = tid; i < n_c; i += kT) f(s.cand_key[i]);
-            }, kk, s, need_eq) : 0xFFFFFFFFu;
-    } else {
-        int cnt = 0;
-        for (int i = tid; i < nv; i += kT) cnt += order_key(x[i]) != 0u;
-        kk = min(k, block_sum(cnt, s));
-        T = kk > 0 ? radix_kth([&](auto f) {
-                for (int i = tid; i < nv; i += kT) f(order_key(x[i]));
-            }, kk, s, need_eq) : 0xFFFFFFFFu;
-    }
-
-    // ties at T: keep the need_eq lowest indices
-    uint32_t imax = 0x7FFFFFFFu;
-    if (kk > 0) {
-        int eq = 0;
-        if (!whole) {
-            for (int i = tid; i < n_c; i += kT) eq += s.cand_key[i] == T;
-        } else {
-            for (int i = tid; i < nv; i += kT) eq += order_key(x[i]) == T;
-        }
-        const int n_eq = block_sum(eq, s);
-        if (n_eq > need_eq) {
-            int one;
-            uint32_t t2;
-            if (!whole) {
-                t2 = radix_kth([&](auto f) {
-                    for (int i = tid; i < n_c; i += kT) f(s.cand_key[i] == T ? ~(uint32_t)s.cand_idx[i] : 0u);
-                }, need_eq, s, one);
-            } else {
-                t2 = radix_kth([&](auto f) {
-                    for (int i = tid; i < nv; i += kT) f(order_key(x[i]) == T ? ~(uint32_t)i : 0u);
-                }, need_eq, s, one);
-            }
-            imax = ~t2;
-        }
-    }
-
-    // 5. collect, sort, write
-    if (tid == 0) s.misc[2] = 0;
-    __syncthreads();
-    if (kk > 0) {
-        auto take = [&](uint32_t key, int idx) {
-            if (key > T || (key == T && (uint32_t)idx <= imax)) {
-                const int at = atomicAdd(&s.misc[2], 1);
-                if (at < kMaxK) s.sel[at] = idx;
-            }
-        };
-        if (!whole) {
-            for (int i = tid; i < n_c; i += kT) take(s.cand_key[i], s.cand_idx[i]);
-        } else {
-            for (int i = tid; i < nv; i += kT) take(order_key(x[i]), i);
-        }
-    }
-    __syncthreads();
-    const int n_sel = min(s.misc[2], kk);
-    sort_sel(s, n_sel);
-    int32_t *o = p.out + (int64_t)b * p.out_sb;
-    for (int i = tid; i < k; i += kT) o[i] = i < n_sel ? s.sel[i] : -1;
+    if (tid == 0) ws.count[(size_t)b * nch + c] = total;
 }
+
+// select launch: grid (B)
+__global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
+{
+    constexpr int KPT = kDirectMax / kT;
+    __shared__ Shared s;
+    __shared__ uint32_t ckey[kDirectMax];
+    __shared__ int32_t cpos[kDirectMax];
+    __shared__ int offs[kMaxChunks];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const float *x = p.x + (int64_t)b * p.x_sb;
+    int32_t *out = p.out + (int64_t)b * p.out_sb;
+    int nv = p.n_valid ? p.n_valid[b] : p.N;
+    nv = min(max(nv, 0), p.N);
+    const TopkWs ws = topk_ws(p.workspace, p.B, nch);
+    const int *cnt = ws.count + (size_t)b * nch;
+
+    // slot offsets in chunk (= position) order
+    constexpr int CPT = kMaxChunks / kT;
+    int cl[CPT], local = 0, over = 0;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int ci = tid * CPT + j;
+        cl[j] = ci < nch ? cnt[ci] : 0;
+        over |= cl[j] > kSlotCap;
+        local += cl[j];
+    }
+    int total;
+    int o = block_excl_scan(local, s, total);
+    int any_over;
+    block_excl_scan(over, s, any_over);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int ci = tid * CPT + j;
+        if (ci < nch) offs[ci] = o;
+        o += cl[j];
+    }
+    const uint32_t tau = ws.tau[b];
+    const bool ok = any_over == 0 && total <= kDirectMax && (total >= p.k || tau == 1u);
+    if (!ok) {
+        select_streaming(x, nv, p.k, out, s);
+        return;
+    }
+    __syncthreads();
+    // gather the slots into LDS, one wave per chunk
+    for (int ci = w; ci < nch; ci += kW) {
+        const int n = cnt[ci], at = offs[ci];
+        const size_t slot = ((size_t)b * nch + ci) * kSlotCap;
+        for (int i = lane; i < n; i += kWave) {
+            ckey[at + i] = ws.key[slot + i];
+            cpos[at + i] = ws.pos[slot + i];
+        }
+    }
+    __syncthreads();
+    uint32_t key[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const int i = tid * KPT + j;
+        key[j] = i < total ? ckey[i] : 0u;
+    }
+    const int kk = min(p.k, total);
+    int gt_seen = 0, eq_seen = 0;
+    if (kk > 0) {
+        auto for_each = [&](auto f) {
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) f(key[j]);
+        };
+        const Sel q = radix_select(for_each, kk, s);
+        emit_block<KPT>(key, [&](int j) { return cpos[tid * KPT + j]; }, q, out, gt_seen, eq_seen, s);
+    }
+    pad_out(out, kk, p.k);
+}
+
+__global__ __launch_bounds__(kT) void topk_stream_kernel(TopkParams p)
+{
+    __shared__ Shared s;
+    const int b = blockIdx.x;
+    int nv = p.n_valid ? p.n_valid[b] : p.N;
+    nv = min(max(nv, 0), p.N);
+    select_streaming(p.x + (int64_t)b * p.x_sb, nv, p.k, p.out + (int64_t)b * p.out_sb, s);
+}
+
+int n_chunks(int N) { return (N + kChunk - 1) / kChunk; }
 
 }  // namespace
 
-size_t topk_slot_bytes(int, int, int) { return 0; }
+size_t topk_workspace_bytes(int B, int N, int k)
+{
+    (void)k;
+    if (N <= kDirectMax || n_chunks(N) > kMaxChunks) return 0;
+    return topk_ws_size(B, n_chunks(N));
+}
 
 hipError_t launch_topk(const TopkParams &p, hipStream_t st)
 {
     if (p.B == 0) return hipSuccess;
-    hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)p.B), dim3(kT), 0, st, p);
+    if (p.N <= kDirectMax) {
+        if (p.N <= 8 * kT) hipLaunchKernelGGL(topk_direct_kernel<8>, dim3((unsigned)p.B), dim3(kT), 0, st, p);
+        else if (p.N <= 16 * kT) hipLaunchKernelGGL(topk_direct_kernel<16>, dim3((unsigned)p.B), dim3(kT), 0, st, p);
+        else hipLaunchKernelGGL(topk_direct_kernel<32>, dim3((unsigned)p.B), dim3(kT), 0, st, p);
+        return hipGetLastError();
+    }
+    const int nch = n_chunks(p.N);
+    if (nch > kMaxChunks) {
+        hipLaunchKernelGGL(topk_stream_kernel, dim3((unsigned)p.B), dim3(kT), 0, st, p);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)nch, (unsigned)p.B), dim3(kT), 0, st, p, nch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)p.B), dim3(kT), 0, st, p, nch);
     return hipGetLastError();
 }
 

@@ -114,8 +114,9 @@ def test_indexer_argument_checks(L):
 
 def test_topk_argument_checks(L):
     ws = L.sap_topk_workspace_bytes
-    assert ws(1, 4096, 512) == 0                      # one workgroup per row: no workspace
-    assert ws(4, 131072, 512) == 0
+    assert ws(1, 4096, 512) == 0                      # rows of <= 16384 entries: one launch, no workspace
+    assert ws(2, 16384, 512) == 0
+    assert ws(4, 131072, 512) > ws(1, 131072, 512) > 0  # longer rows: per-chunk candidate slots
 
     def call(**kw):
         a = dict(x=A, sb=131072, nv=None, B=1, N=131072, k=512, out=A, osb=512, ws=None, wsb=0)
@@ -129,6 +130,8 @@ def test_topk_argument_checks(L):
     assert call(out=None) == ENULL
     assert call(x=None) == ENULL
     assert call(sb=100) == ESHAPE
+    assert call() == EWS                       # 131072 entries need the slots
+    assert call(ws=A, wsb=ws(1, 131072, 512) - 1) == EWS
 
 
 def test_index_build_argument_checks(L):

@@ -97,7 +97,8 @@ def test_indexer_extreme_scales_and_strides():
 
 
 @pytest.mark.parametrize("B,N,k", [(1, 131072, 512), (4, 131072, 512), (1, 8192, 512), (3, 4096, 512),
-                                   (2, 1000, 512), (2, 70000, 2048), (1, 100000, 1), (2, 50000, 300)])
+                                   (2, 1000, 512), (2, 70000, 2048), (1, 100000, 1), (2, 50000, 300),
+                                   (2, 12000, 4096), (2, 16384, 512), (2, 16385, 512), (1, 5000, 4096)])
 def test_topk_same_logits_bit_exact(B, N, k):
     need_gpu()
     g = torch.Generator().manual_seed(N + k + B)
@@ -110,6 +111,22 @@ def test_topk_same_logits_bit_exact(B, N, k):
     torch.cuda.synchronize()
     ref = oracle.topk(x, k, nv)
     assert torch.equal(got.cpu(), ref), f"B{B} N{N} k{k}"
+
+
+def test_topk_fallback_paths():
+    """Long rows whose strided sample misleads the filter threshold: keys at
+    the sampled positions dominate (too few keys pass), or one chunk holds
+    more passing keys than its slot.  Both must still give the exact set."""
+    need_gpu()
+    N, k = 131072, 512
+    g = torch.Generator().manual_seed(77)
+    x = torch.randn((2, N), generator=g)
+    pos = (torch.arange(4096, dtype=torch.int64) * N) // 4096          # the sampled positions
+    x[0, pos] = 100.0 + torch.rand(4096, generator=g)                  # sample top >> everything else
+    x[1, :4096] = 50.0                                                 # chunk 0 passes whole: slot overflow
+    got = sap.topk_select(dev(x), k)
+    torch.cuda.synchronize()
+    assert torch.equal(got.cpu(), oracle.topk(x, k))
 
 
 def test_topk_on_indexer_logits():
