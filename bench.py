@@ -117,6 +117,40 @@ def time_loop(fn, iters, warmup):
     return e0.elapsed_time(e1) / iters        # ms
 
 
+def capture(fn, per=1):
+    """A HIP graph of `per` back-to-back calls of fn (the calls enqueue on the
+    current stream, which is the capture stream inside the graph context)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(fn, iters, warmup, per=1):
+    """ms per fn call, from HIP events around `iters` replays of a graph of
+    `per` calls (no host launch cost inside the timed region)."""
+    g = capture(fn, per)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(iters):
+        g.replay()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / (iters * per)
+
+
 def roofline(bound, achieved, peak, unit, traffic=None):
     return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 5), "traffic": traffic}
@@ -142,8 +176,8 @@ def prefill_secondary(iters):
 def decode_secondary(B, kv, iters):
     st = DecodeStep(B=B, kv_dtype=kv, seed=W.SEED_BASE + (4 if kv == "e4m3" else 2))
     st.select()
-    ms_attn = time_loop(st.attend, iters, 5)
-    ms_step = time_loop(st.step, iters, 5)
+    ms_attn = time_graph(st.attend, iters, 5)
+    ms_step = time_graph(st.step, iters, 5)
     gb = st.attn_alg_bytes() / (ms_attn * 1e-3) / 1e9
     return {"workload": f"decode_b{B}_pos32767_r4_{kv}", "attn_us": round(ms_attn * 1e3, 2),
             "step_us": round(ms_step * 1e3, 2),
@@ -158,8 +192,8 @@ def indexer_secondary(B, iters):
     out = torch.empty((B, case.N), dtype=torch.float32, device=d)
     sel = torch.empty((B, 512), dtype=torch.int32, device=d)
     ws = torch.empty(max(sap.topk_workspace_bytes(B, case.N, 512), 1), dtype=torch.uint8, device=d)
-    ms_idx = time_loop(lambda: sap.indexer_logits_packed(q, w, pool, pt, case.page, case.N, out=out), iters, 5)
-    ms_topk = time_loop(lambda: sap.topk_select(out, 512, out=sel, workspace=ws), iters, 5)
+    ms_idx = time_graph(lambda: sap.indexer_logits_packed(q, w, pool, pt, case.page, case.N, out=out), iters, 5)
+    ms_topk = time_graph(lambda: sap.topk_select(out, 512, out=sel, workspace=ws), iters, 5)
     alg = B * (case.N * 68 + case.N * 4 + 32 * 128 * 2 + 32 * 4)
     gb = alg / (ms_idx * 1e-3) / 1e9
     return {"workload": f"indexer_b{B}_ctx131072", "indexer_us": round(ms_idx * 1e3, 2),
@@ -207,11 +241,12 @@ def main():
     log("building decode step inputs (B1, position 32767, r4)")
     st = DecodeStep(B=1, pos=32767, ratio=4)
 
-    log("timing whole steps")
-    ms_step = time_loop(st.step, args.steps, args.warmup)
+    log("timing whole steps (graph replays; eager launches for reference)")
+    ms_step = time_graph(st.step, args.steps, args.warmup)
+    ms_step_eager = time_loop(st.step, args.steps, args.warmup)
     log("timing the attention launches alone")
-    ms_attn = time_loop(st.attend, args.steps, args.warmup)
-    ms_sel = time_loop(st.select, args.steps, args.warmup)
+    ms_attn = time_graph(st.attend, args.steps, args.warmup)
+    ms_sel = time_graph(st.select, args.steps, args.warmup)
     value = st.gathered_bytes() / (ms_step * 1e-3) / 1e9
     attn_gbs = st.attn_alg_bytes() / (ms_attn * 1e-3) / 1e9
 
@@ -222,6 +257,8 @@ def main():
         "config": {"workload": "decode_b1_pos32767_r4_bf16", "global_batch": 1, "seq_len": 32768, "heads": 64,
                    "head_dim": 512, "window": 128, "topk": 512, "ratio": 4, "parallelism": "single-gpu",
                    "step": "indexer(8192 fp4 keys) + top-512 + index build + split-K attention + merge"},
+        "timing": "HIP-graph replays of the whole step, HIP events around the timed replays",
+        "eager_ms_per_step": round(ms_step_eager, 5),
         "attn_us": round(ms_attn * 1e3, 3), "select_us": round(ms_sel * 1e3, 3), "splits": st.splits,
         "roofline": roofline("hbm", attn_gbs, HBM_PEAK_GBS, "GB/s"),
     }

@@ -9,6 +9,7 @@ from __future__ import annotations
 import concurrent.futures as cf
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -37,6 +38,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
+def check_no_scratch(remarks: str) -> None:
+    """The bf16 attention kernels count their own in-flight gathers with
+    s_waitcnt vmcnt(N); a compiler-generated scratch access would be one more
+    vector memory operation in that count.  Refuse such a build."""
+    name = None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and "attn_kernel" in name and int(m.group(1)) > 0:
+            # kernel template <D, KV, OUT>: KV == 0 is bf16 (mangled ...ILi<D>ELi0E...)
+            if re.search(r"attn_kernelILi\d+ELi0E", name):
+                raise RuntimeError(f"{name} uses scratch memory ({m.group(1)} bytes/lane); "
+                                   "its gather wait counts would be wrong")
+
+
 def build(verbose: bool = False, jobs: int = 8) -> str:
     cc = hipcc()
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
@@ -46,11 +65,16 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     def compile_one(src):
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         cmd = [cc, *FLAGS, "-c", src, "-o", obj]
+        guard = os.path.basename(src) == "attn.hip"
+        if guard:
+            cmd.append("-Rpass-analysis=kernel-resource-usage")
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n{r.stderr}")
+        if guard:
+            check_no_scratch(r.stderr)
         return obj
 
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:

@@ -514,7 +514,21 @@ void attn_kernel(AttnParams p)
         const int cn = min(c_end - cc, kIdxChunk);
         n_tiles = (cn + kAttnTile - 1) / kAttnTile;
         __syncthreads();   // the previous chunk's indices are no longer read
-        for (int i = tid; i < n_tiles * kAttnTile; i += kThreads) sidx[i] = i < cn ? idx_row[cc + i] : -1;
+        // four loads in flight per thread before their stores (up to 1024
+        // columns per memory round trip)
+        for (int i0 = 0; i0 < n_tiles * kAttnTile; i0 += 4 * kThreads) {
+            int iv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + tid + u * kThreads;
+                iv[u] = i < cn ? idx_row[cc + i] : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + tid + u * kThreads;
+                if (i < n_tiles * kAttnTile) sidx[i] = iv[u];
+            }
+        }
         // a wait the compiler sees: Q and the index loads are complete, so no
         // wait for them is left inside the tile loops (s_waitcnt vmcnt(0))
         __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -610,26 +624,44 @@ void attn_kernel(AttnParams p)
 }
 
 // out[t, h, :] = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j over the splits
-// j in order; zero when every split was empty.
+// j in order; zero when every split was empty.  One thread per 4 head_dim
+// values; the partial loads of 8 splits are issued before any is used.
 template <int D, int OUT>
 __global__ __launch_bounds__(128) void attn_merge_kernel(AttnParams p)
 {
+    constexpr int U = 8;
     const int t = blockIdx.x, head = blockIdx.y, tid = threadIdx.x;
     if (4 * tid >= D) return;
     const int S = p.num_splits;
     const int64_t slot0 = ((int64_t)t * S) * p.H + head;
     float M = -INFINITY;
-    for (int j = 0; j < S; ++j) M = fmaxf(M, p.part_ml[(slot0 + (int64_t)j * p.H) * 2]);
+    for (int j0 = 0; j0 < S; j0 += U) {
+        float m[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) m[u] = p.part_ml[(slot0 + (int64_t)min(j0 + u, S - 1) * p.H) * 2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) M = fmaxf(M, m[u]);   // repeats of split S-1 change nothing
+    }
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     float L = 0.0f;
     if (M != -INFINITY) {
-        for (int j = 0; j < S; ++j) {
-            const int64_t slot = slot0 + (int64_t)j * p.H;
-            const float2 ml = *(const float2 *)(p.part_ml + slot * 2);
-            const float w = fast_exp2(ml.x - M);
-            L += w * ml.y;
-            const float4 v = *(const float4 *)(p.part_o + slot * D + 4 * tid);
-            o.x += w * v.x; o.y += w * v.y; o.z += w * v.z; o.w += w * v.w;
+        for (int j0 = 0; j0 < S; j0 += U) {
+            float2 ml[U];
+            float4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t slot = slot0 + (int64_t)min(j0 + u, S - 1) * p.H;
+                ml[u] = *(const float2 *)(p.part_ml + slot * 2);
+                v[u] = *(const float4 *)(p.part_o + slot * D + 4 * tid);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (j0 + u < S) {
+                    const float w = fast_exp2(ml[u].x - M);
+                    L += w * ml[u].y;
+                    o.x += w * v[u].x; o.y += w * v[u].y; o.z += w * v[u].z; o.w += w * v[u].w;
+                }
+            }
         }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;

@@ -36,7 +36,7 @@ __device__ __forceinline__ void wave_lds_sync()
 
 __global__ __launch_bounds__(256) void indexer_kernel(IndexerParams p)
 {
-    __shared__ uint32_t stage[4][kTileWords];
+    __shared__ __attribute__((aligned(16))) uint32_t stage[4][kTileWords];
     const int b = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -51,12 +51,18 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerParams p)
         for (int s = 0; s < 8; ++s)
             qa[s] = hok ? *(const uint4 *)(qr + 16 * s + 8 * hh) : make_uint4(0, 0, 0, 0);
     }
-    // head weights of this lane's 16 output rows: head = 8(i/4) + 4hh + i%4
+    // head weights of this lane's 16 output rows: head = 8(i/4) + 4hh + i%4;
+    // the 32 weights are wave-uniform loads, the half-wave picks its own
     float wv[16];
+    {
+        const float *wr = p.w + (int64_t)b * p.w_sb;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int h = 8 * (i >> 2) + 4 * hh + (i & 3);
-        wv[i] = h < p.Hi ? p.w[(int64_t)b * p.w_sb + h] : 0.0f;
+        for (int i = 0; i < 16; ++i) {
+            const int h0 = 8 * (i >> 2) + (i & 3), h1 = h0 + 4;
+            const float w0 = h0 < p.Hi ? wr[h0] : 0.0f;
+            const float w1 = h1 < p.Hi ? wr[h1] : 0.0f;
+            wv[i] = hh ? w1 : w0;
+        }
     }
 
     const int n_tiles = (p.N + kKeyTile - 1) / kKeyTile;
@@ -64,8 +70,35 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerParams p)
     uint32_t *st = stage[wave];
     uint32_t regs[kWordsPerLane];
 
+    // A tile of 64 keys starting at a multiple of 64 lies inside one page
+    // when the page size is a multiple of 64: one (wave-uniform) page-table
+    // read gives the pool row of its first key and the rest follow it.
+    const bool page_tiles = p.pt == nullptr || p.page % kKeyTile == 0;
+    // a full tile of 17-word rows is one contiguous 4352-byte block: 16-byte
+    // loads (4 per lane) plus one word per lane instead of 17 word loads
+    const bool vec_ok = page_tiles && p.row_words == kRowWords && (reinterpret_cast<uintptr_t>(p.pool) & 15u) == 0;
+    bool vec = false;   // layout of regs for the tile in flight (wave-uniform)
     auto load_tile = [&](int kt) {
         const int key0 = kt * kKeyTile;
+        int64_t row0 = (int64_t)b * p.N + key0;
+        if (p.pt && page_tiles) {
+            const int pg = key0 / p.page;
+            row0 = (int64_t)p.pt[(int64_t)b * p.pt_sb + pg] * p.page + (key0 - pg * p.page);
+        }
+        vec = vec_ok && key0 + kKeyTile <= nk;
+        if (vec) {
+            const uint32_t *tp = (const uint32_t *)p.pool + row0 * kRowWords;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint4 v = *(const uint4 *)(tp + 4 * (lane + kWave * k));
+                regs[4 * k] = v.x;
+                regs[4 * k + 1] = v.y;
+                regs[4 * k + 2] = v.z;
+                regs[4 * k + 3] = v.w;
+            }
+            regs[16] = tp[4 * 4 * kWave + lane];
+            return;
+        }
 #pragma unroll
         for (int k = 0; k < kWordsPerLane; ++k) {
             const int i = lane + kWave * k;
@@ -74,8 +107,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerParams p)
             const int n = key0 + row;
             uint32_t v = 0;
             if (n < nk) {
-                const int64_t prow = p.pt ? (int64_t)p.pt[(int64_t)b * p.pt_sb + n / p.page] * p.page + n % p.page
-                                          : (int64_t)b * p.N + n;
+                int64_t prow = row0 + row;
+                if (!page_tiles) prow = (int64_t)p.pt[(int64_t)b * p.pt_sb + n / p.page] * p.page + n % p.page;
                 v = (uint32_t)p.pool[prow * p.row_words + wd];
             }
             regs[k] = v;
@@ -86,8 +119,15 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerParams p)
     for (int it = 0; it < p.tiles_per_wave; ++it) {
         const int kt = tile0 + it;
         if (kt >= n_tiles) break;
+        if (vec) {
 #pragma unroll
-        for (int k = 0; k < kWordsPerLane; ++k) st[lane + kWave * k] = regs[k];
+            for (int k = 0; k < 4; ++k)
+                *(uint4 *)(st + 4 * (lane + kWave * k)) = make_uint4(regs[4 * k], regs[4 * k + 1], regs[4 * k + 2], regs[4 * k + 3]);
+            st[4 * 4 * kWave + lane] = regs[16];
+        } else {
+#pragma unroll
+            for (int k = 0; k < kWordsPerLane; ++k) st[lane + kWave * k] = regs[k];
+        }
         wave_lds_sync();
         if (it + 1 < p.tiles_per_wave && kt + 1 < n_tiles) load_tile(kt + 1);
 

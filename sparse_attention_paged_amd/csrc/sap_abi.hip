@@ -226,8 +226,9 @@ int sap_indexer_logits_packed(const void *q, int64_t q_stride_b,
     p.B = B;
     p.Hi = Hi;
     p.N = N;
+    // about two waves per SIMD (256 CUs x 4 SIMDs), each streaming its tiles
     const int64_t tiles = ((int64_t)N + 63) / 64 * B;
-    p.tiles_per_wave = (int)((tiles + 4095) / 4096);
+    p.tiles_per_wave = (int)((tiles + 2047) / 2048);
     if (p.tiles_per_wave < 1) p.tiles_per_wave = 1;
     return launched(sap::launch_indexer(p, (hipStream_t)stream));
 }
