@@ -162,9 +162,15 @@ void attn_kernel(AttnParams p)
     // per-column bias (0 or -inf) and dequant scale, and the row indices of
     // the current chunk of columns
     constexpr int DEPTH = KV == 0 ? 4 : 3;
+    // bf16: the gather instructions of tile u are spread over three phases
+    // so that the four waves never issue them in one burst: rows [0, GA)
+    // during PV(u-3), rows [GA, GA+GB) during S(u-2), the rest during the
+    // softmax of u-2.  Tile u's buffer held tile u-4, free after B1(u-3).
+    constexpr int GA = SH::NQ * 3 / 8, GB = SH::NQ * 3 / 8;
+    static_assert(GA <= SH::PM && GB <= SH::SK, "every gather row needs a PV or S step");
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[DEPTH][SH::TILE_BYTES];
     __shared__ __attribute__((aligned(16))) float metas[DEPTH][2 * kAttnTile];
-    __shared__ int sidx[kIdxChunk];
+    __shared__ __attribute__((aligned(16))) int sidx[kIdxChunk];
     __shared__ float4 xs[4][2][64];          // partial scores for the partner wave
     // bf16 P by [term][dq][nt][ch][lane]: the two column halves of one head
     // tile sit 512 bytes apart, so a lane reads its B operand with one
@@ -229,12 +235,13 @@ void attn_kernel(AttnParams p)
 
     // issue gather instruction q of tile `tile` (of the current chunk) into
     // buffer `bf`; the row index comes from the staged chunk
-    auto issue_row = [&](uint8_t *bf, float *meta, int tile, int q) __attribute__((always_inline)) {
+    // rr: the row index when one instruction moves one row (RPI == 1, taken
+    // from registers filled ahead of time, so issuing never waits on an LDS
+    // read); otherwise each lane reads its own row's index here
+    auto issue_row = [&](uint8_t *bf, float *meta, int tile, int q, int rr) __attribute__((always_inline)) {
         const int rho = grow(q);
         const int c = cc + tile * kAttnTile + rho;
-        const int ri = sidx[tile * kAttnTile + rho];
-        // one row per instruction: the index is wave-uniform, use an SGPR
-        const int r = SH::RPI == 1 ? __builtin_amdgcn_readfirstlane(ri) : ri;
+        const int r = SH::RPI == 1 ? rr : sidx[tile * kAttnTile + rho];
         const bool win = c < n_win;
         const uint8_t *base = win ? win_pool : cmp_pool;
         const int64_t rs = win ? win_rs : cmp_rs;
@@ -252,9 +259,25 @@ void attn_kernel(AttnParams p)
         }
         if (gpos == 0) meta[rho] = r >= 0 ? 0.0f : -INFINITY;
     };
-    auto issue = [&](uint8_t *bf, float *meta, int tile) __attribute__((always_inline)) {
+    // the row indices of this wave's 8 rows of a tile, wave-uniform (RPI == 1)
+    struct Rows {
+        int r[SH::NQ];
+    };
+    auto rows_of = [&](int tile, Rows &rw) __attribute__((always_inline)) {
+        if constexpr (SH::RPI == 1) {
+            // two 16-byte LDS reads (the address is wave-uniform)
+            const int4 *src = (const int4 *)(sidx + tile * kAttnTile + 8 * w);
+            const int4 a = src[0], b = src[1];
+            const int v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-        for (int q = 0; q < SH::NQ; ++q) issue_row(bf, meta, tile, q);
+            for (int q = 0; q < SH::NQ; ++q) rw.r[q] = __builtin_amdgcn_readfirstlane(v[q]);
+        }
+    };
+    auto issue = [&](uint8_t *bf, float *meta, int tile) __attribute__((always_inline)) {
+        Rows rw;
+        rows_of(tile, rw);
+#pragma unroll
+        for (int q = 0; q < SH::NQ; ++q) issue_row(bf, meta, tile, q, rw.r[q]);
     };
     // e4m3: widen the registers of the issued tile into its buffer
     auto land = [&](uint8_t *bf, float *meta) __attribute__((always_inline)) {
@@ -306,7 +329,7 @@ void attn_kernel(AttnParams p)
 
     // --- S^T over head_dim half dq for columns 16ch .. 16ch+15:
     //     sacc[j] = S^T[col 16ch + 4g + i][head 16j + l16] (partial)
-    auto s_part = [&](const uint8_t *bf, f32x4 (&sacc)[4]) __attribute__((always_inline)) {
+    auto s_part = [&](const uint8_t *bf, f32x4 (&sacc)[4], int dma_tile, uint8_t *nb2, float *nm2, const Rows &r2) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         auto kfrag = [&](int s) __attribute__((always_inline)) { return lds_b128(bf + kb[s & 1] + 128 * (s >> 1)); };
@@ -319,6 +342,12 @@ void attn_kernel(AttnParams p)
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) sacc[j] = mfma16x16x32(f[s % 3], qf[j][s], sacc[j]);
+            if constexpr (KV == 0) {
+                // GB gathers of tile t+2, at k-steps spread over the loop
+                constexpr int STEP = GB > 0 ? SH::SK / GB : 1;   // GB <= SK: rows at s = STEP-1, 2 STEP-1, ...
+                if (GB > 0 && s % STEP == STEP - 1 && s / STEP < GB && dma_tile < n_tiles)
+                    issue_row(nb2, nm2, dma_tile, GA + s / STEP, r2.r[GA + s / STEP]);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -357,7 +386,8 @@ void attn_kernel(AttnParams p)
 
     // --- O^T += V^T P^T for head_dim quarter w; P^T of head tile j comes from
     //     the owners (j/2, ch = 0) and (j/2, ch = 1)
-    auto pv = [&](const uint8_t *bf, const uint2 (*px)[2][2][2][64], int dma_tile, uint8_t *nb3, float *nm3) __attribute__((always_inline)) {
+    auto pv = [&](const uint8_t *bf, const uint2 (*px)[2][2][2][64], int dma_tile, uint8_t *nb3, float *nm3,
+                  const Rows &r3) __attribute__((always_inline)) {
         uint4 pb[NP][4];
 #pragma unroll
         for (int e = 0; e < NP; ++e)
@@ -385,10 +415,13 @@ void attn_kernel(AttnParams p)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[m][j] = mfma16x16x32(a, pb[1][j], acc[m][j]);
             }
-            // bf16: one gather instruction of tile t+3 per m-step, so the
-            // memory pipeline fills while the MFMAs run (NQ == PM)
+            // bf16: the remaining gather instructions of tile t+3, one per
+            // m-step, so the memory pipeline fills while the MFMAs run
             if constexpr (KV == 0) {
-                if (dma_tile < n_tiles) issue_row(nb3, nm3, dma_tile, m);
+                // GA gathers of tile t+3, at m-steps spread over the loop
+                constexpr int STEP = GA > 0 ? SH::PM / GA : 1;   // GA <= PM
+                if (GA > 0 && m % STEP == STEP - 1 && m / STEP < GA && dma_tile < n_tiles)
+                    issue_row(nb3, nm3, dma_tile, m / STEP, r3.r[m / STEP]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -404,9 +437,16 @@ void attn_kernel(AttnParams p)
     // workgroup's combined flags (bit 0: some head sees its first valid
     // column, bit 1: some head's max grows by more than the slack).
     auto front = [&](int tile, const uint8_t *cb, const float *cm, uint8_t *nb1, float *nm1, uint8_t *nb2,
-                     float *nm2, Soft &st) __attribute__((always_inline)) {
+                     float *nm2, uint8_t *nb3, float *nm3, Soft &st, Rows &r3) __attribute__((always_inline)) {
+        // row indices of the gathers this tile issues (tile t+2 here, tile
+        // t+3 during PV), read from LDS before any fragment read is pending
+        Rows r2;
+        if constexpr (KV == 0) {
+            if (tile + 2 < n_tiles) rows_of(tile + 2, r2);
+            if (tile + 3 < n_tiles) rows_of(tile + 3, r3);
+        }
         f32x4 sacc[4];
-        s_part(cb, sacc);
+        s_part(cb, sacc, tile + 2, nb2, nm2, r2);
         // send the partner's heads, keep mine (register arrays are only
         // indexed by constants; the wave-uniform choice is a select)
         f32x4 mine[2], theirs[2];
@@ -418,10 +458,12 @@ void attn_kernel(AttnParams p)
         xs[w][0][lane] = make_float4(theirs[0][0], theirs[0][1], theirs[0][2], theirs[0][3]);
         xs[w][1][lane] = make_float4(theirs[1][0], theirs[1][1], theirs[1][2], theirs[1][3]);
         if constexpr (KV == 0) {
-            // tile t+1 has landed; the gathers of tile t+2 may stay in flight
-            if (tile + 2 < n_tiles) wait_vm<SH::NQ>();
-            else wait_vm<0>();
             __syncthreads();
+            // the remaining gathers of tile t+2
+            if (tile + 2 < n_tiles) {
+#pragma unroll
+                for (int q = GA + GB; q < SH::NQ; ++q) issue_row(nb2, nm2, tile + 2, q, r2.r[q]);
+            }
         } else {
             // tile t+1 arrived in registers: widen it into its buffer, then
             // start tile t+2
@@ -468,13 +510,21 @@ void attn_kernel(AttnParams p)
         const int wf = (__builtin_amdgcn_ballot_w64((flag & 1) != 0) ? 1 : 0) |
                        (__builtin_amdgcn_ballot_w64((flag & 2) != 0) ? 2 : 0);
         if (lane == 0) xf[w] = wf;
+        if constexpr (KV == 0) {
+            // tile t+1 has landed before this barrier publishes it; only the
+            // gathers of tile t+2 (all issued after those of tile t+1) may
+            // stay in flight
+            if (tile + 2 < n_tiles) wait_vm<SH::NQ>();
+            else wait_vm<0>();
+        }
         __syncthreads();
         return __builtin_amdgcn_readfirstlane(xf[0] | xf[1] | xf[2] | xf[3]);
     };
 
     // second half: agree on new maxima if any head needs one (RESCALE: also
     // from a finite max, which rescales O and the sums), then PV
-    auto back = [&](auto rescale_tag, int any, const uint8_t *cb, Soft &st, int dma_tile, uint8_t *nb3, float *nm3) __attribute__((always_inline)) {
+    auto back = [&](auto rescale_tag, int any, const uint8_t *cb, Soft &st, int dma_tile, uint8_t *nb3, float *nm3,
+                    const Rows &r3) __attribute__((always_inline)) {
         constexpr bool RESCALE = decltype(rescale_tag)::value;
         if (any) {
 #pragma unroll
@@ -502,7 +552,7 @@ void attn_kernel(AttnParams p)
             put_p(xq, phi, plo);
             __syncthreads();
         }
-        pv(cb, any ? xq : xp, dma_tile, nb3, nm3);
+        pv(cb, any ? xq : xp, dma_tile, nb3, nm3, r3);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) l_run[nt] += (st.pr[nt][0] + st.pr[nt][1]) + (st.pr[nt][2] + st.pr[nt][3]);
     };
@@ -541,7 +591,13 @@ void attn_kernel(AttnParams p)
         }
         if (n_tiles > 1) issue(tiles[1], metas[1], 1);
         if constexpr (KV == 0) {
-            if (n_tiles > 2) issue(tiles[2], metas[2], 2);
+            // the rows of tile 2 that PV(-1) would have issued
+            if (n_tiles > 2) {
+                Rows rw;
+                rows_of(2, rw);
+#pragma unroll
+                for (int q = 0; q < GA; ++q) issue_row(tiles[2], metas[2], 2, q, rw.r[q]);
+            }
             wait_vm<0>();
         }
         __syncthreads();
@@ -554,11 +610,13 @@ void attn_kernel(AttnParams p)
             for (int k = 0; k + 1 < DEPTH; ++k) bi[k] = bi[k + 1];
             bi[DEPTH - 1] = b0;
         };
+        Rows r3;   // row indices of tile t+3, read in front, used in PV
         auto fr = [&](int it, Soft &st) __attribute__((always_inline)) {
-            return front(it, tiles[bi[0]], metas[bi[0]], tiles[bi[1]], metas[bi[1]], tiles[bi[2]], metas[bi[2]], st);
+            return front(it, tiles[bi[0]], metas[bi[0]], tiles[bi[1]], metas[bi[1]], tiles[bi[2]], metas[bi[2]],
+                         tiles[bi[DEPTH - 1]], metas[bi[DEPTH - 1]], st, r3);
         };
         auto bk = [&](auto tag, int any, int it, Soft &st) __attribute__((always_inline)) {
-            back(tag, any, tiles[bi[0]], st, it + 3, tiles[bi[DEPTH - 1]], metas[bi[DEPTH - 1]]);
+            back(tag, any, tiles[bi[0]], st, it + 3, tiles[bi[DEPTH - 1]], metas[bi[DEPTH - 1]], r3);
         };
         Soft st;
         int it = 0, any = 0;
