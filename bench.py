@@ -19,6 +19,7 @@ indexer at context 131072), each with its own roofline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -151,6 +152,23 @@ def time_graph(fn, iters, warmup, per=1):
     return e0.elapsed_time(e1) / (iters * per)
 
 
+def counted_traffic(key):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (profiles/attn_traffic_counters.json), or None when attn.hip changed since
+    the counters were taken."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(os.path.join(here, "profiles", "attn_traffic_counters.json")) as f:
+            doc = json.load(f)
+        with open(os.path.join(here, "sparse_attention_paged_amd", "csrc", "attn.hip"), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if doc.get("attn_source_sha256") != sha or key not in doc:
+        return None
+    return doc[key]["traffic_bytes"]
+
+
 def roofline(bound, achieved, peak, unit, traffic=None):
     return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 5), "traffic": traffic}
@@ -170,7 +188,8 @@ def prefill_secondary(iters):
     tf = flops / (ms * 1e-3) / 1e12
     return {"workload": "prefill_s8192_r4_bf16", "us": round(ms * 1e3, 2), "tflops": round(tf, 2),
             "gflop": round(flops / 1e9, 2),
-            "roofline": roofline("mfma", tf, BF16_PEAK_TFLOPS, "TFLOP/s")}
+            "roofline": roofline("mfma", tf, BF16_PEAK_TFLOPS, "TFLOP/s",
+                                 traffic=counted_traffic("prefill_s8192_r4_bf16"))}
 
 
 def decode_secondary(B, kv, iters):
@@ -260,7 +279,8 @@ def main():
         "timing": "HIP-graph replays of the whole step, HIP events around the timed replays",
         "eager_ms_per_step": round(ms_step_eager, 5),
         "attn_us": round(ms_attn * 1e3, 3), "select_us": round(ms_sel * 1e3, 3), "splits": st.splits,
-        "roofline": roofline("hbm", attn_gbs, HBM_PEAK_GBS, "GB/s"),
+        "roofline": roofline("hbm", attn_gbs, HBM_PEAK_GBS, "GB/s",
+                             traffic=counted_traffic("decode_b1_r4_bf16_attention_pair")),
     }
     res["roofline"]["kernel"] = "sparse attention split-K + merge (per launch pair)"
     res["roofline"]["bytes_per_launch"] = st.attn_alg_bytes()
