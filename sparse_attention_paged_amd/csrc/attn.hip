@@ -312,42 +312,43 @@ void attn_kernel(AttnParams p)
 #pragma unroll
         for (int e = 0; e < 2; ++e) kb[e] = rho * 2 * D + 16 * (((D / 16) * dq + 4 * e + g) ^ sw);
     }
+    // (rows r and r + 16 have the same swizzle, so the second PV row is the
+    // first plus a constant)
     constexpr int VB = SH::PM < 4 ? SH::PM : 4;
-    int vb[2][VB];
+    int vb[VB];
     {
         const int dsub = 4 * (l16 & 3);
+        const int r = 4 * g + (l16 >> 2), vs = rswz(r);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int r = 16 * h + 4 * g + (l16 >> 2), vs = rswz(r);
-#pragma unroll
-            for (int mm = 0; mm < VB; ++mm) {
-                const int d = (D / 4) * w + 16 * mm + dsub;
-                vb[h][mm] = r * 2 * D + 16 * ((d >> 3) ^ vs) + 2 * (d & 7);
-            }
+        for (int mm = 0; mm < VB; ++mm) {
+            const int d = (D / 4) * w + 16 * mm + dsub;
+            vb[mm] = r * 2 * D + 16 * ((d >> 3) ^ vs) + 2 * (d & 7);
         }
     }
 
     // --- S^T over head_dim half dq for columns 16ch .. 16ch+15:
     //     sacc[j] = S^T[col 16ch + 4g + i][head 16j + l16] (partial)
-    auto s_part = [&](const uint8_t *bf, f32x4 (&sacc)[4], int dma_tile, uint8_t *nb2, float *nm2, const Rows &r2) __attribute__((always_inline)) {
+    auto s_part = [&](const uint8_t *bf, f32x4 (&sacc)[4], int dma_tile, uint8_t *nb2, float *nm2, const Rows &r2,
+                      auto hook) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         auto kfrag = [&](int s) __attribute__((always_inline)) { return lds_b128(bf + kb[s & 1] + 128 * (s >> 1)); };
-        uint4 f[3];
+        uint4 f[2];   // fragment ring: step s+1 is read while step s multiplies
         f[0] = kfrag(0);
-        if (SH::SK > 1) f[1] = kfrag(1);
 #pragma unroll
         for (int s = 0; s < SH::SK; ++s) {
-            if (s + 2 < SH::SK) f[(s + 2) % 3] = kfrag(s + 2);
+            if (s + 1 < SH::SK) f[(s + 1) % 2] = kfrag(s + 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sacc[j] = mfma16x16x32(f[s % 3], qf[j][s], sacc[j]);
+            for (int j = 0; j < 4; ++j) sacc[j] = mfma16x16x32(f[s % 2], qf[j][s], sacc[j]);
             if constexpr (KV == 0) {
                 // GB gathers of tile t+2, at k-steps spread over the loop
                 constexpr int STEP = GB > 0 ? SH::SK / GB : 1;   // GB <= SK: rows at s = STEP-1, 2 STEP-1, ...
-                if (GB > 0 && s % STEP == STEP - 1 && s / STEP < GB && dma_tile < n_tiles)
+                if (GB > 0 && s % STEP == STEP - 1 && s / STEP < GB && dma_tile >= 0 && dma_tile < n_tiles)
                     issue_row(nb2, nm2, dma_tile, GA + s / STEP, r2.r[GA + s / STEP]);
             }
+            // VALU work of the previous tile runs while these MFMAs execute
+            hook(s);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -397,8 +398,8 @@ void attn_kernel(AttnParams p)
                 pb[e][j] = make_uint4(a.x, a.y, b.x, b.y);
             }
         auto vfrag = [&](int m) __attribute__((always_inline)) {
-            const uint2 v0 = lds_tr16(bf + vb[0][m & 3] + 128 * (m >> 2));
-            const uint2 v1 = lds_tr16(bf + vb[1][m & 3] + 128 * (m >> 2));
+            const uint2 v0 = lds_tr16(bf + vb[m & 3] + 128 * (m >> 2));
+            const uint2 v1 = lds_tr16(bf + vb[m & 3] + 16 * 2 * D + 128 * (m >> 2));
             return make_uint4(v0.x, v0.y, v1.x, v1.y);
         };
         uint4 vr[3];
@@ -429,69 +430,33 @@ void attn_kernel(AttnParams p)
 
     // softmax inputs of the current tile, kept between the two halves of a step
     struct Soft {
-        float x[2][4], csc[4], pr[2][4];
+        float x[2][4], csc[4], psum[2];   // scores, e4m3 scales, sums of this lane's weights
     };
 
-    // first half of a tile: S, partial-score exchange, gather of tile t+2,
-    // weights against the current max and their publication.  Returns the
-    // workgroup's combined flags (bit 0: some head sees its first valid
-    // column, bit 1: some head's max grows by more than the slack).
-    auto front = [&](int tile, const uint8_t *cb, const float *cm, uint8_t *nb1, float *nm1, uint8_t *nb2,
-                     float *nm2, uint8_t *nb3, float *nm3, Soft &st, Rows &r3) __attribute__((always_inline)) {
-        // row indices of the gathers this tile issues (tile t+2 here, tile
-        // t+3 during PV), read from LDS before any fragment read is pending
-        Rows r2;
-        if constexpr (KV == 0) {
-            if (tile + 2 < n_tiles) rows_of(tile + 2, r2);
-            if (tile + 3 < n_tiles) rows_of(tile + 3, r3);
+    // --- softmax of heads 32dq + 16nt + l16, columns 16ch + 4g + i, in three
+    //     pieces so they can be placed between the MFMAs of the next tile's S
+    // (a) the partner's partial scores and the tile's bias / scales -> scores
+    auto soft_a = [&](const float *cm, const f32x4 (&mine)[2], Soft &st) __attribute__((always_inline)) {
+        const float4 o0 = xs[w ^ 1][0][lane], o1 = xs[w ^ 1][1][lane];
+        const float4 b4 = *(const float4 *)(cm + 16 * ch + 4 * g);
+        const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+        if constexpr (KV == 2) {
+            const float4 s4 = *(const float4 *)(cm + kAttnTile + 16 * ch + 4 * g);
+            st.csc[0] = s4.x; st.csc[1] = s4.y; st.csc[2] = s4.z; st.csc[3] = s4.w;
         }
-        f32x4 sacc[4];
-        s_part(cb, sacc, tile + 2, nb2, nm2, r2);
-        // send the partner's heads, keep mine (register arrays are only
-        // indexed by constants; the wave-uniform choice is a select)
-        f32x4 mine[2], theirs[2];
+        const float ov[2][4] = {{o0.x, o0.y, o0.z, o0.w}, {o1.x, o1.y, o1.z, o1.w}};
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            mine[nt] = dq ? sacc[2 + nt] : sacc[nt];
-            theirs[nt] = dq ? sacc[nt] : sacc[2 + nt];
-        }
-        xs[w][0][lane] = make_float4(theirs[0][0], theirs[0][1], theirs[0][2], theirs[0][3]);
-        xs[w][1][lane] = make_float4(theirs[1][0], theirs[1][1], theirs[1][2], theirs[1][3]);
-        if constexpr (KV == 0) {
-            __syncthreads();
-            // the remaining gathers of tile t+2
-            if (tile + 2 < n_tiles) {
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-                for (int q = GA + GB; q < SH::NQ; ++q) issue_row(nb2, nm2, tile + 2, q, r2.r[q]);
+            for (int i = 0; i < 4; ++i) {
+                float v = (mine[nt][i] + ov[nt][i]) * sl2;
+                if constexpr (KV == 2) v *= st.csc[i];
+                st.x[nt][i] = v + bb[i];
             }
-        } else {
-            // tile t+1 arrived in registers: widen it into its buffer, then
-            // start tile t+2
-            wait_vm<0>();
-            if (tile + 1 < n_tiles) land(nb1, nm1);
-            __syncthreads();
-            if (tile + 2 < n_tiles) issue(nb2, nm2, tile + 2);
-        }
-        // --- softmax of heads 32dq + 16nt + l16, columns 16ch + 4g + i
-        {
-            const float4 o0 = xs[w ^ 1][0][lane], o1 = xs[w ^ 1][1][lane];
-            const float4 b4 = *(const float4 *)(cm + 16 * ch + 4 * g);
-            const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-            if constexpr (KV == 2) {
-                const float4 s4 = *(const float4 *)(cm + kAttnTile + 16 * ch + 4 * g);
-                st.csc[0] = s4.x; st.csc[1] = s4.y; st.csc[2] = s4.z; st.csc[3] = s4.w;
-            }
-            const float ov[2][4] = {{o0.x, o0.y, o0.z, o0.w}, {o1.x, o1.y, o1.z, o1.w}};
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v = (mine[nt][i] + ov[nt][i]) * sl2;
-                    if constexpr (KV == 2) v *= st.csc[i];
-                    st.x[nt][i] = v + bb[i];
-                }
-        }
-        float tmax[2];
+    };
+    // (b) tile maxima of the owned heads and the flags (bit 0: a first
+    //     valid column, bit 1: a max beyond the slack)
+    auto soft_b = [&](const Soft &st, float (&tmax)[2]) __attribute__((always_inline)) {
         int flag = 0;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
@@ -500,8 +465,15 @@ void attn_kernel(AttnParams p)
             if (mr == -INFINITY) flag |= tmax[nt] > -INFINITY ? 1 : 0;
             else flag |= tmax[nt] > mr + kRescaleSlack ? 2 : 0;
         }
+        return flag;
+    };
+    // (c) weights against the current max, published with the maxima and flags
+    auto soft_c = [&](Soft &st, const float (&tmax)[2], int flag) __attribute__((always_inline)) {
         uint2 phi[2], plo[2];
-        weights(st.x, st.csc, st.pr, phi, plo);
+        float pr[2][4];
+        weights(st.x, st.csc, pr, phi, plo);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) st.psum[nt] = (pr[nt][0] + pr[nt][1]) + (pr[nt][2] + pr[nt][3]);
         put_p(xp, phi, plo);
         if (g == 0) {
             xm[w][l16] = tmax[0];
@@ -510,15 +482,79 @@ void attn_kernel(AttnParams p)
         const int wf = (__builtin_amdgcn_ballot_w64((flag & 1) != 0) ? 1 : 0) |
                        (__builtin_amdgcn_ballot_w64((flag & 2) != 0) ? 2 : 0);
         if (lane == 0) xf[w] = wf;
+    };
+
+    // S^T partials of a tile: send the partner's heads, keep mine (register
+    // arrays are only indexed by constants; the wave-uniform choice is a select)
+    auto send_scores = [&](const f32x4 (&sacc)[4], f32x4 (&mine)[2]) __attribute__((always_inline)) {
+        f32x4 theirs[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            mine[nt] = dq ? sacc[2 + nt] : sacc[nt];
+            theirs[nt] = dq ? sacc[nt] : sacc[2 + nt];
+        }
+        xs[w][0][lane] = make_float4(theirs[0][0], theirs[0][1], theirs[0][2], theirs[0][3]);
+        xs[w][1][lane] = make_float4(theirs[1][0], theirs[1][1], theirs[1][2], theirs[1][3]);
+    };
+
+    // One tile t, software pipelined: S of tile t+1 on the MFMAs while the
+    // softmax of tile t runs on the VALU between them; then the second
+    // barrier, the partial scores of tile t+1 (their buffer is free: every
+    // wave has read tile t's), and (back) PV of tile t.  Tile t's partial
+    // scores were exchanged before the first barrier of tile t (tail of the
+    // previous tile).  Gathers: all of tile t+3 (bf16) or tile t+2 (e4m3).
+    // Returns the workgroup's combined flags.
+    auto front = [&](int tile, const float *cm, const uint8_t *nb1, uint8_t *nb2, float *nm2, uint8_t *nb3,
+                     float *nm3, Soft &st, f32x4 (&mine)[2], Rows &r3) __attribute__((always_inline)) {
+        const bool more1 = tile + 1 < n_tiles;
         if constexpr (KV == 0) {
-            // tile t+1 has landed before this barrier publishes it; only the
-            // gathers of tile t+2 (all issued after those of tile t+1) may
-            // stay in flight
-            if (tile + 2 < n_tiles) wait_vm<SH::NQ>();
-            else wait_vm<0>();
+            if (tile + 3 < n_tiles) rows_of(tile + 3, r3);
+        } else {
+            if (tile + 2 < n_tiles) issue(nb2, nm2, tile + 2);   // into registers; landed at the tail
+        }
+        float tmax[2];
+        int flag = 0;
+        auto hook = [&](int s) __attribute__((always_inline)) {
+            constexpr int SK = SH::SK;
+            if (s == 0) {
+                soft_a(cm, mine, st);
+                if constexpr (KV == 0) {
+                    // the last gathers of tile t+3 (the rest go out in S and PV)
+                    if (tile + 3 < n_tiles) {
+#pragma unroll
+                        for (int q = GA + GB; q < SH::NQ; ++q) issue_row(nb3, nm3, tile + 3, q, r3.r[q]);
+                    }
+                }
+            }
+            if (s == (SK - 1) / 2) flag = soft_b(st, tmax);
+            if (s == SK - 1) soft_c(st, tmax, flag);
+        };
+        f32x4 sacc[4];
+        if (more1) {
+            s_part(nb1, sacc, tile + 3, nb3, nm3, r3, hook);
+        } else {
+#pragma unroll
+            for (int s = 0; s < SH::SK; ++s) hook(s);   // the same pieces, no S
         }
         __syncthreads();
-        return __builtin_amdgcn_readfirstlane(xf[0] | xf[1] | xf[2] | xf[3]);
+        const int any = __builtin_amdgcn_readfirstlane(xf[0] | xf[1] | xf[2] | xf[3]);
+        if (more1) send_scores(sacc, mine);
+        return any;
+    };
+    // tail of tile t: tile t+2 has landed, the partial scores of tile t+1 are
+    // published (first barrier of tile t+1)
+    auto tail = [&](int tile, uint8_t *nb2, float *nm2) __attribute__((always_inline)) {
+        if (tile + 1 >= n_tiles) return;
+        if constexpr (KV == 0) {
+            // only the gathers of tile t+3 (all issued after those of t+2)
+            // may stay in flight
+            if (tile + 3 < n_tiles) wait_vm<SH::NQ>();
+            else wait_vm<0>();
+        } else {
+            wait_vm<0>();
+            if (tile + 2 < n_tiles) land(nb2, nm2);
+        }
+        __syncthreads();
     };
 
     // second half: agree on new maxima if any head needs one (RESCALE: also
@@ -548,13 +584,16 @@ void attn_kernel(AttnParams p)
                 }
             }
             uint2 phi[2], plo[2];
-            weights(st.x, st.csc, st.pr, phi, plo);
+            float pr[2][4];
+            weights(st.x, st.csc, pr, phi, plo);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) st.psum[nt] = (pr[nt][0] + pr[nt][1]) + (pr[nt][2] + pr[nt][3]);
             put_p(xq, phi, plo);
             __syncthreads();
         }
         pv(cb, any ? xq : xp, dma_tile, nb3, nm3, r3);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) l_run[nt] += (st.pr[nt][0] + st.pr[nt][1]) + (st.pr[nt][2] + st.pr[nt][3]);
+        for (int nt = 0; nt < 2; ++nt) l_run[nt] += st.psum[nt];
     };
 
     using Fast = std::integral_constant<bool, false>;
@@ -583,22 +622,28 @@ void attn_kernel(AttnParams p)
         // wait for them is left inside the tile loops (s_waitcnt vmcnt(0))
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
-        // prologue: the first DEPTH-1 tiles
+        // prologue: tiles 0 and 1 in LDS (bf16: tile 2 too), S of tile 0 and
+        // its partial-score exchange
         issue(tiles[0], metas[0], 0);
         if constexpr (KV == 2) {
             wait_vm<0>();
             land(tiles[0], metas[0]);
         }
         if (n_tiles > 1) issue(tiles[1], metas[1], 1);
-        if constexpr (KV == 0) {
-            // the rows of tile 2 that PV(-1) would have issued
-            if (n_tiles > 2) {
-                Rows rw;
-                rows_of(2, rw);
-#pragma unroll
-                for (int q = 0; q < GA; ++q) issue_row(tiles[2], metas[2], 2, q, rw.r[q]);
-            }
+        if constexpr (KV == 2) {
             wait_vm<0>();
+            if (n_tiles > 1) land(tiles[1], metas[1]);
+        } else {
+            if (n_tiles > 2) issue(tiles[2], metas[2], 2);
+            wait_vm<0>();
+        }
+        __syncthreads();
+        f32x4 mine[2];
+        {
+            Rows none;
+            f32x4 sacc[4];
+            s_part(tiles[0], sacc, -1, tiles[0], metas[0], none, [](int) {});
+            send_scores(sacc, mine);
         }
         __syncthreads();
         int bi[DEPTH];
@@ -610,13 +655,15 @@ void attn_kernel(AttnParams p)
             for (int k = 0; k + 1 < DEPTH; ++k) bi[k] = bi[k + 1];
             bi[DEPTH - 1] = b0;
         };
-        Rows r3;   // row indices of tile t+3, read in front, used in PV
+        Rows r3;   // row indices of tile t+3 (bf16)
         auto fr = [&](int it, Soft &st) __attribute__((always_inline)) {
-            return front(it, tiles[bi[0]], metas[bi[0]], tiles[bi[1]], metas[bi[1]], tiles[bi[2]], metas[bi[2]],
-                         tiles[bi[DEPTH - 1]], metas[bi[DEPTH - 1]], st, r3);
+            return front(it, metas[bi[0]], tiles[bi[1]], tiles[bi[2]], metas[bi[2]], tiles[bi[DEPTH - 1]],
+                         metas[bi[DEPTH - 1]], st, mine, r3);
         };
         auto bk = [&](auto tag, int any, int it, Soft &st) __attribute__((always_inline)) {
             back(tag, any, tiles[bi[0]], st, it + 3, tiles[bi[DEPTH - 1]], metas[bi[DEPTH - 1]], r3);
+            tail(it, tiles[bi[2]], metas[bi[2]]);
+            rotate();
         };
         Soft st;
         int it = 0, any = 0;
@@ -626,15 +673,12 @@ void attn_kernel(AttnParams p)
             any = fr(it, st);
             if (any & 2) break;
             bk(Fast{}, any, it, st);
-            rotate();
         }
         if (it < n_tiles) {
             bk(Slow{}, any, it, st);
-            rotate();
             for (++it; it < n_tiles; ++it) {
                 any = fr(it, st);
                 bk(Slow{}, any, it, st);
-                rotate();
             }
         }
     }
