@@ -118,6 +118,9 @@ def time_loop(fn, iters, warmup):
     return e0.elapsed_time(e1) / iters        # ms
 
 
+GRAPH_CALLS = 10   # calls captured per graph: spreads the graph launch over several calls
+
+
 def capture(fn, per=1):
     """A HIP graph of `per` back-to-back calls of fn (the calls enqueue on the
     current stream, which is the capture stream inside the graph context)."""
@@ -174,29 +177,35 @@ def roofline(bound, achieved, peak, unit, traffic=None):
             "frac": round(achieved / peak, 5), "traffic": traffic}
 
 
-def prefill_secondary(iters):
-    case = W.prefill_case(T=8192, ratio=4)
+def prefill_secondary(iters, kv="bf16"):
+    if kv == "e4m3":
+        case = W.prefill_case(T=8192, ratio=4, kv_dtype="e4m3", q_scale=2.0 ** -7, seed=W.SEED_BASE + 35)
+    else:
+        case = W.prefill_case(T=8192, ratio=4)
     d = torch.device("cuda")
     q, win, cmp = case.q.to(d), case.win_pool.to(d), case.cmp_pool.to(d)
+    wsc = case.win_scale.to(d) if case.win_scale is not None else None
+    csc = case.cmp_scale.to(d) if case.cmp_scale is not None else None
     idx = sap.build_sparse_idx(case.pos.to(d), case.seq.to(d), case.n_win, case.win_pt.to(d), case.page,
                                case.cmp_logical.to(d), case.cmp_pt.to(d))
     out = torch.empty((case.T, 64, 512), dtype=torch.float32, device=d)
     valid = (idx >= 0).sum().item()
     flops = valid * 64 * 512 * 4.0
     ms = time_loop(lambda: sap.sparse_attn_paged(q, win, cmp, idx, case.n_win, case.sm_scale, out=out,
-                                                 num_splits=1), iters, 2)
+                                                 win_scale=wsc, cmp_scale=csc, num_splits=1), iters, 2)
     tf = flops / (ms * 1e-3) / 1e12
-    return {"workload": "prefill_s8192_r4_bf16", "us": round(ms * 1e3, 2), "tflops": round(tf, 2),
+    key = f"prefill_s8192_r4_{kv}"
+    # e4m3 rows are widened to bf16 tiles: the MFMAs are bf16 (P as hi + lo terms doubles PV)
+    return {"workload": key, "us": round(ms * 1e3, 2), "tflops": round(tf, 2),
             "gflop": round(flops / 1e9, 2),
-            "roofline": roofline("mfma", tf, BF16_PEAK_TFLOPS, "TFLOP/s",
-                                 traffic=counted_traffic("prefill_s8192_r4_bf16"))}
+            "roofline": roofline("mfma", tf, BF16_PEAK_TFLOPS, "TFLOP/s", traffic=counted_traffic(key))}
 
 
 def decode_secondary(B, kv, iters):
     st = DecodeStep(B=B, kv_dtype=kv, seed=W.SEED_BASE + (4 if kv == "e4m3" else 2))
     st.select()
-    ms_attn = time_graph(st.attend, iters, 5)
-    ms_step = time_graph(st.step, iters, 5)
+    ms_attn = time_graph(st.attend, iters // GRAPH_CALLS, 1, GRAPH_CALLS)
+    ms_step = time_graph(st.step, iters // GRAPH_CALLS, 1, GRAPH_CALLS)
     gb = st.attn_alg_bytes() / (ms_attn * 1e-3) / 1e9
     return {"workload": f"decode_b{B}_pos32767_r4_{kv}", "attn_us": round(ms_attn * 1e3, 2),
             "step_us": round(ms_step * 1e3, 2),
@@ -211,8 +220,10 @@ def indexer_secondary(B, iters):
     out = torch.empty((B, case.N), dtype=torch.float32, device=d)
     sel = torch.empty((B, 512), dtype=torch.int32, device=d)
     ws = torch.empty(max(sap.topk_workspace_bytes(B, case.N, 512), 1), dtype=torch.uint8, device=d)
-    ms_idx = time_graph(lambda: sap.indexer_logits_packed(q, w, pool, pt, case.page, case.N, out=out), iters, 5)
-    ms_topk = time_graph(lambda: sap.topk_select(out, 512, out=sel, workspace=ws), iters, 5)
+    ms_idx = time_graph(lambda: sap.indexer_logits_packed(q, w, pool, pt, case.page, case.N, out=out),
+                        iters // GRAPH_CALLS, 1, GRAPH_CALLS)
+    ms_topk = time_graph(lambda: sap.topk_select(out, 512, out=sel, workspace=ws), iters // GRAPH_CALLS, 1,
+                         GRAPH_CALLS)
     alg = B * (case.N * 68 + case.N * 4 + 32 * 128 * 2 + 32 * 4)
     gb = alg / (ms_idx * 1e-3) / 1e9
     return {"workload": f"indexer_b{B}_ctx131072", "indexer_us": round(ms_idx * 1e3, 2),
@@ -261,11 +272,14 @@ def main():
     st = DecodeStep(B=1, pos=32767, ratio=4)
 
     log("timing whole steps (graph replays; eager launches for reference)")
-    ms_step = time_graph(st.step, args.steps, args.warmup)
+    # a graph holds GRAPH_CALLS steps back to back; K = steps (a multiple of it)
+    reps = max(1, args.steps // GRAPH_CALLS)
+    args.steps = reps * GRAPH_CALLS
+    ms_step = time_graph(st.step, reps, max(1, args.warmup // GRAPH_CALLS), GRAPH_CALLS)
     ms_step_eager = time_loop(st.step, args.steps, args.warmup)
     log("timing the attention launches alone")
-    ms_attn = time_graph(st.attend, args.steps, args.warmup)
-    ms_sel = time_graph(st.select, args.steps, args.warmup)
+    ms_attn = time_graph(st.attend, reps, 1, GRAPH_CALLS)
+    ms_sel = time_graph(st.select, reps, 1, GRAPH_CALLS)
     value = st.gathered_bytes() / (ms_step * 1e-3) / 1e9
     attn_gbs = st.attn_alg_bytes() / (ms_attn * 1e-3) / 1e9
 
@@ -276,7 +290,7 @@ def main():
         "config": {"workload": "decode_b1_pos32767_r4_bf16", "global_batch": 1, "seq_len": 32768, "heads": 64,
                    "head_dim": 512, "window": 128, "topk": 512, "ratio": 4, "parallelism": "single-gpu",
                    "step": "indexer(8192 fp4 keys) + top-512 + index build + split-K attention + merge"},
-        "timing": "HIP-graph replays of the whole step, HIP events around the timed replays",
+        "timing": f"HIP-graph replays ({GRAPH_CALLS} steps per graph), HIP events around the timed replays",
         "eager_ms_per_step": round(ms_step_eager, 5),
         "attn_us": round(ms_attn * 1e3, 3), "select_us": round(ms_sel * 1e3, 3), "splits": st.splits,
         "roofline": roofline("hbm", attn_gbs, HBM_PEAK_GBS, "GB/s",
@@ -288,6 +302,8 @@ def main():
         sec = []
         log("secondary: prefill S8192 r4")
         sec.append(prefill_secondary(10))
+        log("secondary: prefill S8192 r4 e4m3")
+        sec.append(prefill_secondary(5, "e4m3"))
         for B, kv in ((8, "bf16"), (8, "e4m3")):
             log(f"secondary: decode B{B} {kv}")
             sec.append(decode_secondary(B, kv, 100))

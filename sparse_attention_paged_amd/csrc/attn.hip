@@ -34,7 +34,7 @@
 //    read back from LDS in the B-operand layout; the V^T A-operand is read
 //    from the row-major tile with ds_read_b64_tr_b16 (within 16 lanes, lane i
 //    receives element i%4 of the 8 bytes addressed by lanes i/4 + 4r,
-//    r = 0..3).  e4m3 pools feed P as a hi + lo pair of bf16 terms.
+//    r = 0..3).  e4m3 pools feed P as hi + mid + lo bf16 terms.
 // The PV reduction index kk = 8g + 4c + i stands for tile column
 // 16c + 4g + i, which lets each lane take its own 4 weights of column half c
 // straight from the softmax layout.
@@ -156,7 +156,10 @@ void attn_kernel(AttnParams p)
 {
     using SH = AttnShape<D>;
     using Raw = typename RawRow<KV>::T;
-    constexpr int NP = KV == 2 ? 2 : 1;   // P terms per weight (e4m3: hi + lo)
+    // bf16 terms per PV weight: e4m3 weights carry the row scale and PV must
+    // hold them to fp32-like precision (outputs reach ~1e3 against an
+    // absolute bar), so they go in as hi + mid + lo (relative error ~2^-25)
+    constexpr int NP = KV == 2 ? 3 : 1;
     // rotating tiles (bf16: 4, the gathers of tile t+3 are issued while tile
     // t computes; e4m3: 3, rows pass through registers), each tile's
     // per-column bias (0 or -inf) and dequant scale, and the row indices of
@@ -354,9 +357,10 @@ void attn_kernel(AttnParams p)
     };
 
     // weights of the owned heads against the current max: per head tile nt,
-    // 4 columns packed as bf16 (and the lo terms for e4m3)
-    auto weights = [&](const float (&x)[2][4], const float (&csc)[4], float (&pr)[2][4], uint2 (&hi)[2],
-                       uint2 (&lo)[2]) __attribute__((always_inline)) {
+    // 4 columns packed as bf16 (e4m3: NP terms, each the bf16 rounding of
+    // what the previous terms left)
+    auto weights = [&](const float (&x)[2][4], const float (&csc)[4], float (&pr)[2][4],
+                       uint2 (&pt)[NP][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             const float mr = dq ? m_run[2 + nt] : m_run[nt];
@@ -364,25 +368,25 @@ void attn_kernel(AttnParams p)
 #pragma unroll
             for (int i = 0; i < 4; ++i) pr[nt][i] = fast_exp2(x[nt][i] - msub);
             if constexpr (KV == 2) {
-                float a[4], b[4];
+                float r[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    a[i] = pr[nt][i] * csc[i];
-                    b[i] = a[i] - __uint_as_float(bf16_bits(a[i]) << 16);
+                for (int i = 0; i < 4; ++i) r[i] = pr[nt][i] * csc[i];
+#pragma unroll
+                for (int e = 0; e < NP; ++e) {
+                    pt[e][nt] = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) r[i] -= __uint_as_float(bf16_bits(r[i]) << 16);
                 }
-                hi[nt] = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
-                lo[nt] = make_uint2(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
             } else {
-                hi[nt] = make_uint2(pack_bf16x2(pr[nt][0], pr[nt][1]), pack_bf16x2(pr[nt][2], pr[nt][3]));
+                pt[0][nt] = make_uint2(pack_bf16x2(pr[nt][0], pr[nt][1]), pack_bf16x2(pr[nt][2], pr[nt][3]));
             }
         }
     };
-    auto put_p = [&](uint2 (*px)[2][2][2][64], const uint2 (&hi)[2], const uint2 (&lo)[2]) __attribute__((always_inline)) {
+    auto put_p = [&](uint2 (*px)[2][2][2][64], const uint2 (&pt)[NP][2]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            px[0][dq][nt][ch][lane] = hi[nt];
-            if constexpr (KV == 2) px[NP - 1][dq][nt][ch][lane] = lo[nt];
-        }
+        for (int e = 0; e < NP; ++e)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) px[e][dq][nt][ch][lane] = pt[e][nt];
     };
 
     // --- O^T += V^T P^T for head_dim quarter w; P^T of head tile j comes from
@@ -412,10 +416,10 @@ void attn_kernel(AttnParams p)
             const uint4 a = vr[m % 3];
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[m][j] = mfma16x16x32(a, pb[0][j], acc[m][j]);
-            if constexpr (KV == 2) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[m][j] = mfma16x16x32(a, pb[1][j], acc[m][j]);
-            }
+            for (int e = 1; e < NP; ++e)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[m][j] = mfma16x16x32(a, pb[e][j], acc[m][j]);
             // bf16: the remaining gather instructions of tile t+3, one per
             // m-step, so the memory pipeline fills while the MFMAs run
             if constexpr (KV == 0) {
@@ -469,12 +473,12 @@ void attn_kernel(AttnParams p)
     };
     // (c) weights against the current max, published with the maxima and flags
     auto soft_c = [&](Soft &st, const float (&tmax)[2], int flag) __attribute__((always_inline)) {
-        uint2 phi[2], plo[2];
+        uint2 pt[NP][2];
         float pr[2][4];
-        weights(st.x, st.csc, pr, phi, plo);
+        weights(st.x, st.csc, pr, pt);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) st.psum[nt] = (pr[nt][0] + pr[nt][1]) + (pr[nt][2] + pr[nt][3]);
-        put_p(xp, phi, plo);
+        put_p(xp, pt);
         if (g == 0) {
             xm[w][l16] = tmax[0];
             xm[w][16 + l16] = tmax[1];
@@ -583,12 +587,12 @@ void attn_kernel(AttnParams p)
                     if (mr == -INFINITY && mt > -INFINITY) m_run[j] = mt;
                 }
             }
-            uint2 phi[2], plo[2];
+            uint2 pt[NP][2];
             float pr[2][4];
-            weights(st.x, st.csc, pr, phi, plo);
+            weights(st.x, st.csc, pr, pt);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) st.psum[nt] = (pr[nt][0] + pr[nt][1]) + (pr[nt][2] + pr[nt][3]);
-            put_p(xq, phi, plo);
+            put_p(xq, pt);
             __syncthreads();
         }
         pv(cb, any ? xq : xp, dma_tile, nb3, nm3, r3);

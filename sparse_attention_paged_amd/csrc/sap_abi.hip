@@ -33,6 +33,9 @@ SplitPlan plan_splits(int T, int H, int n_cols, int requested)
         const int hb = (H + sap::kAttnHeadsPerBlock - 1) / sap::kAttnHeadsPerBlock;
         const int64_t wgs = (int64_t)T * hb;
         s = wgs >= 128 ? 1 : (int)((160 + wgs - 1) / wgs);
+        // a split's fixed cost (its q, index and first-gather round trips,
+        // its partial output) is worth about two tiles of columns
+        if (s > (tiles + 1) / 2) s = (tiles + 1) / 2;
     }
     if (s > tiles) s = tiles;
     if (s < 1) s = 1;

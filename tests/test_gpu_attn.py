@@ -105,10 +105,18 @@ def _sample_tokens(T, n_rand, seed):
     return sorted(set(fixed + rnd))
 
 
-@pytest.mark.parametrize("variant", ["r4_s8192", "r128_s8192", "r0_s8192", "r4_s4096_at28672"])
+@pytest.mark.parametrize("variant", ["r4_s8192", "r128_s8192", "r0_s8192", "r4_s4096_at28672",
+                                     "r4_s8192_e4m3", "r4_s4096_at28672_e4m3"])
 def test_prefill_sampled(variant):
     need_gpu()
-    if variant == "r4_s8192":
+    if variant == "r4_s8192_e4m3":
+        # fp8 KV in prefill: the e4m3 read path with per-row scales (q carries 2^-7)
+        case = W.prefill_case(T=8192, ratio=4, kv_dtype="e4m3", q_scale=2.0 ** -7, seed=W.SEED_BASE + 35)
+    elif variant == "r4_s4096_at28672_e4m3":
+        # a chunk of chunked prefill re-reading an e4m3 prefix
+        case = W.prefill_case(T=4096, start=28672, ratio=4, kv_dtype="e4m3", q_scale=2.0 ** -7,
+                              seed=W.SEED_BASE + 36)
+    elif variant == "r4_s8192":
         case = W.prefill_case(T=8192, ratio=4)
     elif variant == "r128_s8192":
         case = W.prefill_case(T=8192, ratio=128, seed=W.SEED_BASE + 31)
@@ -122,7 +130,8 @@ def test_prefill_sampled(variant):
     toks = _sample_tokens(case.T, 24, 7)
     idx = oracle.case_idx(case)
     assert torch.equal(gidx.cpu(), idx)
-    ref = oracle.sparse_attn(case.q[toks], case.win_pool, case.cmp_pool, idx[toks], case.n_win, case.sm_scale)
+    ref = oracle.sparse_attn(case.q[toks], case.win_pool, case.cmp_pool, idx[toks], case.n_win, case.sm_scale,
+                             case.win_scale, case.cmp_scale)
     assert_attn_close(out[toks], ref, f"{len(toks)} sampled tokens")
 
 
