@@ -23,6 +23,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -155,6 +156,17 @@ def time_graph(fn, iters, warmup, per=1):
     return e0.elapsed_time(e1) / (iters * per)
 
 
+def code_sha256(src: str) -> str:
+    """sha256 of a C++ source with its // comments and blank lines removed
+    (a comment edit does not make the counters stale; a code edit does)."""
+    lines = []
+    for ln in src.splitlines():
+        ln = re.sub(r"//.*$", "", ln).rstrip()
+        if ln.strip():
+            lines.append(ln)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def counted_traffic(key):
     """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
     (profiles/attn_traffic_counters.json), or None when attn.hip changed since
@@ -163,11 +175,11 @@ def counted_traffic(key):
     try:
         with open(os.path.join(here, "profiles", "attn_traffic_counters.json")) as f:
             doc = json.load(f)
-        with open(os.path.join(here, "sparse_attention_paged_amd", "csrc", "attn.hip"), "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        with open(os.path.join(here, "sparse_attention_paged_amd", "csrc", "attn.hip")) as f:
+            sha = code_sha256(f.read())
     except (OSError, ValueError):
         return None
-    if doc.get("attn_source_sha256") != sha or key not in doc:
+    if doc.get("attn_code_sha256") != sha or key not in doc:
         return None
     return doc[key]["traffic_bytes"]
 
@@ -195,7 +207,7 @@ def prefill_secondary(iters, kv="bf16"):
                                                  win_scale=wsc, cmp_scale=csc, num_splits=1), iters, 2)
     tf = flops / (ms * 1e-3) / 1e12
     key = f"prefill_s8192_r4_{kv}"
-    # e4m3 rows are widened to bf16 tiles: the MFMAs are bf16 (P as hi + lo terms doubles PV)
+    # e4m3 rows are widened to bf16 tiles: the MFMAs are bf16 (P as three bf16 terms triples PV)
     return {"workload": key, "us": round(ms * 1e3, 2), "tflops": round(tf, 2),
             "gflop": round(flops / 1e9, 2),
             "roofline": roofline("mfma", tf, BF16_PEAK_TFLOPS, "TFLOP/s", traffic=counted_traffic(key))}

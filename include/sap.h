@@ -110,8 +110,12 @@ int sap_build_sparse_idx(const int32_t *pos, const int32_t *seq, int T, int n_wi
  * D:        64, 128, 256 or 512.  H >= 1.  n_win + n_cmp <= 65536.
  * num_splits: 1 = one pass per token (prefill); k > 1 = split the columns
  *           into k ranges and merge the partial (max, sum, output) triples
- *           (decode); 0 = choose automatically.  Results agree with the
- *           single pass up to fp32 rounding.
+ *           (decode); 0 = choose automatically (about two 32-column tiles
+ *           per split while the launch has fewer than 128 workgroups).  The
+ *           merge is exact algebra, but each split rounds its softmax weights
+ *           to bf16 against its own running max, so split counts agree with
+ *           the single pass to the same tolerance as with an exact result,
+ *           not bit for bit.
  * workspace: device scratch of at least sap_sparse_attn_workspace_bytes(T,
  *           H, D, n_win + n_cmp, num_splits) bytes, 256-byte aligned; may be
  *           NULL when that size is 0.

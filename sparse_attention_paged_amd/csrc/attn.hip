@@ -15,20 +15,23 @@
 // (64 heads as the MFMA N dimension) and every score is exponentiated once:
 //  - gather: each wave moves 8 of the tile's 32 rows straight from HBM into
 //    LDS (global_load_lds_dwordx4, 16 bytes per lane; one wave instruction
-//    moves one 1 KiB row at D = 512), chunk-swizzled per row.  Three LDS
-//    tiles rotate, so tile t+2 is in flight while tile t computes.  e4m3 rows
-//    go through registers and are widened to bf16 on the way.
+//    moves one 1 KiB row at D = 512), chunk-swizzled per row.  bf16: four LDS
+//    tiles rotate and the gathers of tile t+3 are spread over the S, softmax
+//    and PV phases of tiles t+1 and t; e4m3: three tiles, rows go through
+//    registers and are widened to bf16 on the way.
 //  - S^T = K Q^T on MFMA 16x16x32 bf16 (M = columns, N = heads): wave
 //    (dq, ch) = (w & 1, w >> 1) takes columns 16ch .. 16ch+15, all 64 heads,
 //    head_dim half dq.  The two head_dim halves of a column half add their
 //    partial scores through LDS: each keeps the 32 heads whose softmax it
 //    owns (32dq .. 32dq+31) and receives the partner's partial for them.
 //  - online softmax in the log2 domain over the owned 32 heads x 16 columns
-//    (8 scores per lane).  The running max only moves when a tile's max
-//    exceeds it by more than 8 (so weights stay <= 2^8): each wave computes P
-//    against the current max and publishes its tile max; if any head of the
-//    workgroup needs a larger max (first tile, rare later), all waves agree on
-//    the new maxima, rescale and recompute.
+//    (8 scores per lane), placed between the MFMAs of the next tile's S
+//    (software pipelined).  The running max only moves when a tile's max
+//    exceeds it by more than 32 (weights stay <= 2^32); a head's first max
+//    needs no rescale of O.  A later move beyond the slack (rare) leaves the
+//    fast tile loop for a second loop that rescales O after all waves agree
+//    on the new maxima, so the fast loop does no VALU work on the
+//    accumulators.
 //  - O^T += V^T P^T on MFMA 16x16x32 bf16 (M = head_dim, N = heads, K = the
 //    32 columns): wave w owns head_dim quarter w for all 64 heads.  P^T is
 //    read back from LDS in the B-operand layout; the V^T A-operand is read
