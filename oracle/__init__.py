@@ -55,6 +55,9 @@ def lib():
         L.orc_indexer_logits.argtypes = [I, I, I, P, I64, P, I64, P, I64, P, I64, I, P, I,
                                          P, I64]
         L.orc_indexer_logits.restype = I
+        L.orc_indexer_candidates.argtypes = [I, I, I, P, I64, P, I64, P, I64, P, I64, I, P, I64, P, I,
+                                             P, I64]
+        L.orc_indexer_candidates.restype = I
         L.orc_topk.argtypes = [I, I, P, I64, P, I, P, I64]
         L.orc_topk.restype = I
         L.orc_num_threads.argtypes = []; L.orc_num_threads.restype = I
@@ -200,6 +203,39 @@ def indexer_logits(q, w, key_pool, page_table, page, n_keys, N) -> torch.Tensor:
 def case_indexer(case) -> torch.Tensor:
     return indexer_logits(case.q, case.w, case.key_pool, case.page_table, case.page,
                           case.n_keys, case.N)
+
+
+def indexer_prefill_logits(q, w, key_pool, page_table, page, tok_start, n_keys, N) -> torch.Tensor:
+    """float64 [T, N].  Prefill mode: token t of sequence s (rows tok_start[s]
+    .. tok_start[s+1]-1) is scored like a full-mode query over sequence s's
+    keys, with its own visible count n_keys[t] (the causal mask)."""
+    ts = _cpu(tok_start, torch.int64)
+    pt = _cpu(page_table, torch.int32)
+    T = int(ts[-1])
+    seq = torch.repeat_interleave(torch.arange(ts.numel() - 1), ts[1:] - ts[:-1])
+    assert seq.numel() == T
+    return indexer_logits(q, w, key_pool, pt[seq].contiguous(), page, n_keys, N)
+
+
+def indexer_candidates(q, w, key_pool, page_table, page, cand, n_keys) -> torch.Tensor:
+    """float64 [T, NC]: candidate-mode logits (page_table [T, pages], one row
+    per token, or None: candidates are pool rows)."""
+    q = _cpu(q, torch.bfloat16)
+    w = _cpu(w, torch.float32)
+    key_pool = _cpu(key_pool, torch.int32)
+    pt = _cpu(page_table, torch.int32) if page_table is not None else None
+    cand = _cpu(cand, torch.int32)
+    nk = _cpu(n_keys, torch.int32) if n_keys is not None else None
+    T, Hi, Dk = q.shape
+    NC = cand.shape[1]
+    out = torch.empty((T, NC), dtype=torch.float64)
+    rc = lib().orc_indexer_candidates(T, Hi, Dk, _p(q), q.stride(0), _p(w), w.stride(0),
+                                      _p(key_pool), key_pool.stride(0), _p(pt),
+                                      pt.stride(0) if pt is not None else 0, page, _p(cand), cand.stride(0),
+                                      _p(nk), NC, _p(out), out.stride(0))
+    if rc != 0:
+        raise ValueError(f"orc_indexer_candidates rejected its arguments ({rc})")
+    return out
 
 
 def topk(x, k, n_valid=None) -> torch.Tensor:

@@ -357,6 +357,55 @@ int orc_indexer_logits(int B, int Hi, int Dk, const uint16_t *q, int64_t q_sb,
     return 0;
 }
 
+/*
+ * Indexer logits, candidate mode ("perf(kernel): read dsv41 indexer key rows
+ * as int32 words": the Reindex layers score a list of NC candidate rows per
+ * query instead of every key).  Token t scores the keys whose logical
+ * positions are listed in cand[t, 0 .. NC-1]:
+ *   logits[t, c] = sum_h w[t, h] * max(0, q[t, h, :] . k_{cand[t, c]})
+ * and -inf where cand[t, c] < 0 (no candidate) or cand[t, c] >= n_keys[t]
+ * (not visible to the token).  A logical position n maps to pool row
+ * page_table[t * pt_sb + n / page] * page + n % page, or to row n itself
+ * when page_table is NULL.  Same key decode and score as full mode.
+ */
+int orc_indexer_candidates(int T, int Hi, int Dk, const uint16_t *q, int64_t q_sb,
+                           const float *w, int64_t w_sb,
+                           const int32_t *key_pool, int64_t row_words,
+                           const int32_t *page_table, int64_t pt_sb, int page,
+                           const int32_t *cand, int64_t cand_sb, const int32_t *n_keys,
+                           int NC, double *logits, int64_t logits_sb)
+{
+    if (Dk != 128 || row_words < 17 || T < 0 || Hi <= 0 || NC < 0)
+        return -3;
+    if (page_table && page <= 0)
+        return -3;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int c = 0; c < NC; ++c) {
+            const int32_t n = cand[(int64_t)t * cand_sb + c];
+            double acc = 0.0;
+            double k[128];
+            int64_t row;
+            if (n < 0 || (n_keys && n >= n_keys[t])) {
+                logits[(int64_t)t * logits_sb + c] = -INFINITY;
+                continue;
+            }
+            row = page_table ? (int64_t)page_table[(int64_t)t * pt_sb + n / page] * page + n % page
+                             : (int64_t)n;
+            for (int d = 0; d < 128; ++d)
+                k[d] = orc_fp4_row_element(key_pool + row * row_words, d);
+            for (int h = 0; h < Hi; ++h) {
+                double dot = 0.0;
+                for (int d = 0; d < 128; ++d)
+                    dot += orc_bf16_to_double(q[(int64_t)t * q_sb + (int64_t)h * 128 + d]) * k[d];
+                acc += (double)w[(int64_t)t * w_sb + h] * (dot > 0.0 ? dot : 0.0);
+            }
+            logits[(int64_t)t * logits_sb + c] = acc;
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------ */
 /* Exact top-k selection                                                */
 /* ------------------------------------------------------------------ */

@@ -115,3 +115,68 @@ def test_topk_degenerate_rows():
     assert out[1].tolist() == [4, -1, -1, -1]
     assert out[2].tolist() == [0, 1, 2, 3]                          # all tied: lowest indices
     assert oracle.topk(x, 0).shape == (3, 0)
+
+
+def _seq_keys(key_pool, pt_row, n):
+    rows = torch.stack([key_pool[int(pt_row[j // W.PAGE]) * W.PAGE + j % W.PAGE] for j in range(n)])
+    return _torch_decode_rows(rows)
+
+
+def test_indexer_candidates_brute_force():
+    """Candidate mode against torch, candidate by candidate, with planted -1,
+    duplicate and beyond-visible entries and signed head weights."""
+    case = W.indexer_cand_case(T=3, n_ctx=700, NC=96, seed=23, extras=True, sort=False)
+    out = oracle.indexer_candidates(case.q, case.w, case.key_pool, case.page_table, case.page, case.cand,
+                                    case.n_keys)
+    assert out.shape == (3, 96)
+    assert (case.w < 0).any()
+    for t in range(3):
+        k_all = _seq_keys(case.key_pool, case.page_table[t], int(case.n_keys[t]))
+        s = torch.relu(case.q[t].to(torch.float64) @ k_all.T)            # [Hi, n]
+        full = (case.w[t].to(torch.float64).unsqueeze(1) * s).sum(0)
+        for c in range(96):
+            n = int(case.cand[t, c])
+            if n < 0 or n >= int(case.n_keys[t]):
+                assert out[t, c].item() == -math.inf
+            else:
+                assert abs(out[t, c].item() - full[n].item()) <= 1e-12 * max(1.0, abs(full[n].item()))
+    assert out[:, 1].eq(-math.inf).all() and out[:, 3].eq(-math.inf).all()
+    assert torch.equal(out[:, 0], out[:, 2])
+
+
+def test_indexer_candidates_gather_full_mode():
+    """Listing every key in order reproduces full mode; a permuted list
+    permutes the logits; NULL page table means candidates are pool rows."""
+    case = W.indexer_case(B=2, N=200, seed=24, n_keys=[200, 150])
+    full = oracle.case_indexer(case)
+    cand = torch.arange(200, dtype=torch.int32).repeat(2, 1)
+    out = oracle.indexer_candidates(case.q, case.w, case.key_pool, case.page_table, case.page, cand, case.n_keys)
+    assert torch.equal(out, full)
+    perm = torch.randperm(200, generator=torch.Generator().manual_seed(5)).to(torch.int32)
+    outp = oracle.indexer_candidates(case.q, case.w, case.key_pool, case.page_table, case.page,
+                                     perm.repeat(2, 1), case.n_keys)
+    assert torch.equal(outp, full[:, perm.long()])
+    rows = torch.tensor([[W.pool_row(case.page_table, b, n) for n in range(200)] for b in range(2)],
+                        dtype=torch.int32)
+    outr = oracle.indexer_candidates(case.q, case.w, case.key_pool, None, case.page, rows, case.n_keys + 10 ** 6)
+    assert torch.equal(outr, torch.where(torch.isinf(full), outr, full))
+    assert torch.equal(outr[0], full[0])
+
+
+def test_indexer_prefill_causal_brute_force():
+    """Prefill mode over two sequences against a dense torch product with the
+    causal mask n < ceil((p+1)/r) applied afterwards."""
+    case = W.indexer_prefill_case(lengths=(70, 33), starts=(0, 230), ratio=2, seed=25)
+    out = oracle.indexer_prefill_logits(case.q, case.w, case.key_pool, case.page_table, case.page,
+                                        case.tok_start, case.n_keys, case.N)
+    assert out.shape == (103, case.N)
+    for s in range(2):
+        a, b = int(case.tok_start[s]), int(case.tok_start[s + 1])
+        k = _seq_keys(case.key_pool, case.page_table[s], case.N)
+        sc = torch.relu(torch.einsum("thd,nd->thn", case.q[a:b].to(torch.float64), k))
+        ref = (case.w[a:b].to(torch.float64).unsqueeze(2) * sc).sum(1)      # [Ts, N]
+        nk = ((case.pos[a:b].to(torch.int64) + 2) // 2)
+        mask = torch.arange(case.N).unsqueeze(0) < nk.unsqueeze(1)
+        assert torch.equal(nk.to(torch.int32), case.n_keys[a:b])
+        np.testing.assert_allclose(out[a:b][mask].numpy(), ref[mask].numpy(), rtol=1e-12, atol=1e-12)
+        assert out[a:b][~mask].eq(-math.inf).all()

@@ -300,3 +300,124 @@ def indexer_case(B: int = 1, N: int = 131072, Hi: int = 32, Dk: int = 128,
     nk = torch.tensor(n_keys if n_keys is not None else [N] * B, dtype=torch.int32)
     return IndexerCase(name=f"indexer_b{B}_n{N}", q=q, w=w, key_pool=pool, page_table=pt,
                        n_keys=nk, N=N, page=page)
+
+
+@dataclass
+class IndexerPrefillCase:
+    """S sequences of query tokens: the tokens of sequence s are rows
+    tok_start[s] .. tok_start[s+1]-1 of q [T, Hi, Dk] bf16 and w [T, Hi] fp32
+    and sit at positions pos[t]; n_keys[t] = keys visible to token t (causal);
+    key_pool / page_table [S, pages] as in IndexerCase; N = logits width."""
+    name: str
+    q: torch.Tensor
+    w: torch.Tensor
+    key_pool: torch.Tensor
+    page_table: torch.Tensor
+    tok_start: torch.Tensor
+    pos: torch.Tensor
+    n_keys: torch.Tensor
+    N: int
+    ratio: int
+    page: int = PAGE
+
+    @property
+    def T(self):
+        return int(self.q.shape[0])
+
+    @property
+    def max_tokens(self):
+        return int((self.tok_start[1:] - self.tok_start[:-1]).max()) if self.tok_start.numel() > 1 else 0
+
+
+def indexer_prefill_case(lengths=(8192,), starts=(0,), ratio: int = 2, Hi: int = 32, Dk: int = 128,
+                         seed: int = SEED_BASE + 40, w_signed: bool = True, N: Optional[int] = None,
+                         exp_lo: int = 120, exp_hi: int = 134) -> IndexerPrefillCase:
+    """Sequence s holds lengths[s] query tokens at positions starts[s] ..;
+    its keys are the compressed entries at ratio r (r = 1: one key per token)
+    and token p sees ceil((p+1)/r) of them.  N defaults to the largest
+    visible count.  w ~ U(-1, 1) when w_signed (the score allows any sign)."""
+    g = make_generator(seed)
+    S = len(lengths)
+    pos = torch.cat([torch.arange(st, st + ln, dtype=torch.int32) for ln, st in zip(lengths, starts)]) \
+        if S else torch.zeros(0, dtype=torch.int32)
+    nk = _n_visible_cmp(pos, ratio).to(torch.int32)
+    if N is None:
+        N = int(nk.max()) if nk.numel() else 0
+    T = int(pos.numel())
+    q = _normal_bf16((T, Hi, Dk), g)
+    w = torch.rand((T, Hi), generator=g).to(torch.float32)
+    if w_signed:
+        w = w * 2.0 - 1.0
+    pages = max(1, math.ceil(N / PAGE))
+    pt = page_table(S, pages, g)
+    pool = fp4_key_rows(S * pages * PAGE, g, exp_lo, exp_hi)
+    ts = torch.zeros(S + 1, dtype=torch.int32)
+    if S:
+        ts[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int32), 0)
+    name = "indexer_prefill_" + "_".join(f"n{ln}s{st}" for ln, st in zip(lengths, starts)) + f"_r{ratio}"
+    return IndexerPrefillCase(name=name, q=q, w=w, key_pool=pool, page_table=pt, tok_start=ts, pos=pos,
+                              n_keys=nk, N=N, ratio=ratio)
+
+
+@dataclass
+class IndexerCandCase:
+    """T query tokens, each scoring the NC candidates cand[t] (logical key
+    positions, -1 = none) of its sequence: q [T, Hi, Dk] bf16, w [T, Hi] fp32,
+    page_table [T, pages] (one row per token; an expanded view with stride 0
+    when all tokens share one sequence), n_keys [T]."""
+    name: str
+    q: torch.Tensor
+    w: torch.Tensor
+    key_pool: torch.Tensor
+    page_table: torch.Tensor
+    cand: torch.Tensor
+    n_keys: torch.Tensor
+    page: int = PAGE
+
+    @property
+    def T(self):
+        return int(self.q.shape[0])
+
+    @property
+    def NC(self):
+        return int(self.cand.shape[1])
+
+
+def indexer_cand_case(T: int = 1, n_ctx: int = 131072, NC: int = 16384, shared_seq: bool = False,
+                      start: Optional[int] = None, Hi: int = 32, Dk: int = 128, seed: int = SEED_BASE + 45,
+                      sort: bool = True, w_signed: bool = True, extras: bool = False) -> IndexerCandCase:
+    """Decode (shared_seq False): T sequences with n_ctx keys each, one query
+    token each.  Prefill (shared_seq True): T tokens of one sequence at
+    positions start .. start+T-1 (r = 1: token p sees p+1 keys).  Each token's
+    candidates are min(NC, visible) distinct visible keys (ascending when
+    sort, as a top-k hands them over), padded with -1.  extras plants, per
+    token, a -1 inside the list, a duplicate and a key beyond the visible
+    count (those score -inf)."""
+    g = make_generator(seed)
+    if shared_seq:
+        st = n_ctx - T if start is None else start
+        nk = torch.arange(st, st + T, dtype=torch.int32) + 1
+        n_keys_pool, S = int(nk.max()) if T else 0, 1
+    else:
+        nk = torch.full((T,), n_ctx, dtype=torch.int32)
+        n_keys_pool, S = n_ctx, T
+    q = _normal_bf16((T, Hi, Dk), g)
+    w = torch.rand((T, Hi), generator=g).to(torch.float32)
+    if w_signed:
+        w = w * 2.0 - 1.0
+    pages = max(1, math.ceil((n_keys_pool + 1) / PAGE))
+    pt = page_table(S, pages, g)
+    pool = fp4_key_rows(S * pages * PAGE, g)
+    cand = random_unique_indices(nk, NC, g)
+    if sort:
+        big = torch.iinfo(torch.int32).max
+        cand = torch.where(cand < 0, torch.full_like(cand, big), cand).sort(dim=1).values
+        cand = torch.where(cand == big, torch.full_like(cand, -1), cand)
+    if extras and NC >= 4:
+        for t in range(T):
+            cand[t, 1] = -1
+            cand[t, 2] = cand[t, 0]
+            cand[t, 3] = int(nk[t])          # one past the visible keys
+    pt_tok = pt.expand(T, pages) if shared_seq else pt
+    name = f"indexer_cand_t{T}_ctx{n_ctx}_nc{NC}" + ("_shared" if shared_seq else "")
+    return IndexerCandCase(name=name, q=q, w=w, key_pool=pool, page_table=pt_tok, cand=cand, n_keys=nk)
