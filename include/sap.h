@@ -166,6 +166,67 @@ int sap_indexer_logits_packed(const void *q, int64_t q_stride_b,
                               int B, int Hi, int D, int N, sap_stream_t stream);
 
 /* -------------------------------------------------------------------------
+ * Indexer logits, candidate mode ("perf(kernel): read dsv41 indexer key rows
+ * as int32 words", Call path: the Reindex layers score a list of candidate
+ * rows; Kernel time: NC = 16384 candidates per query).  Token t scores the
+ * keys whose logical positions are listed in cand[t, 0 .. NC-1]:
+ *
+ *   logits[t, c] = sum_h w[t, h] * max(0, q[t, h, :] . k(cand[t, c]))
+ *
+ * and -inf where cand[t, c] < 0 (no candidate) or cand[t, c] >= n_keys[t].
+ * Position n maps to pool row page_table[t * pt_stride_t + n / page] * page
+ * + n % page (pt_stride_t = 0 when every token reads one sequence), or to
+ * row n itself when page_table is NULL.  Keys decode as in full mode.
+ *
+ * q [T, Hi, 128] bf16 (16-byte aligned rows), w [T, Hi] fp32,
+ * cand [T, NC] int32 (row stride cand_stride_t), n_keys [T] or NULL (no
+ * bound), logits [T, NC] fp32.  1 <= Hi <= 32, D = 128, T <= 65535.
+ * Candidate values below n_keys[t] must address rows inside the pool and
+ * pages inside the page table (not checked on the device).
+ * Errors: SAP_ERR_NULL, SAP_ERR_ALIGN, SAP_ERR_SHAPE, SAP_ERR_LAUNCH.
+ * ------------------------------------------------------------------------- */
+int sap_indexer_logits_candidates(const void *q, int64_t q_stride_t,
+                                  const float *w, int64_t w_stride_t,
+                                  const int32_t *key_pool, int64_t key_row_words,
+                                  const int32_t *page_table, int64_t pt_stride_t, int page,
+                                  const int32_t *cand, int64_t cand_stride_t,
+                                  const int32_t *n_keys,
+                                  float *logits, int64_t logits_stride_t,
+                                  int T, int Hi, int D, int NC, sap_stream_t stream);
+
+/* -------------------------------------------------------------------------
+ * Indexer logits, prefill mode with causal masking ("perf(kernel): read
+ * dsv41 indexer key rows as int32 words", Call path: the indexer runs in
+ * prefill and decode; Kernel time: full prefill of 2k / 8k prompts, 2k chunks
+ * at 128k context, bounded decoder variants).  S sequences; the query tokens
+ * of sequence s are rows tok_start[s] .. tok_start[s+1]-1 and score that
+ * sequence's keys:
+ *
+ *   logits[t, n] = sum_h w[t, h] * max(0, q[t, h, :] . k_s(n))  for n < n_keys[t]
+ *   logits[t, n] = -inf                                        for n_keys[t] <= n < N
+ *
+ * n_keys[t] is the number of keys token t may see (the caller's causal
+ * bound, e.g. ceil((p+1)/r) for a token at position p over entries of
+ * ratio r); NULL means N for every token.  Key n of sequence s is pool row
+ * page_table[s * pt_stride_s + n / page] * page + n % page, or s * N + n when
+ * page_table is NULL.
+ *
+ * tok_start [S + 1] int32 (device, non-decreasing); max_tokens >= every
+ * sequence's token count (the launch covers that many tokens per sequence).
+ * q [T, Hi, 128] bf16, w [T, Hi] fp32, logits [T, N] fp32 (row stride
+ * logits_stride_t >= N).  1 <= Hi <= 32, D = 128, S <= 65535.
+ * Errors: SAP_ERR_NULL, SAP_ERR_ALIGN, SAP_ERR_SHAPE, SAP_ERR_LAUNCH.
+ * ------------------------------------------------------------------------- */
+int sap_indexer_logits_prefill(const void *q, int64_t q_stride_t,
+                               const float *w, int64_t w_stride_t,
+                               const int32_t *key_pool, int64_t key_row_words,
+                               const int32_t *page_table, int64_t pt_stride_s, int page,
+                               const int32_t *tok_start, int S, int max_tokens,
+                               const int32_t *n_keys,
+                               float *logits, int64_t logits_stride_t,
+                               int Hi, int D, int N, sap_stream_t stream);
+
+/* -------------------------------------------------------------------------
  * Exact top-k selection (the index top-k of "perf(kernel): keep 16-byte kv
  * loads ...", Kernel time).  For each row b the candidates are the n <
  * n_valid[b] (n < N when n_valid is NULL) whose value is neither NaN nor -inf.

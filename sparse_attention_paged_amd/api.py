@@ -122,6 +122,41 @@ def indexer_logits_packed(q, w, key_pool, page_table, page: int, N: int, n_keys=
     return out
 
 
+def indexer_logits_candidates(q, w, key_pool, page_table, page: int, cand, n_keys=None,
+                              out=None) -> torch.Tensor:
+    """q [T, Hi, 128] bf16, w [T, Hi] fp32, cand [T, NC] int32 logical key
+    positions (-1 = none), page_table [T, pages] (stride 0 rows allowed) or
+    None -> logits [T, NC] fp32."""
+    _dev(q, w, key_pool, page_table, cand, n_keys, out)
+    T, Hi, D = q.shape
+    NC = cand.shape[1]
+    if out is None:
+        out = torch.empty((T, NC), dtype=torch.float32, device=q.device)
+    rc = lib().sap_indexer_logits_candidates(
+        _p(q), q.stride(0), _p(w), w.stride(0), _p(key_pool), key_pool.stride(0),
+        _p(page_table), page_table.stride(0) if page_table is not None else 0, page,
+        _p(cand), cand.stride(0), _p(n_keys), _p(out), out.stride(0), T, Hi, D, NC, _stream(q))
+    check(rc, "sap_indexer_logits_candidates")
+    return out
+
+
+def indexer_logits_prefill(q, w, key_pool, page_table, page: int, tok_start, max_tokens: int, N: int,
+                           n_keys=None, out=None) -> torch.Tensor:
+    """q [T, Hi, 128] bf16, w [T, Hi] fp32, page_table [S, pages] or None,
+    tok_start [S + 1] int32, n_keys [T] int32 -> logits [T, N] fp32."""
+    _dev(q, w, key_pool, page_table, tok_start, n_keys, out)
+    T, Hi, D = q.shape
+    S = tok_start.numel() - 1
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=q.device)
+    rc = lib().sap_indexer_logits_prefill(
+        _p(q), q.stride(0), _p(w), w.stride(0), _p(key_pool), key_pool.stride(0),
+        _p(page_table), page_table.stride(0) if page_table is not None else 0, page,
+        _p(tok_start), S, max_tokens, _p(n_keys), _p(out), out.stride(0), Hi, D, N, _stream(q))
+    check(rc, "sap_indexer_logits_prefill")
+    return out
+
+
 def topk_workspace_bytes(B: int, N: int, k: int) -> int:
     return int(lib().sap_topk_workspace_bytes(B, N, k))
 

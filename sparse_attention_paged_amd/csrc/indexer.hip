@@ -153,7 +153,325 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerParams p)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Candidate and prefill modes.  Both read key rows straight into registers
+// with a permuted reduction order: in MFMA step s, lane half hh covers
+// head_dim elements 64hh + 8s .. 64hh + 8s + 7 (the sum over head_dim does not
+// depend on the order).  A lane's B operands over the 8 steps are then the
+// code words 8hh .. 8hh+7 of one key row (two 16-byte loads) with scale bytes
+// 2hh and 2hh+1 of word 16, and its A operands the q elements 64hh .. 64hh+63
+// of one head.
+
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// raw words of one lane's half of a key row
+struct KeyHalf {
+    u32x4_a4 lo, hi;
+    uint32_t sc;
+};
+
+__device__ __forceinline__ void load_key_half(const int32_t *row, int hh, KeyHalf &k)
+{
+    const u32x4_a4 *p = reinterpret_cast<const u32x4_a4 *>(row + 8 * hh);
+    k.lo = p[0];
+    k.hi = p[1];
+    k.sc = (uint32_t)row[16];
+}
+
+__device__ __forceinline__ void zero_key_half(KeyHalf &k)
+{
+    k.lo = u32x4_a4{0, 0, 0, 0};
+    k.hi = u32x4_a4{0, 0, 0, 0};
+    k.sc = 0x7F7F7F7Fu;   // scale 1: zero codes decode to +0 on the fast path
+}
+
+// B operands of the 8 steps: word 8hh + s with scale byte 2hh + s/4.  When
+// every lane's two scale bytes lie in 2..252 (the usual case) the hardware
+// scaled conversion is exact and is used directly, else each word takes the
+// general decode.
+__device__ __forceinline__ void decode_key_half(const KeyHalf &k, int hh, uint4 (&b)[8])
+{
+    const uint32_t e0 = (k.sc >> (16 * hh)) & 0xFFu, e1 = (k.sc >> (16 * hh + 8)) & 0xFFu;
+    const bool fast = e0 - 2u <= 250u && e1 - 2u <= 250u;
+    if (__builtin_amdgcn_ballot_w64(!fast) == 0) {
+        const float s0 = __uint_as_float(e0 << 23), s1 = __uint_as_float(e1 << 23);
+        const uint32_t w[8] = {k.lo.x, k.lo.y, k.lo.z, k.lo.w, k.hi.x, k.hi.y, k.hi.z, k.hi.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float sc = i < 4 ? s0 : s1;
+            b[i].x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], sc, 0));
+            b[i].y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], sc, 1));
+            b[i].z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], sc, 2));
+            b[i].w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], sc, 3));
+        }
+        return;
+    }
+    b[0] = fp4x8_to_bf16x8(k.lo.x, e0);
+    b[1] = fp4x8_to_bf16x8(k.lo.y, e0);
+    b[2] = fp4x8_to_bf16x8(k.lo.z, e0);
+    b[3] = fp4x8_to_bf16x8(k.lo.w, e0);
+    b[4] = fp4x8_to_bf16x8(k.hi.x, e1);
+    b[5] = fp4x8_to_bf16x8(k.hi.y, e1);
+    b[6] = fp4x8_to_bf16x8(k.hi.z, e1);
+    b[7] = fp4x8_to_bf16x8(k.hi.w, e1);
+}
+
+// the logit of this lane's key (column l32 of a 32x32 score block): its own
+// 16 heads 8(i/4) + 4hh + i%4 plus the other half's 16
+__device__ __forceinline__ float head_sum(const f32x16 &acc, const float (&wv)[16])
+{
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part = fmaf(wv[i], fmaxf(acc[i], 0.0f), part);
+    const uint32_t u = __float_as_uint(part);
+    const auto x = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(x[0]) + __uint_as_float(x[1]);
+}
+
+// weights of the lane's 16 output heads, from a token's 32 weights
+__device__ __forceinline__ void lane_weights(const float *wr, int Hi, int hh, float (&wv)[16])
+{
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int h0 = 8 * (i >> 2) + (i & 3), h1 = h0 + 4;
+        const float w0 = h0 < Hi ? wr[h0] : 0.0f;
+        const float w1 = h1 < Hi ? wr[h1] : 0.0f;
+        wv[i] = hh ? w1 : w0;
+    }
+}
+
+// Candidate mode: one query token per blockIdx.y, scoring the keys listed in
+// its candidate row.  Each wave takes a run of 64-candidate tiles; the pool
+// rows of up to kCandChunk tiles are resolved first (all candidate loads,
+// then all page-table loads: two memory round trips per chunk), then the
+// tiles stream through registers with the next tile's rows in flight while
+// the current one is scored.
+constexpr int kCandChunk = 8;
+
+__global__ __launch_bounds__(256) void indexer_cand_kernel(IndexerParams p)
+{
+    __shared__ int rowtab[4][kCandChunk * kKeyTile];
+    const int t = blockIdx.y;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int nk = p.n_keys ? p.n_keys[t] : 0x7FFFFFFF;
+
+    uint4 qa[8];
+    {
+        const bool hok = l32 < p.Hi;
+        const uint16_t *qr = p.q + (int64_t)t * p.q_sb + (int64_t)(hok ? l32 : 0) * 128 + 64 * hh;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) qa[s] = hok ? *(const uint4 *)(qr + 8 * s) : make_uint4(0, 0, 0, 0);
+    }
+    float wv[16];
+    lane_weights(p.w + (int64_t)t * p.w_sb, p.Hi, hh, wv);
+
+    const int n_tiles = (p.N + kKeyTile - 1) / kKeyTile;
+    const int tile0 = (blockIdx.x * 4 + wave) * p.tiles_per_wave;
+    const int tile_end = min(tile0 + p.tiles_per_wave, n_tiles);
+    const int32_t *cr = p.cand + (int64_t)t * p.cand_sb;
+    float *out = p.logits + (int64_t)t * p.logits_sb;
+    int *rt = rowtab[wave];
+
+    for (int c0 = tile0; c0 < tile_end; c0 += kCandChunk) {
+        const int nc = min(kCandChunk, tile_end - c0);
+        // pool row of candidate (c0 + j) * 64 + lane, -1 = none
+        int cv[kCandChunk];
+#pragma unroll
+        for (int j = 0; j < kCandChunk; ++j) {
+            const int c = (c0 + j) * kKeyTile + lane;
+            cv[j] = (j < nc && c < p.N) ? cr[c] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < kCandChunk; ++j) {
+            const int n = cv[j];
+            int r = -1;
+            if (n >= 0 && n < nk)
+                r = p.pt ? p.pt[(int64_t)t * p.pt_sb + n / p.page] * p.page + n % p.page : n;
+            rt[j * kKeyTile + lane] = r;
+        }
+        wave_lds_sync();
+        KeyHalf kh[2];
+        auto load = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const int r = rt[j * kKeyTile + 32 * nt + l32];
+                if (r >= 0) load_key_half(p.pool + (int64_t)r * p.row_words, hh, kh[nt]);
+                else zero_key_half(kh[nt]);
+            }
+        };
+        load(0);
+        for (int j = 0; j < nc; ++j) {
+            uint4 kb[2][8];
+            decode_key_half(kh[0], hh, kb[0]);
+            decode_key_half(kh[1], hh, kb[1]);
+            const int r0 = rt[j * kKeyTile + l32], r1 = rt[j * kKeyTile + 32 + l32];
+            if (j + 1 < nc) load(j + 1);
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                f32x16 acc = {};
+#pragma unroll
+                for (int s = 0; s < 8; ++s) acc = mfma32x32x16(qa[s], kb[nt][s], acc);
+                const float logit = head_sum(acc, wv);
+                const int c = (c0 + j) * kKeyTile + 32 * nt + l32;
+                if (hh == 0 && c < p.N) out[c] = (nt ? r1 : r0) >= 0 ? logit : -INFINITY;
+            }
+        }
+        wave_lds_sync();   // the row table is rewritten by the next chunk
+    }
+}
+
+// Prefill mode: a workgroup takes kPfTok consecutive query tokens of one
+// sequence and a chunk of kc keys.  The tokens' q (64 KiB, 16-byte chunks
+// swizzled by head so the A-operand reads are conflict-free) and weights are
+// staged in LDS once; each wave decodes a 64-key sub-tile into registers and
+// scores it for every token of the workgroup (16 MFMAs per token), so a key
+// is decoded once per 8 tokens.  Keys at or beyond a token's visible count
+// are -inf (the causal mask); sub-tiles beyond every token's count are only
+// filled with -inf.
+constexpr int kPfTok = 8;
+constexpr int kPfPass = 4 * kKeyTile;
+
+__global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(IndexerPrefillParams p)
+{
+    __shared__ __attribute__((aligned(16))) uint4 qs[kPfTok][32][16];
+    __shared__ __attribute__((aligned(16))) float ws[kPfTok][32];
+    __shared__ int nks[kPfTok];
+    const int sq = blockIdx.z;
+    const int ta = p.tok_start[sq], tb = p.tok_start[sq + 1];
+    // token tiles with the most visible keys are dispatched first
+    const int t0 = ta + ((int)gridDim.y - 1 - (int)blockIdx.y) * kPfTok;
+    if (t0 >= tb) return;
+    const int ntok = min(kPfTok, tb - t0);
+    const int k0 = blockIdx.x * p.kc, k1 = min(p.N, k0 + p.kc);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int l32 = lane & 31, hh = lane >> 5;
+
+    for (int i = tid; i < kPfTok * 32 * 16; i += 256) {
+        const int j = i >> 9, h = (i >> 4) & 31, c = i & 15;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (j < ntok && h < p.Hi) v = *(const uint4 *)(p.q + (int64_t)(t0 + j) * p.q_st + h * 128 + 8 * c);
+        qs[j][h][c ^ (h & 15)] = v;
+    }
+    {
+        const int j = tid >> 5, h = tid & 31;
+        ws[j][h] = (j < ntok && h < p.Hi) ? p.w[(int64_t)(t0 + j) * p.w_st + h] : 0.0f;
+    }
+    if (tid < kPfTok) {
+        int v = 0;
+        if (tid < ntok) v = min(max(p.n_keys ? p.n_keys[t0 + tid] : p.N, 0), p.N);
+        nks[tid] = v;
+    }
+    __syncthreads();
+    int nk[kPfTok];
+    int kmax = 0;
+#pragma unroll
+    for (int j = 0; j < kPfTok; ++j) {
+        nk[j] = __builtin_amdgcn_readfirstlane(nks[j]);
+        kmax = max(kmax, nk[j]);
+    }
+    const int32_t *ptr = p.pt ? p.pt + (int64_t)sq * p.pt_ss : nullptr;
+    const bool page_tiles = ptr == nullptr || p.page % kKeyTile == 0;
+
+    for (int pb = k0; pb < k1; pb += kPfPass) {
+        const int kb0 = pb + kKeyTile * wave;
+        if (kb0 >= k1) break;
+        const int kend = min(kb0 + kKeyTile, k1);
+        if (kb0 >= kmax) {
+            // no token of the tile sees these keys
+            for (int j = 0; j < ntok; ++j)
+                if (kb0 + lane < kend) p.logits[(int64_t)(t0 + j) * p.logits_st + kb0 + lane] = -INFINITY;
+            continue;
+        }
+        // raw rows of keys kb0 + 32 nt + l32 (zero beyond kmax)
+        KeyHalf kh[2];
+        int64_t row0 = (int64_t)sq * p.N + kb0;
+        if (ptr && page_tiles) {
+            const int pg = kb0 / p.page;
+            row0 = (int64_t)ptr[pg] * p.page + (kb0 - pg * p.page);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int n = kb0 + 32 * nt + l32;
+            if (n < kmax) {
+                int64_t row = row0 + 32 * nt + l32;
+                if (!page_tiles) row = (int64_t)ptr[n / p.page] * p.page + n % p.page;
+                load_key_half(p.pool + row * p.row_words, hh, kh[nt]);
+            } else {
+                zero_key_half(kh[nt]);
+            }
+        }
+        uint4 kb[2][8];
+        decode_key_half(kh[0], hh, kb[0]);
+        decode_key_half(kh[1], hh, kb[1]);
+
+#pragma unroll
+        for (int j = 0; j < kPfTok; ++j) {
+            if (j >= ntok) break;
+            float *orow = p.logits + (int64_t)(t0 + j) * p.logits_st;
+            if (nk[j] <= kb0) {
+                if (kb0 + lane < kend) orow[kb0 + lane] = -INFINITY;
+                continue;
+            }
+            f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const uint4 a = qs[j][l32][(8 * hh + s) ^ (l32 & 15)];
+                acc0 = mfma32x32x16(a, kb[0][s], acc0);
+                acc1 = mfma32x32x16(a, kb[1][s], acc1);
+            }
+            float wv[16];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float4 w4 = *(const float4 *)&ws[j][8 * m + 4 * hh];
+                wv[4 * m] = w4.x;
+                wv[4 * m + 1] = w4.y;
+                wv[4 * m + 2] = w4.z;
+                wv[4 * m + 3] = w4.w;
+            }
+            const float g0 = head_sum(acc0, wv), g1 = head_sum(acc1, wv);
+            const int n0 = kb0 + l32, n1 = kb0 + 32 + l32;
+            if (hh == 0) {
+                if (n0 < kend) orow[n0] = n0 < nk[j] ? g0 : -INFINITY;
+                if (n1 < kend) orow[n1] = n1 < nk[j] ? g1 : -INFINITY;
+            }
+        }
+    }
+}
+
 }  // namespace
+
+int indexer_prefill_chunk(int S, int max_tokens, int N)
+{
+    // about 2048 workgroups (8 per CU): split the keys into chunks of whole
+    // 256-key passes
+    const int64_t tiles = (int64_t)S * ((max_tokens + kPfTok - 1) / kPfTok);
+    const int64_t passes = ((int64_t)N + kPfPass - 1) / kPfPass;
+    if (tiles <= 0 || passes <= 0) return kPfPass;
+    int64_t chunks = (2048 + tiles - 1) / tiles;
+    if (chunks > passes) chunks = passes;
+    if (chunks < 1) chunks = 1;
+    return (int)((passes + chunks - 1) / chunks) * kPfPass;
+}
+
+hipError_t launch_indexer_prefill(const IndexerPrefillParams &p, hipStream_t s)
+{
+    const unsigned gx = (unsigned)((p.N + p.kc - 1) / p.kc);
+    const unsigned gy = (unsigned)((p.max_tokens + kPfTok - 1) / kPfTok);
+    if (gx == 0 || gy == 0 || p.S == 0) return hipSuccess;
+    hipLaunchKernelGGL(indexer_prefill_kernel, dim3(gx, gy, (unsigned)p.S), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_indexer_candidates(const IndexerParams &p, hipStream_t s)
+{
+    const int n_tiles = (p.N + kKeyTile - 1) / kKeyTile;
+    const int waves = (n_tiles + p.tiles_per_wave - 1) / p.tiles_per_wave;
+    const unsigned gx = (unsigned)((waves + 3) / 4);
+    if (gx == 0 || p.B == 0) return hipSuccess;
+    hipLaunchKernelGGL(indexer_cand_kernel, dim3(gx, (unsigned)p.B), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_indexer(const IndexerParams &p, hipStream_t s)
 {

@@ -49,8 +49,31 @@ struct IndexerParams {
     int64_t logits_sb;
     int B, Hi, N;
     int tiles_per_wave;
+    const int32_t *cand;             // candidate mode: [B, N] logical key positions (-1 = none)
+    int64_t cand_sb;
 };
 hipError_t launch_indexer(const IndexerParams &p, hipStream_t s);
+hipError_t launch_indexer_candidates(const IndexerParams &p, hipStream_t s);
+
+struct IndexerPrefillParams {
+    const uint16_t *q;               // bf16 [T, Hi, 128]
+    int64_t q_st;
+    const float *w;                  // [T, Hi]
+    int64_t w_st;
+    const int32_t *pool;
+    int64_t row_words;
+    const int32_t *pt;               // [S, pages] (may be null: rows s * N + n)
+    int64_t pt_ss;
+    int page;
+    const int32_t *tok_start;        // [S + 1]
+    const int32_t *n_keys;           // [T] visible keys per token (may be null: N)
+    float *logits;                   // [T, N]
+    int64_t logits_st;
+    int S, max_tokens, Hi, N;
+    int kc;                          // keys per workgroup (multiple of 256)
+};
+int indexer_prefill_chunk(int S, int max_tokens, int N);
+hipError_t launch_indexer_prefill(const IndexerPrefillParams &p, hipStream_t s);
 
 struct TopkParams {
     const float *x;

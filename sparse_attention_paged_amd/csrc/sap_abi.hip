@@ -236,6 +236,91 @@ int sap_indexer_logits_packed(const void *q, int64_t q_stride_b,
     return launched(sap::launch_indexer(p, (hipStream_t)stream));
 }
 
+int sap_indexer_logits_candidates(const void *q, int64_t q_stride_t,
+                                  const float *w, int64_t w_stride_t,
+                                  const int32_t *key_pool, int64_t key_row_words,
+                                  const int32_t *page_table, int64_t pt_stride_t, int page,
+                                  const int32_t *cand, int64_t cand_stride_t,
+                                  const int32_t *n_keys,
+                                  float *logits, int64_t logits_stride_t,
+                                  int T, int Hi, int D, int NC, sap_stream_t stream)
+{
+    if (T < 0 || NC < 0 || Hi < 1 || Hi > 32 || D != 128 || T > 65535) return SAP_ERR_SHAPE;
+    if (key_row_words < 17) return SAP_ERR_SHAPE;
+    if (page_table && page < 1) return SAP_ERR_SHAPE;
+    if (T == 0 || NC == 0) return SAP_OK;
+    if (!q || !w || !key_pool || !cand || !logits) return SAP_ERR_NULL;
+    if (q_stride_t < 0 || w_stride_t < 0 || pt_stride_t < 0 || cand_stride_t < 0 ||
+        logits_stride_t < NC)
+        return SAP_ERR_SHAPE;
+    if (!aligned(key_pool, 4)) return SAP_ERR_ALIGN;
+    if (!aligned(q, 16) || (q_stride_t * 2) % 16) return SAP_ERR_ALIGN;
+    if (!aligned(w, 4) || !aligned(cand, 4) || !aligned(logits, 4)) return SAP_ERR_ALIGN;
+    sap::IndexerParams p{};
+    p.q = (const uint16_t *)q;
+    p.q_sb = q_stride_t;
+    p.w = w;
+    p.w_sb = w_stride_t;
+    p.pool = key_pool;
+    p.row_words = key_row_words;
+    p.pt = page_table;
+    p.pt_sb = pt_stride_t;
+    p.page = page_table ? page : 1;
+    p.n_keys = n_keys;
+    p.logits = logits;
+    p.logits_sb = logits_stride_t;
+    p.B = T;
+    p.Hi = Hi;
+    p.N = NC;
+    p.cand = cand;
+    p.cand_sb = cand_stride_t;
+    const int64_t tiles = ((int64_t)NC + 63) / 64 * T;
+    p.tiles_per_wave = (int)((tiles + 2047) / 2048);
+    if (p.tiles_per_wave < 1) p.tiles_per_wave = 1;
+    return launched(sap::launch_indexer_candidates(p, (hipStream_t)stream));
+}
+
+int sap_indexer_logits_prefill(const void *q, int64_t q_stride_t,
+                               const float *w, int64_t w_stride_t,
+                               const int32_t *key_pool, int64_t key_row_words,
+                               const int32_t *page_table, int64_t pt_stride_s, int page,
+                               const int32_t *tok_start, int S, int max_tokens,
+                               const int32_t *n_keys,
+                               float *logits, int64_t logits_stride_t,
+                               int Hi, int D, int N, sap_stream_t stream)
+{
+    if (S < 0 || max_tokens < 0 || N < 0 || Hi < 1 || Hi > 32 || D != 128 || S > 65535) return SAP_ERR_SHAPE;
+    if (key_row_words < 17) return SAP_ERR_SHAPE;
+    if (page_table && page < 1) return SAP_ERR_SHAPE;
+    if (S == 0 || max_tokens == 0 || N == 0) return SAP_OK;
+    if ((int64_t)max_tokens > (int64_t)65535 * 8) return SAP_ERR_SHAPE;
+    if (!q || !w || !key_pool || !tok_start || !logits) return SAP_ERR_NULL;
+    if (q_stride_t < 0 || w_stride_t < 0 || pt_stride_s < 0 || logits_stride_t < N) return SAP_ERR_SHAPE;
+    if (!aligned(key_pool, 4)) return SAP_ERR_ALIGN;
+    if (!aligned(q, 16) || (q_stride_t * 2) % 16) return SAP_ERR_ALIGN;
+    if (!aligned(w, 4) || !aligned(logits, 4)) return SAP_ERR_ALIGN;
+    sap::IndexerPrefillParams p{};
+    p.q = (const uint16_t *)q;
+    p.q_st = q_stride_t;
+    p.w = w;
+    p.w_st = w_stride_t;
+    p.pool = key_pool;
+    p.row_words = key_row_words;
+    p.pt = page_table;
+    p.pt_ss = pt_stride_s;
+    p.page = page_table ? page : 1;
+    p.tok_start = tok_start;
+    p.n_keys = n_keys;
+    p.logits = logits;
+    p.logits_st = logits_stride_t;
+    p.S = S;
+    p.max_tokens = max_tokens;
+    p.Hi = Hi;
+    p.N = N;
+    p.kc = sap::indexer_prefill_chunk(S, max_tokens, N);
+    return launched(sap::launch_indexer_prefill(p, (hipStream_t)stream));
+}
+
 size_t sap_topk_workspace_bytes(int B, int N, int k)
 {
     if (B <= 0 || N <= 0 || k < 1 || k > 4096) return 0;

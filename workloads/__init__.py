@@ -331,7 +331,7 @@ class IndexerPrefillCase:
 
 def indexer_prefill_case(lengths=(8192,), starts=(0,), ratio: int = 2, Hi: int = 32, Dk: int = 128,
                          seed: int = SEED_BASE + 40, w_signed: bool = True, N: Optional[int] = None,
-                         exp_lo: int = 120, exp_hi: int = 134) -> IndexerPrefillCase:
+                         exp_lo: int = 120, exp_hi: int = 134, page: int = PAGE) -> IndexerPrefillCase:
     """Sequence s holds lengths[s] query tokens at positions starts[s] ..;
     its keys are the compressed entries at ratio r (r = 1: one key per token)
     and token p sees ceil((p+1)/r) of them.  N defaults to the largest
@@ -348,15 +348,15 @@ def indexer_prefill_case(lengths=(8192,), starts=(0,), ratio: int = 2, Hi: int =
     w = torch.rand((T, Hi), generator=g).to(torch.float32)
     if w_signed:
         w = w * 2.0 - 1.0
-    pages = max(1, math.ceil(N / PAGE))
+    pages = max(1, math.ceil(N / page))
     pt = page_table(S, pages, g)
-    pool = fp4_key_rows(S * pages * PAGE, g, exp_lo, exp_hi)
+    pool = fp4_key_rows(S * pages * page, g, exp_lo, exp_hi)
     ts = torch.zeros(S + 1, dtype=torch.int32)
     if S:
         ts[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int32), 0)
     name = "indexer_prefill_" + "_".join(f"n{ln}s{st}" for ln, st in zip(lengths, starts)) + f"_r{ratio}"
     return IndexerPrefillCase(name=name, q=q, w=w, key_pool=pool, page_table=pt, tok_start=ts, pos=pos,
-                              n_keys=nk, N=N, ratio=ratio)
+                              n_keys=nk, N=N, ratio=ratio, page=page)
 
 
 @dataclass
