@@ -242,6 +242,36 @@ def indexer_secondary(B, iters):
             "topk512_us": round(ms_topk * 1e3, 2), "roofline": roofline("hbm", gb, HBM_PEAK_GBS, "GB/s")}
 
 
+def indexer_prefill_secondary(length, start, ratio, iters):
+    case = W.indexer_prefill_case(lengths=(length,), starts=(start,), ratio=ratio,
+                                  seed=W.SEED_BASE + 650 + length + ratio)
+    d = torch.device("cuda")
+    q, w, pool, pt, ts, nk = (x.to(d) for x in (case.q, case.w, case.key_pool, case.page_table, case.tok_start,
+                                                  case.n_keys))
+    out = torch.empty((case.T, case.N), dtype=torch.float32, device=d)
+    ms = time_graph(lambda: sap.indexer_logits_prefill(q, w, pool, pt, case.page, ts, case.max_tokens, case.N,
+                                                       n_keys=nk, out=out), iters, 1, 2)
+    # useful flops: each visible (token, key) pair costs 32 heads x 128 x 2
+    tf = float(case.n_keys.to(torch.float64).sum()) * 32 * 128 * 2 / (ms * 1e-3) / 1e12
+    return {"workload": f"indexer_prefill_n{length}_start{start}_r{ratio}", "us": round(ms * 1e3, 2),
+            "tflops": round(tf, 2), "roofline": roofline("mfma", tf, BF16_PEAK_TFLOPS, "TFLOP/s")}
+
+
+def indexer_cand_secondary(T, shared, iters):
+    case = W.indexer_cand_case(T=T, n_ctx=131072, NC=16384, shared_seq=shared, seed=W.SEED_BASE + 620 + T)
+    d = torch.device("cuda")
+    q, w, pool, pt, cand, nk = (x.to(d) for x in (case.q, case.w, case.key_pool, case.page_table, case.cand,
+                                                    case.n_keys))
+    out = torch.empty((case.T, case.NC), dtype=torch.float32, device=d)
+    ms = time_graph(lambda: sap.indexer_logits_candidates(q, w, pool, pt, case.page, cand, n_keys=nk, out=out),
+                    iters // GRAPH_CALLS, 1, GRAPH_CALLS)
+    # per candidate: the 68-byte key row, its index and its logit
+    gb = T * case.NC * (68 + 4 + 4) / (ms * 1e-3) / 1e9
+    kind = "prefill_n128" if shared else f"decode_b{T}"
+    return {"workload": f"indexer_cand_{kind}_ctx131072_nc16384", "us": round(ms * 1e3, 2),
+            "roofline": roofline("hbm", gb, HBM_PEAK_GBS, "GB/s")}
+
+
 def cpu_baseline(st: DecodeStep, budget_s: float):
     """The oracle on the same decode step, on the host cores."""
     import oracle
@@ -322,6 +352,12 @@ def main():
         for B in (1, 4):
             log(f"secondary: indexer B{B}")
             sec.append(indexer_secondary(B, 100))
+        for length, start, ratio in ((2048, 129024, 2), (8192, 0, 2)):
+            log(f"secondary: indexer prefill n{length} start{start} r{ratio}")
+            sec.append(indexer_prefill_secondary(length, start, ratio, 5))
+        for T, shared in ((1, False), (128, True)):
+            log(f"secondary: indexer candidates T{T}")
+            sec.append(indexer_cand_secondary(T, shared, 100))
         res["secondary"] = sec
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the same decode step")

@@ -326,7 +326,8 @@ __global__ __launch_bounds__(256) void indexer_cand_kernel(IndexerParams p)
 // swizzled by head so the A-operand reads are conflict-free) and weights are
 // staged in LDS once; each wave decodes a 64-key sub-tile into registers and
 // scores it for every token of the workgroup (16 MFMAs per token), so a key
-// is decoded once per 8 tokens.  Keys at or beyond a token's visible count
+// is decoded once per 8 tokens; the next sub-tile's rows load meanwhile and
+// each token's epilogue overlaps the next token's MFMAs.  Keys at or beyond a token's visible count
 // are -inf (the causal mask); sub-tiles beyond every token's count are only
 // filled with -inf.
 constexpr int kPfTok = 8;
@@ -373,18 +374,8 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(IndexerPrefillP
     const int32_t *ptr = p.pt ? p.pt + (int64_t)sq * p.pt_ss : nullptr;
     const bool page_tiles = ptr == nullptr || p.page % kKeyTile == 0;
 
-    for (int pb = k0; pb < k1; pb += kPfPass) {
-        const int kb0 = pb + kKeyTile * wave;
-        if (kb0 >= k1) break;
-        const int kend = min(kb0 + kKeyTile, k1);
-        if (kb0 >= kmax) {
-            // no token of the tile sees these keys
-            for (int j = 0; j < ntok; ++j)
-                if (kb0 + lane < kend) p.logits[(int64_t)(t0 + j) * p.logits_st + kb0 + lane] = -INFINITY;
-            continue;
-        }
-        // raw rows of keys kb0 + 32 nt + l32 (zero beyond kmax)
-        KeyHalf kh[2];
+    // raw rows of keys kb0 + 32 nt + l32 (zero beyond kmax)
+    auto load_keys = [&](int kb0, KeyHalf (&kh)[2]) __attribute__((always_inline)) {
         int64_t row0 = (int64_t)sq * p.N + kb0;
         if (ptr && page_tiles) {
             const int pg = kb0 / p.page;
@@ -401,25 +392,45 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(IndexerPrefillP
                 zero_key_half(kh[nt]);
             }
         }
+    };
+    // this wave's sub-tile of the next pass is in flight while the current
+    // one is scored
+    KeyHalf kh[2];
+    if (k0 + kKeyTile * wave < min(k1, kmax)) load_keys(k0 + kKeyTile * wave, kh);
+
+    for (int pb = k0; pb < k1; pb += kPfPass) {
+        const int kb0 = pb + kKeyTile * wave;
+        if (kb0 >= k1) break;
+        const int kend = min(kb0 + kKeyTile, k1);
+        if (kb0 >= kmax) {
+            // no token of the tile sees these keys
+            for (int j = 0; j < ntok; ++j)
+                if (kb0 + lane < kend) p.logits[(int64_t)(t0 + j) * p.logits_st + kb0 + lane] = -INFINITY;
+            continue;
+        }
         uint4 kb[2][8];
         decode_key_half(kh[0], hh, kb[0]);
         decode_key_half(kh[1], hh, kb[1]);
+        if (kb0 + kPfPass < min(k1, kmax)) load_keys(kb0 + kPfPass, kh);
 
-#pragma unroll
-        for (int j = 0; j < kPfTok; ++j) {
-            if (j >= ntok) break;
-            float *orow = p.logits + (int64_t)(t0 + j) * p.logits_st;
-            if (nk[j] <= kb0) {
-                if (kb0 + lane < kend) orow[kb0 + lane] = -INFINITY;
-                continue;
-            }
-            f32x16 acc0 = {}, acc1 = {};
+        // every token slot of the tile is scored (q and w are zero for absent
+        // tokens, whose stores are skipped); the MFMAs of token j+1 go out
+        // ahead of the epilogue of token j
+        f32x16 acc[2][2];
+        auto mm = [&](int j, f32x16 (&a2)[2]) __attribute__((always_inline)) {
+            a2[0] = f32x16{};
+            a2[1] = f32x16{};
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const uint4 a = qs[j][l32][(8 * hh + s) ^ (l32 & 15)];
-                acc0 = mfma32x32x16(a, kb[0][s], acc0);
-                acc1 = mfma32x32x16(a, kb[1][s], acc1);
+                a2[0] = mfma32x32x16(a, kb[0][s], a2[0]);
+                a2[1] = mfma32x32x16(a, kb[1][s], a2[1]);
             }
+        };
+        mm(0, acc[0]);
+#pragma unroll
+        for (int j = 0; j < kPfTok; ++j) {
+            if (j + 1 < kPfTok) mm(j + 1, acc[(j + 1) & 1]);
             float wv[16];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
@@ -429,9 +440,10 @@ __global__ __launch_bounds__(256, 2) void indexer_prefill_kernel(IndexerPrefillP
                 wv[4 * m + 2] = w4.z;
                 wv[4 * m + 3] = w4.w;
             }
-            const float g0 = head_sum(acc0, wv), g1 = head_sum(acc1, wv);
+            const float g0 = head_sum(acc[j & 1][0], wv), g1 = head_sum(acc[j & 1][1], wv);
             const int n0 = kb0 + l32, n1 = kb0 + 32 + l32;
-            if (hh == 0) {
+            float *orow = p.logits + (int64_t)(t0 + j) * p.logits_st;
+            if (hh == 0 && j < ntok) {
                 if (n0 < kend) orow[n0] = n0 < nk[j] ? g0 : -INFINITY;
                 if (n1 < kend) orow[n1] = n1 < nk[j] ? g1 : -INFINITY;
             }
