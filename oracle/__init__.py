@@ -58,6 +58,8 @@ def lib():
         L.orc_indexer_candidates.argtypes = [I, I, I, P, I64, P, I64, P, I64, P, I64, I, P, I64, P, I,
                                              P, I64]
         L.orc_indexer_candidates.restype = I
+        L.orc_gated_pool.argtypes = [I, I, I, P, P, P]
+        L.orc_gated_pool.restype = I
         L.orc_topk.argtypes = [I, I, P, I64, P, I, P, I64]
         L.orc_topk.restype = I
         L.orc_num_threads.argtypes = []; L.orc_num_threads.restype = I
@@ -235,6 +237,19 @@ def indexer_candidates(q, w, key_pool, page_table, page, cand, n_keys) -> torch.
                                       _p(nk), NC, _p(out), out.stride(0))
     if rc != 0:
         raise ValueError(f"orc_indexer_candidates rejected its arguments ({rc})")
+    return out
+
+
+def gated_pool(x, gate) -> torch.Tensor:
+    """float64 [B, D]: softmax over R of the gates weighting the R rows
+    (x, gate [B, R, D] of any float dtype; values are taken exactly)."""
+    xd = _cpu(x, torch.float64)
+    gd = _cpu(gate, torch.float64)
+    B, R, D = xd.shape
+    out = torch.empty((B, D), dtype=torch.float64)
+    rc = lib().orc_gated_pool(B, R, D, _p(xd), _p(gd), _p(out))
+    if rc != 0:
+        raise ValueError(f"orc_gated_pool rejected its arguments ({rc})")
     return out
 
 

@@ -407,6 +407,51 @@ int orc_indexer_candidates(int T, int Hi, int Dk, const uint16_t *q, int64_t q_s
 }
 
 /* ------------------------------------------------------------------ */
+/* Gated pool (the compressor step that produces compressed rows)      */
+/* ------------------------------------------------------------------ */
+
+/*
+ * "perf(kernel): keep 16-byte kv loads in dsv4 sparse attention and unroll
+ * gated pool" names gated_pool (Call paths: the compressor's decode step)
+ * and says it runs a max loop and a second loop over R; it prints no
+ * formula.  Reading taken: each of the D channels of R raw rows is pooled by
+ * a softmax over R of its gate scores,
+ *   out[b, d] = sum_r exp(g[b,r,d] - m) x[b,r,d] / sum_r exp(g[b,r,d] - m),
+ *   m = max_r g[b,r,d]   (the max loop),
+ * with -inf gates contributing nothing and an all -inf column giving 0.
+ * x, g: [B, R, D] contiguous doubles (exact copies of the bf16 / fp32
+ * inputs); out: [B, D].
+ */
+int orc_gated_pool(int B, int R, int D, const double *x, const double *g, double *out)
+{
+    if (B < 0 || R < 1 || D < 0)
+        return -3;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; ++b) {
+        for (int d = 0; d < D; ++d) {
+            double m = -INFINITY, s = 0.0, a = 0.0;
+            for (int r = 0; r < R; ++r) {
+                double v = g[((int64_t)b * R + r) * D + d];
+                if (v > m)
+                    m = v;
+            }
+            if (m == -INFINITY) {
+                out[(int64_t)b * D + d] = 0.0;
+                continue;
+            }
+            for (int r = 0; r < R; ++r) {
+                int64_t i = ((int64_t)b * R + r) * D + d;
+                double e = exp(g[i] - m);
+                s += e;
+                a += e * x[i];
+            }
+            out[(int64_t)b * D + d] = a / s;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Exact top-k selection                                                */
 /* ------------------------------------------------------------------ */
 

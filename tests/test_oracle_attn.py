@@ -204,3 +204,54 @@ def test_e4m3_pools_match_torch_dequant_dense():
         kk = torch.stack(keys)
         ref = torch.softmax(case.q[t].double() @ kk.T * case.sm_scale, -1) @ kk
         np.testing.assert_allclose(out[t].numpy(), ref.numpy(), rtol=1e-10, atol=1e-9)
+
+
+# ------------------------------------------------------------- gated pool
+
+def test_gated_pool_softmax_reference():
+    """Against torch's softmax over R (an independent route), bf16 x and
+    fp32 gates, odd R and D."""
+    for B, R, D in ((2, 7, 37), (1, 129, 64), (3, 1, 10)):
+        case = W.gated_pool_case(B=B, R=R, D=D, seed=W.SEED_BASE + 900 + R)
+        out = oracle.gated_pool(case.x, case.gate)
+        p = torch.softmax(case.gate.to(torch.float64), dim=1)
+        ref = (p * case.x.to(torch.float64)).sum(1)
+        np.testing.assert_allclose(out.numpy(), ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_gated_pool_closed_forms():
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn(2, 5, 9, generator=g, dtype=torch.float64)
+    # R = 1: the row itself
+    assert torch.equal(oracle.gated_pool(x[:, :1], torch.randn(2, 1, 9, generator=g, dtype=torch.float64)), x[:, 0])
+    # equal gates: the mean over R
+    gate = torch.full((2, 5, 9), 0.37, dtype=torch.float64)
+    np.testing.assert_allclose(oracle.gated_pool(x, gate).numpy(), x.mean(1).numpy(), rtol=1e-14, atol=1e-15)
+    # one gate far above the rest: exactly that row
+    gate = torch.zeros(2, 5, 9, dtype=torch.float64)
+    gate[:, 3] = 2000.0
+    assert torch.equal(oracle.gated_pool(x, gate), x[:, 3])
+    # -inf gates drop their rows; an all -inf column pools to 0
+    gate = torch.randn(2, 5, 9, generator=g, dtype=torch.float64)
+    gm = gate.clone()
+    gm[:, 1] = -math.inf
+    keep = [0, 2, 3, 4]
+    np.testing.assert_allclose(oracle.gated_pool(x, gm).numpy(), oracle.gated_pool(x[:, keep], gate[:, keep]).numpy(),
+                               rtol=1e-14, atol=1e-15)
+    gm[:, :, 4] = -math.inf
+    assert (oracle.gated_pool(x, gm)[:, 4] == 0).all()
+
+
+def test_gated_pool_invariances():
+    """A per-column shift of the gates and a permutation of the R rows leave
+    the pooled row unchanged; the result lies within each column's range."""
+    case = W.gated_pool_case(B=2, R=16, D=33, seed=W.SEED_BASE + 910)
+    out = oracle.gated_pool(case.x, case.gate)
+    shift = torch.randn(2, 1, 33, generator=torch.Generator().manual_seed(3), dtype=torch.float64) * 50
+    np.testing.assert_allclose(oracle.gated_pool(case.x, case.gate.to(torch.float64) + shift).numpy(), out.numpy(),
+                               rtol=1e-11, atol=1e-12)
+    perm = torch.randperm(16, generator=torch.Generator().manual_seed(4))
+    np.testing.assert_allclose(oracle.gated_pool(case.x[:, perm], case.gate[:, perm]).numpy(), out.numpy(),
+                               rtol=1e-13, atol=1e-14)
+    xd = case.x.to(torch.float64)
+    assert (out <= xd.max(1).values + 1e-12).all() and (out >= xd.min(1).values - 1e-12).all()

@@ -421,3 +421,40 @@ def indexer_cand_case(T: int = 1, n_ctx: int = 131072, NC: int = 16384, shared_s
     pt_tok = pt.expand(T, pages) if shared_seq else pt
     name = f"indexer_cand_t{T}_ctx{n_ctx}_nc{NC}" + ("_shared" if shared_seq else "")
     return IndexerCandCase(name=name, q=q, w=w, key_pool=pool, page_table=pt_tok, cand=cand, n_keys=nk)
+
+
+@dataclass
+class GatedPoolCase:
+    """x [B, R, D] (raw rows to pool) and gate [B, R, D] (per-channel gate
+    scores); either may be a strided view of a larger buffer."""
+    name: str
+    x: torch.Tensor
+    gate: torch.Tensor
+
+    @property
+    def B(self):
+        return int(self.x.shape[0])
+
+    @property
+    def R(self):
+        return int(self.x.shape[1])
+
+    @property
+    def D(self):
+        return int(self.x.shape[2])
+
+
+def gated_pool_case(B: int = 1, R: int = 128, D: int = 512, x_dtype=torch.bfloat16, gate_dtype=torch.float32,
+                    seed: int = SEED_BASE + 70, gate_scale: float = 2.0, strided: bool = False) -> GatedPoolCase:
+    """x ~ N(0, 1), gate ~ N(0, gate_scale^2), rounded to their dtypes.
+    strided: x and gate are views with padded row and batch strides."""
+    g = make_generator(seed)
+    if strided:
+        xb = torch.randn((B, R + 1, D + 24), generator=g).to(x_dtype)
+        gb = (torch.randn((B, R + 2, D + 40), generator=g) * gate_scale).to(gate_dtype)
+        x, gate = xb[:, 1:, 8:8 + D], gb[:, :R, 16:16 + D]
+    else:
+        x = torch.randn((B, R, D), generator=g).to(x_dtype)
+        gate = (torch.randn((B, R, D), generator=g) * gate_scale).to(gate_dtype)
+    name = f"gated_pool_b{B}_r{R}_d{D}" + ("_strided" if strided else "")
+    return GatedPoolCase(name=name, x=x, gate=gate)
