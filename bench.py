@@ -272,6 +272,17 @@ def indexer_cand_secondary(T, shared, iters):
             "roofline": roofline("hbm", gb, HBM_PEAK_GBS, "GB/s")}
 
 
+def gated_pool_secondary(B, R, D, iters):
+    case = W.gated_pool_case(B=B, R=R, D=D, seed=W.SEED_BASE + 700 + B + R + D)
+    x, g = case.x.cuda(), case.gate.cuda()
+    out = torch.empty((B, D), dtype=torch.float32, device="cuda")
+    ms = time_graph(lambda: sap.gated_pool(x, g, out=out), iters // GRAPH_CALLS, 1, GRAPH_CALLS)
+    # bf16 rows, fp32 gates in; fp32 pooled rows out
+    alg = B * R * D * (2 + 4) + B * D * 4
+    return {"workload": f"gated_pool_b{B}_r{R}_d{D}", "us": round(ms * 1e3, 2),
+            "roofline": roofline("hbm", alg / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")}
+
+
 def cpu_baseline(st: DecodeStep, budget_s: float):
     """The oracle on the same decode step, on the host cores."""
     import oracle
@@ -358,6 +369,9 @@ def main():
         for T, shared in ((1, False), (128, True)):
             log(f"secondary: indexer candidates T{T}")
             sec.append(indexer_cand_secondary(T, shared, 100))
+        for B, R in ((1, 128), (8, 128), (8, 8)):
+            log(f"secondary: gated pool B{B} R{R} D512")
+            sec.append(gated_pool_secondary(B, R, 512, 100))
         res["secondary"] = sec
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the same decode step")

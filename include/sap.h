@@ -227,6 +227,28 @@ int sap_indexer_logits_prefill(const void *q, int64_t q_stride_t,
                                int Hi, int D, int N, sap_stream_t stream);
 
 /* -------------------------------------------------------------------------
+ * Gated pool: the compressor step that turns R raw rows into one compressed
+ * row ("perf(kernel): keep 16-byte kv loads in dsv4 sparse attention and
+ * unroll gated pool", Call paths: Compressor.decode_step -> gated_pool;
+ * Changes: a max loop and a second loop over R; Kernel time: B 1 / 8,
+ * R 8 / 128, D 128 / 512).  The pages print no formula; the reading
+ * implemented is a softmax over R of each channel's gate scores:
+ *
+ *   out[b, d] = sum_r exp(g[b,r,d] - m) x[b,r,d] / sum_r exp(g[b,r,d] - m),
+ *   m = max_r g[b,r,d];  -inf gates add nothing; an all -inf column gives 0.
+ *
+ * x, gate: [B, R, D] of SAP_BF16 or SAP_F32 with element strides (b, r) and
+ * unit stride along d; out: [B, D] of SAP_BF16 or SAP_F32 (row stride
+ * out_stride_b).  Computed in fp32.  R >= 1, B <= 65535.
+ * Errors: SAP_ERR_NULL, SAP_ERR_ALIGN (element alignment), SAP_ERR_SHAPE,
+ * SAP_ERR_DTYPE, SAP_ERR_LAUNCH.
+ * ------------------------------------------------------------------------- */
+int sap_gated_pool(const void *x, sap_dtype x_dtype, int64_t x_stride_b, int64_t x_stride_r,
+                   const void *gate, sap_dtype gate_dtype, int64_t gate_stride_b, int64_t gate_stride_r,
+                   void *out, sap_dtype out_dtype, int64_t out_stride_b,
+                   int B, int R, int D, sap_stream_t stream);
+
+/* -------------------------------------------------------------------------
  * Exact top-k selection (the index top-k of "perf(kernel): keep 16-byte kv
  * loads ...", Kernel time).  For each row b the candidates are the n <
  * n_valid[b] (n < N when n_valid is NULL) whose value is neither NaN nor -inf.

@@ -157,6 +157,32 @@ def indexer_logits_prefill(q, w, key_pool, page_table, page: int, tok_start, max
     return out
 
 
+def _float_dtype(dt) -> int:
+    if dt == torch.bfloat16:
+        return SAP_BF16
+    if dt == torch.float32:
+        return SAP_F32
+    raise ValueError(f"unsupported dtype {dt} (bf16 or fp32)")
+
+
+def gated_pool(x, gate, out_dtype=torch.float32, out=None) -> torch.Tensor:
+    """x, gate [B, R, D] (bf16 or fp32, unit stride along D) -> [B, D]:
+    softmax over R of the gates weighting the rows."""
+    _dev(x, gate, out)
+    B, R, D = x.shape
+    if gate.shape != x.shape:
+        raise ValueError("x and gate must have the same shape")
+    if D > 1 and (x.stride(2) != 1 or gate.stride(2) != 1):
+        raise ValueError("x and gate need unit stride along D")
+    if out is None:
+        out = torch.empty((B, D), dtype=out_dtype, device=x.device)
+    rc = lib().sap_gated_pool(_p(x), _float_dtype(x.dtype), x.stride(0), x.stride(1),
+                              _p(gate), _float_dtype(gate.dtype), gate.stride(0), gate.stride(1),
+                              _p(out), _float_dtype(out.dtype), out.stride(0), B, R, D, _stream(x))
+    check(rc, "sap_gated_pool")
+    return out
+
+
 def topk_workspace_bytes(B: int, N: int, k: int) -> int:
     return int(lib().sap_topk_workspace_bytes(B, N, k))
 

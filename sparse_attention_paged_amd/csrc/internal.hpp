@@ -73,6 +73,18 @@ struct IndexerPrefillParams {
     int kc;                          // keys per workgroup (multiple of 256)
 };
 int indexer_prefill_chunk(int S, int max_tokens, int N);
+
+struct GatedPoolParams {
+    const void *x;                   // [B, R, D] bf16 or fp32, element strides
+    int64_t x_sb, x_sr;
+    const void *g;                   // gate scores [B, R, D] bf16 or fp32
+    int64_t g_sb, g_sr;
+    void *out;                       // [B, D] bf16 or fp32
+    int64_t out_sb;
+    int B, R, D;
+    int x_bf16, g_bf16, out_bf16;
+};
+hipError_t launch_gated_pool(const GatedPoolParams &p, hipStream_t s);
 hipError_t launch_indexer_prefill(const IndexerPrefillParams &p, hipStream_t s);
 
 struct TopkParams {

@@ -321,6 +321,40 @@ int sap_indexer_logits_prefill(const void *q, int64_t q_stride_t,
     return launched(sap::launch_indexer_prefill(p, (hipStream_t)stream));
 }
 
+int sap_gated_pool(const void *x, sap_dtype x_dtype, int64_t x_stride_b, int64_t x_stride_r,
+                   const void *gate, sap_dtype gate_dtype, int64_t gate_stride_b, int64_t gate_stride_r,
+                   void *out, sap_dtype out_dtype, int64_t out_stride_b,
+                   int B, int R, int D, sap_stream_t stream)
+{
+    if (B < 0 || R < 1 || D < 0 || B > 65535) return SAP_ERR_SHAPE;
+    const bool dt_ok = (x_dtype == SAP_BF16 || x_dtype == SAP_F32) && (gate_dtype == SAP_BF16 || gate_dtype == SAP_F32) &&
+                       (out_dtype == SAP_BF16 || out_dtype == SAP_F32);
+    if (!dt_ok) return SAP_ERR_DTYPE;
+    if (B == 0 || D == 0) return SAP_OK;
+    if (!x || !gate || !out) return SAP_ERR_NULL;
+    if (x_stride_b < 0 || x_stride_r < 0 || gate_stride_b < 0 || gate_stride_r < 0 || out_stride_b < 0)
+        return SAP_ERR_SHAPE;
+    if (!aligned(x, dtype_size(x_dtype)) || !aligned(gate, dtype_size(gate_dtype)) ||
+        !aligned(out, dtype_size(out_dtype)))
+        return SAP_ERR_ALIGN;
+    sap::GatedPoolParams p{};
+    p.x = x;
+    p.x_sb = x_stride_b;
+    p.x_sr = x_stride_r;
+    p.g = gate;
+    p.g_sb = gate_stride_b;
+    p.g_sr = gate_stride_r;
+    p.out = out;
+    p.out_sb = out_stride_b;
+    p.B = B;
+    p.R = R;
+    p.D = D;
+    p.x_bf16 = x_dtype == SAP_BF16;
+    p.g_bf16 = gate_dtype == SAP_BF16;
+    p.out_bf16 = out_dtype == SAP_BF16;
+    return launched(sap::launch_gated_pool(p, (hipStream_t)stream));
+}
+
 size_t sap_topk_workspace_bytes(int B, int N, int k)
 {
     if (B <= 0 || N <= 0 || k < 1 || k > 4096) return 0;
