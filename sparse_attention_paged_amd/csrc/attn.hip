@@ -205,17 +205,26 @@ void attn_kernel(AttnParams p)
     const int dq = w & 1, ch = w >> 1;
     const int hbase = blockIdx.y * kAttnHeadsPerBlock;
 
-    // Q as the B operand of S^T over head_dim half dq:
-    // qf[j][s] = q[t, hbase + 16j + l16, D/2*dq + 32s + 8g .. +7]
-    uint4 qf[4][SH::SK];
+    // The block's 64 q rows are staged in the (still unused) first two tiles
+    // with whole-row LDS DMA (each instruction moves 1 KiB; 16-byte chunk c
+    // of row h lands in slot c ^ (h & 15), or h & 7 at D = 64), then each wave reads its
+    // fragments: loading the MFMA operand layout straight from memory would
+    // touch 16 rows per instruction and fetch every row twice.
+    // (bf16: tiles 2 and 3, so the first two tiles' gathers can go out
+    // while the fragments are read)
+    uint8_t *const qstage = KV == 0 ? &tiles[2][0] : &tiles[0][0];
+    constexpr int QSW = D >= 128 ? 15 : 7;   // chunk swizzle mask (a row has D/8 chunks)
+    {
+        constexpr int QI = 64 * 2 * D / 1024 / 4;   // DMA instructions per wave
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int head = hbase + 16 * j + l16;
-        const bool ok = head < p.H;
-        const uint16_t *qrow = p.q + (int64_t)t * p.q_st + (int64_t)(ok ? head : 0) * p.q_sh + (D / 2) * dq;
-#pragma unroll
-        for (int s = 0; s < SH::SK; ++s)
-            qf[j][s] = ok ? *(const uint4 *)(qrow + 32 * s + 8 * g) : make_uint4(0, 0, 0, 0);
+        for (int k = 0; k < QI; ++k) {
+            const int u = 4 * k + w;                  // 1 KiB block of the staging area
+            const int f = 1024 * u + 16 * lane;       // byte of the staging area this lane fills
+            const int h = f / (2 * D), c = (f % (2 * D)) / 16;
+            const int head = hbase + h < p.H ? hbase + h : hbase;   // rows past H: finite stand-in
+            const uint16_t *src = p.q + (int64_t)t * p.q_st + (int64_t)head * p.q_sh + 8 * (c ^ (h & QSW));
+            dma16(src, lds_offset(qstage + 1024 * u));
+        }
     }
     // finite data that invalid columns load instead of a pool row (their
     // scores are masked to -inf and their weights are 0)
@@ -238,6 +247,28 @@ void attn_kernel(AttnParams p)
     float rsc[SH::NQ];
     int cc = c_begin;      // first column of the current chunk
     int n_tiles = 0;       // tiles of the current chunk
+
+    // row indices of the first 4 x 256 columns, loaded while q lands and
+    // staged for the first chunk
+    {
+        int iv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + u * kThreads;
+            iv[u] = i < c_end - c_begin ? idx_row[c_begin + i] : -1;
+        }
+        const int n0 = (min(c_end - c_begin, kIdxChunk) + kAttnTile - 1) / kAttnTile * kAttnTile;
+        wait_vm<0>();
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + u * kThreads;
+            if (i < n0) sidx[i] = iv[u];
+        }
+    }
+    __syncthreads();
+    // Q as the B operand of S^T over head_dim half dq, read from the staging
+    // area below: qf[j][s] = q[t, hbase + 16j + l16, D/2*dq + 32s + 8g .. +7]
+    uint4 qf[4][SH::SK];
 
     // issue gather instruction q of tile `tile` (of the current chunk) into
     // buffer `bf`; the row index comes from the staged chunk
@@ -603,6 +634,25 @@ void attn_kernel(AttnParams p)
         for (int nt = 0; nt < 2; ++nt) l_run[nt] += st.psum[nt];
     };
 
+    // bf16: the first chunk's first two tiles go out now; their gathers are
+    // in flight while the q fragments are read
+    const bool early = KV == 0 && c_end > c_begin;
+    if (early) {
+        n_tiles = (min(c_end - c_begin, kIdxChunk) + kAttnTile - 1) / kAttnTile;
+        issue(tiles[0], metas[0], 0);
+        if (n_tiles > 1) issue(tiles[1], metas[1], 1);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bool ok = hbase + 16 * j + l16 < p.H;
+        const uint8_t *row = qstage + (16 * j + l16) * 2 * D;
+#pragma unroll
+        for (int s = 0; s < SH::SK; ++s) {
+            const int c = (D / 16) * dq + 4 * s + g;
+            qf[j][s] = ok ? *(const uint4 *)(row + 16 * (c ^ (l16 & QSW))) : make_uint4(0, 0, 0, 0);
+        }
+    }
+
     using Fast = std::integral_constant<bool, false>;
     using Slow = std::integral_constant<bool, true>;
     // columns are taken in chunks whose row indices are staged in LDS
@@ -612,7 +662,8 @@ void attn_kernel(AttnParams p)
         __syncthreads();   // the previous chunk's indices are no longer read
         // four loads in flight per thread before their stores (up to 1024
         // columns per memory round trip)
-        for (int i0 = 0; i0 < n_tiles * kAttnTile; i0 += 4 * kThreads) {
+        // (the first 4 x 256 of the first chunk were staged with q)
+        for (int i0 = cc == c_begin ? 4 * kThreads : 0; i0 < n_tiles * kAttnTile; i0 += 4 * kThreads) {
             int iv[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -630,13 +681,16 @@ void attn_kernel(AttnParams p)
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         // prologue: tiles 0 and 1 in LDS (bf16: tile 2 too), S of tile 0 and
-        // its partial-score exchange
-        issue(tiles[0], metas[0], 0);
+        // its partial-score exchange (the first chunk's tiles 0 and 1 went
+        // out with the q fragments; the barrier above also freed tile 2,
+        // which held q)
+        const bool issued = early && cc == c_begin;
+        if (!issued) issue(tiles[0], metas[0], 0);
         if constexpr (KV == 2) {
             wait_vm<0>();
             land(tiles[0], metas[0]);
         }
-        if (n_tiles > 1) issue(tiles[1], metas[1], 1);
+        if (!issued && n_tiles > 1) issue(tiles[1], metas[1], 1);
         if constexpr (KV == 2) {
             wait_vm<0>();
             if (n_tiles > 1) land(tiles[1], metas[1]);
@@ -722,63 +776,81 @@ void attn_kernel(AttnParams p)
                 }
             }
         } else {
+            // partial outputs in the accumulators' own layout
+            // [t][split][head block][w][m][j][lane] x 4 floats: each store
+            // instruction writes 1 KiB of consecutive bytes
             const int64_t slot = ((int64_t)t * p.num_splits + split) * p.H + head;
-            float *o = p.part_o + slot * D + d0;
+            const int64_t pb = (((int64_t)t * p.num_splits + split) * gridDim.y + blockIdx.y) * 4 + w;
 #pragma unroll
             for (int m = 0; m < SH::PM; ++m)
-                *(float4 *)(o + 16 * m) = make_float4(acc[m][j][0], acc[m][j][1], acc[m][j][2], acc[m][j][3]);
+                *(float4 *)(p.part_o + (((pb * SH::PM + m) * 4 + j) * 64 + lane) * 4) =
+                    make_float4(acc[m][j][0], acc[m][j][1], acc[m][j][2], acc[m][j][3]);
             if (g == 0 && w == 0) *(float2 *)(p.part_ml + slot * 2) = make_float2(m_run[j], l_tot);
         }
     }
 }
 
 // out[t, h, :] = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j over the splits
-// j in order; zero when every split was empty.  One thread per 4 head_dim
-// values; the partial loads of 8 splits are issued before any is used.
+// j in order; zero when every split was empty.  The partial outputs are in
+// the split kernel's accumulator layout [t][split][head block][w][m][j][lane]
+// x 4 floats: one wave of this kernel takes one (head block, w, m, j) group,
+// lane l owning head 16j + l%16 and head_dim 16m + 4(l/16) .. +3 of quarter w,
+// so its partial loads are 1 KiB contiguous per split.  The loads of up to 16
+// splits are issued before any is used (one memory round trip at the usual
+// split counts).
 template <int D, int OUT>
-__global__ __launch_bounds__(128) void attn_merge_kernel(AttnParams p)
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p)
 {
-    constexpr int U = 8;
-    const int t = blockIdx.x, head = blockIdx.y, tid = threadIdx.x;
-    if (4 * tid >= D) return;
+    constexpr int U = 16;
+    constexpr int PM = D / 64;
+    const int t = blockIdx.x;
+    const int grp = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int HB = (p.H + kAttnHeadsPerBlock - 1) / kAttnHeadsPerBlock;
+    if (grp >= HB * 4 * PM * 4) return;
+    const int j = grp % 4, m = (grp / 4) % PM, w = (grp / (4 * PM)) % 4, hb = grp / (16 * PM);
+    const int head = hb * kAttnHeadsPerBlock + 16 * j + (lane & 15);
+    if (head >= p.H) return;
+    const int d = (D / 4) * w + 16 * m + 4 * (lane >> 4);
     const int S = p.num_splits;
-    const int64_t slot0 = ((int64_t)t * S) * p.H + head;
-    float M = -INFINITY;
-    for (int j0 = 0; j0 < S; j0 += U) {
-        float m[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) m[u] = p.part_ml[(slot0 + (int64_t)min(j0 + u, S - 1) * p.H) * 2];
-#pragma unroll
-        for (int u = 0; u < U; ++u) M = fmaxf(M, m[u]);   // repeats of split S-1 change nothing
-    }
+    const int64_t pstride = (int64_t)HB * 4 * PM * 4 * 64;   // float4 slots per split
+    const float4 *po = (const float4 *)p.part_o + ((int64_t)t * S) * pstride + (int64_t)grp * 64 + lane;
+    const float2 *pml = (const float2 *)p.part_ml + ((int64_t)t * S) * p.H + head;
+    // one pass: each batch's (max, sum) and partial loads go out together and
+    // the running result is rescaled when a later batch raises the max
+    float M = -INFINITY, L = 0.0f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    float L = 0.0f;
-    if (M != -INFINITY) {
-        for (int j0 = 0; j0 < S; j0 += U) {
-            float2 ml[U];
-            float4 v[U];
+    for (int j0 = 0; j0 < S; j0 += U) {
+        float2 ml[U];
+        float4 v[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t slot = slot0 + (int64_t)min(j0 + u, S - 1) * p.H;
-                ml[u] = *(const float2 *)(p.part_ml + slot * 2);
-                v[u] = *(const float4 *)(p.part_o + slot * D + 4 * tid);
-            }
+        for (int u = 0; u < U; ++u) {
+            const int js = min(j0 + u, S - 1);
+            ml[u] = pml[(int64_t)js * p.H];
+            v[u] = po[(int64_t)js * pstride];
+        }
+        float Mb = M;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (j0 + u < S) {
-                    const float w = fast_exp2(ml[u].x - M);
-                    L += w * ml[u].y;
-                    o.x += w * v[u].x; o.y += w * v[u].y; o.z += w * v[u].z; o.w += w * v[u].w;
-                }
+        for (int u = 0; u < U; ++u) Mb = fmaxf(Mb, ml[u].x);   // repeats of split S-1 change nothing
+        if (Mb == -INFINITY) continue;                         // every split so far empty
+        const float r = M == -INFINITY ? 0.0f : fast_exp2(M - Mb);
+        L *= r;
+        o.x *= r; o.y *= r; o.z *= r; o.w *= r;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (j0 + u < S) {
+                const float wt = fast_exp2(ml[u].x - Mb);
+                L += wt * ml[u].y;
+                o.x += wt * v[u].x; o.y += wt * v[u].y; o.z += wt * v[u].z; o.w += wt * v[u].w;
             }
         }
+        M = Mb;
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     if constexpr (OUT == 1) {
-        float *dst = (float *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + 4 * tid;
+        float *dst = (float *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d;
         *(float4 *)dst = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
     } else {
-        uint16_t *dst = (uint16_t *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + 4 * tid;
+        uint16_t *dst = (uint16_t *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d;
         *(uint2 *)dst = make_uint2(pack_bf16x2(o.x * inv, o.y * inv), pack_bf16x2(o.z * inv, o.w * inv));
     }
 }
@@ -801,9 +873,11 @@ hipError_t launch_attn_d(const AttnParams &p, int kv, int out, hipStream_t s)
 template <int D>
 hipError_t launch_merge_d(const AttnParams &p, int out, hipStream_t s)
 {
-    const dim3 grid((unsigned)p.T, (unsigned)p.H);
-    if (out == 1) hipLaunchKernelGGL((attn_merge_kernel<D, 1>), grid, dim3(128), 0, s, p);
-    else hipLaunchKernelGGL((attn_merge_kernel<D, 0>), grid, dim3(128), 0, s, p);
+    // one wave per (head block, w, m, j) group of the partial layout
+    const int HB = (p.H + kAttnHeadsPerBlock - 1) / kAttnHeadsPerBlock;
+    const dim3 grid((unsigned)p.T, (unsigned)(HB * (D / 64) * 4));
+    if (out == 1) hipLaunchKernelGGL((attn_merge_kernel<D, 1>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((attn_merge_kernel<D, 0>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

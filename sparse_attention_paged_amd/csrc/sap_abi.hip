@@ -49,8 +49,12 @@ SplitPlan plan_splits(int T, int H, int n_cols, int requested)
 size_t attn_ws_bytes(int T, int H, int D, const SplitPlan &sp)
 {
     if (sp.splits <= 1) return 0;
+    // partial outputs for every head slot of the 64-head blocks, then
+    // (max, sum) per head
     const size_t slots = (size_t)T * sp.splits * H;
-    return align256(slots * D * 4) + align256(slots * 2 * 4);
+    const size_t oslots = (size_t)T * sp.splits * ((H + sap::kAttnHeadsPerBlock - 1) / sap::kAttnHeadsPerBlock) *
+                          sap::kAttnHeadsPerBlock;
+    return align256(oslots * D * 4) + align256(slots * 2 * 4);
 }
 
 inline int launched(hipError_t e) { return e == hipSuccess ? SAP_OK : SAP_ERR_LAUNCH; }
@@ -185,9 +189,10 @@ int sap_sparse_attn_paged(const void *q, sap_dtype q_dtype, int64_t q_stride_t, 
     p.num_splits = sp.splits;
     p.cols_per_split = sp.cols_per_split;
     if (sp.splits > 1) {
-        const size_t slots = (size_t)T * sp.splits * H;
+        const size_t oslots = (size_t)T * sp.splits *
+                              ((H + sap::kAttnHeadsPerBlock - 1) / sap::kAttnHeadsPerBlock) * sap::kAttnHeadsPerBlock;
         p.part_o = (float *)workspace;
-        p.part_ml = (float *)((uint8_t *)workspace + align256(slots * D * 4));
+        p.part_ml = (float *)((uint8_t *)workspace + align256(oslots * D * 4));
     }
     const int kv = kv_dtype == SAP_FP8_E4M3 ? 2 : 0;
     const int od = out_dtype == SAP_F32 ? 1 : 0;
