@@ -10,10 +10,12 @@
 // selection core runs in one 512-thread workgroup on keys held in registers,
 // each thread owning a contiguous run of positions:
 //  - radix select finds the prefix of the k-th largest key.  It starts below
-//    the bits every candidate shares (found by AND/OR reductions), takes 8
-//    bits per pass with one private LDS histogram per wave (no atomics shared
-//    between waves), and stops as soon as the bin holding the k-th key is
-//    taken whole;
+//    the bits every candidate shares (found by AND/OR reductions, which also
+//    count the candidates), takes 11 bits per pass into one LDS histogram of
+//    2048 bins (wide enough that clustered logits rarely pile onto one bin's
+//    atomics, and two passes usually settle it), finds the bin holding the
+//    k-th key with one block scan over 4 bins per thread, and stops as soon
+//    as that bin is taken whole;
 //  - the selected positions are written through one order-preserving block
 //    scan of (greater, equal) counts, so the output is already in ascending
 //    index order -- no sort.
@@ -48,10 +50,12 @@ __device__ __forceinline__ uint32_t order_key(float v)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // >= 0x00800000 otherwise
 }
 
+constexpr int kDigit = 11;               // bits per radix pass
+constexpr int kBins = 1 << kDigit;       // 4 per thread
+
 struct Shared {
-    uint32_t hist[kW][256];
-    uint32_t tot[256];
-    int red[2 * kW];
+    uint32_t hist[kBins];
+    int red[3 * kW];
     int misc[4];
 };
 
@@ -74,93 +78,97 @@ __device__ int block_excl_scan(int v, Shared &s, int &total)
     return base + x - v;
 }
 
-__device__ void block_and_or(uint32_t &a, uint32_t &o, Shared &s)
+// AND and OR of the nonzero keys and their count, over the workgroup
+__device__ void block_and_or_count(uint32_t &a, uint32_t &o, int &n, Shared &s)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     a = wave_last(wave_scan_dpp(a, ~0u, [](uint32_t x, uint32_t y) { return x & y; }));
     o = wave_last(wave_scan_dpp(o, 0u, [](uint32_t x, uint32_t y) { return x | y; }));
+    n = (int)wave_last((uint32_t)wave_incl_sum(n));
     if (lane == 0) {
         s.red[w] = (int)a;
         s.red[kW + w] = (int)o;
+        s.red[2 * kW + w] = n;
     }
     __syncthreads();
     a = ~0u;
     o = 0u;
+    n = 0;
 #pragma unroll
     for (int i = 0; i < kW; ++i) {
         a &= (uint32_t)s.red[i];
         o |= (uint32_t)s.red[kW + i];
+        n += s.red[2 * kW + i];
     }
     __syncthreads();
 }
 
 // Outcome of a radix select: keys with (key & M) > P are selected; of the
 // cnt_eq keys with (key & M) == P, the rem with the lowest positions are.
+// kk = min(k, number of nonzero keys) keys are selected in all.
 struct Sel {
     uint32_t P, M;
-    int rem;
+    int rem, kk;
 };
 
-// Radix select of the kk-th largest nonzero key (1 <= kk <= number of
-// nonzero keys).  for_each(f) calls f(key) for every key of the row.
+// Radix select of the k largest nonzero keys.  for_each(f) calls f(key) for
+// every key of the row.
 template <class ForEach>
-__device__ Sel radix_select(ForEach for_each, int kk, Shared &s)
+__device__ Sel radix_select(ForEach for_each, int k, Shared &s)
 {
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x;
     uint32_t a = ~0u, o = 0u;
+    int n = 0;
     for_each([&](uint32_t key) {
         if (key) {
             a &= key;
             o |= key;
+            ++n;
         }
     });
-    block_and_or(a, o, s);
+    block_and_or_count(a, o, n, s);
+    const int kk = min(k, n);
+    if (kk <= 0) return Sel{0u, 0u, 0, 0};
     const uint32_t diff = a ^ o;
-    if (diff == 0u) return Sel{a, ~0u, kk};   // every candidate has the same key
+    if (diff == 0u) return Sel{a, ~0u, kk, kk};   // every candidate has the same key
     int hb = 31 - __builtin_clz(diff);
     uint32_t M = ~((2u << hb) - 1u);          // hb == 31: 2u << 31 == 0, M == 0
     uint32_t P = a & M;
     int rem = kk;
-    uint32_t *h = s.hist[w];
+    // cleared once here; afterwards each thread clears the bins it reads
+    for (int i = tid; i < kBins; i += kT) s.hist[i] = 0u;
+    __syncthreads();
     for (;;) {
-        const int lo = hb >= 7 ? hb - 7 : 0;
-        const uint32_t dm = (1u << (hb - lo + 1)) - 1u;
-        // this wave's histogram: cleared and filled by the wave alone (its
-        // LDS operations stay in order), read by all after the barrier
-        for (int i = lane; i < 256; i += kWave) h[i] = 0u;
+        const int lo = hb >= kDigit - 1 ? hb - (kDigit - 1) : 0;
+        const uint32_t dm = (2u << (hb - lo)) - 1u;
         for_each([&](uint32_t key) {
-            if (key && (key & M) == P) atomicAdd(&h[(key >> lo) & dm], 1u);
+            if (key && (key & M) == P) atomicAdd(&s.hist[(key >> lo) & dm], 1u);
         });
         __syncthreads();
-        if (tid < 256) {
-            uint32_t t = 0;
+        // this thread's bins 4 tid .. 4 tid + 3, cleared for the next pass
+        int c[4];
 #pragma unroll
-            for (int i = 0; i < kW; ++i) t += s.hist[i][tid];
-            s.tot[tid] = t;
+        for (int i = 0; i < 4; ++i) {
+            c[i] = (int)s.hist[4 * tid + i];
+            s.hist[4 * tid + i] = 0u;
         }
-        __syncthreads();
-        if (w == 0) {
-            // lane l covers bins 4l .. 4l+3; x = keys in bins >= 4l
-            const int c0 = (int)s.tot[4 * lane], c1 = (int)s.tot[4 * lane + 1];
-            const int c2 = (int)s.tot[4 * lane + 2], c3 = (int)s.tot[4 * lane + 3];
-            const int c = c0 + c1 + c2 + c3;
-            const int pre = wave_incl_sum(c);                      // bins < 4l+4
-            const int x = (int)wave_last((uint32_t)pre) - pre + c;   // bins >= 4l
-            if (x >= rem && x - c < rem) {
-                int above = x - c, d = 4 * lane;
-                const int cb[4] = {c0, c1, c2, c3};
+        const int cs = c[0] + c[1] + c[2] + c[3];
+        int total;
+        const int pre = block_excl_scan(cs, s, total);   // keys in bins < 4 tid
+        const int x = total - pre;                       // keys in bins >= 4 tid
+        if (x >= rem && x - cs < rem) {
+            int above = x - cs, d = 4 * tid;
 #pragma unroll
-                for (int bb = 3; bb >= 0; --bb) {
-                    if (above + cb[bb] >= rem) {
-                        d = 4 * lane + bb;
-                        break;
-                    }
-                    above += cb[bb];
+            for (int bb = 3; bb >= 0; --bb) {
+                if (above + c[bb] >= rem) {
+                    d = 4 * tid + bb;
+                    break;
                 }
-                s.misc[0] = d;
-                s.misc[1] = above;
-                s.misc[2] = (int)s.tot[d];
+                above += c[bb];
             }
+            s.misc[0] = d;
+            s.misc[1] = above;
+            s.misc[2] = c[d - 4 * tid];
         }
         __syncthreads();
         const int d = s.misc[0];
@@ -168,7 +176,7 @@ __device__ Sel radix_select(ForEach for_each, int kk, Shared &s)
         const int cd = s.misc[2];
         P |= (uint32_t)d << lo;
         M |= dm << lo;
-        if (cd == rem || lo == 0) return Sel{P, M, rem};
+        if (cd == rem || lo == 0) return Sel{P, M, rem, kk};
         hb = lo - 1;
     }
 }
@@ -246,14 +254,10 @@ __device__ void select_streaming(const float *x, int nv, int k, int32_t *out, Sh
             for (int j = 0; j < KPT; ++j) f(key[j]);
         }
     };
-    int nz = 0;
-    for_each([&](uint32_t key) { nz += key != 0u; });
-    int valid;
-    block_excl_scan(nz, s, valid);
-    const int kk = min(k, valid);
+    const Sel q = radix_select(for_each, k, s);
+    const int kk = q.kk;
     int gt_seen = 0, eq_seen = 0;
     if (kk > 0) {
-        const Sel q = radix_select(for_each, kk, s);
         for (int base = 0; base < nv; base += BLK) {
             uint32_t key[KPT];
             load_keys<KPT>(x, base, nv, key);
@@ -276,23 +280,17 @@ __global__ __launch_bounds__(kT) void topk_direct_kernel(TopkParams p)
     nv = min(max(nv, 0), p.N);
     uint32_t key[KPT];
     load_keys<KPT>(x, 0, nv, key);
-    int nz = 0;
+    auto for_each = [&](auto f) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) nz += key[j] != 0u;
-    int valid;
-    block_excl_scan(nz, s, valid);
-    const int kk = min(p.k, valid);
+        for (int j = 0; j < KPT; ++j) f(key[j]);
+    };
+    const Sel q = radix_select(for_each, p.k, s);
     int gt_seen = 0, eq_seen = 0;
-    if (kk > 0) {
-        auto for_each = [&](auto f) {
-#pragma unroll
-            for (int j = 0; j < KPT; ++j) f(key[j]);
-        };
-        const Sel q = radix_select(for_each, kk, s);
+    if (q.kk > 0) {
         const int p0 = (int)threadIdx.x * KPT;
         emit_block<KPT>(key, [&](int j) { return p0 + j; }, q, out, gt_seen, eq_seen, s);
     }
-    pad_out(out, kk, p.k);
+    pad_out(out, q.kk, p.k);
 }
 
 // workspace of the two-launch path, per row: chunk counts, the sample
