@@ -80,9 +80,8 @@ class DecodeStep:
         if self.ratio > 0:
             sap.indexer_logits_packed(self.qi, self.wi, self.keys, self.cmp_pt, self.case.page, self.n_c,
                                       n_keys=self.n_vis, out=self.logits)
-            sap.topk_select(self.logits, self.case.n_cmp, out=self.sel, workspace=self.tk_ws)
-            sap.build_sparse_idx(self.pos, self.seq, self.case.n_win, self.win_pt, self.case.page, self.sel,
-                                 self.cmp_pt, out=self.idx)
+            sap.topk_sparse_idx(self.logits, self.case.n_cmp, self.pos, self.seq, self.case.n_win, self.win_pt,
+                                self.cmp_pt, self.case.page, out=self.idx, workspace=self.tk_ws)
         else:
             sap.build_sparse_idx(self.pos, self.seq, self.case.n_win, self.win_pt, self.case.page, out=self.idx)
 
@@ -342,7 +341,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "decode_b1_pos32767_r4_bf16", "global_batch": 1, "seq_len": 32768, "heads": 64,
                    "head_dim": 512, "window": 128, "topk": 512, "ratio": 4, "parallelism": "single-gpu",
-                   "step": "indexer(8192 fp4 keys) + top-512 + index build + split-K attention + merge"},
+                   "step": "indexer(8192 fp4 keys) + top-512 fused with the index build + split-K attention + merge"},
         "timing": f"HIP-graph replays ({GRAPH_CALLS} steps per graph), HIP events around the timed replays",
         "eager_ms_per_step": round(ms_step_eager, 5),
         "attn_us": round(ms_attn * 1e3, 3), "select_us": round(ms_sel * 1e3, 3), "splits": st.splits,

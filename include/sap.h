@@ -268,6 +268,31 @@ int sap_topk_select(const float *logits, int64_t stride_b, const int32_t *n_vali
                     void *workspace, size_t workspace_bytes, sap_stream_t stream);
 
 /* -------------------------------------------------------------------------
+ * Top-k selection fused with the index build (the decode step's selection:
+ * the indexer's logits -> the attention's column rows in one launch).  The
+ * result is exactly that of sap_topk_select(logits, ..., k, sel) followed by
+ * sap_build_sparse_idx(pos, seq, T, n_win, win_pt, ..., cmp_logical = sel,
+ * n_cmp = k, cmp_pt, ..., idx): for token t,
+ *
+ *   idx[t][j]         = window row of position pos[t] - (n_win-1) + j, or -1,
+ *   idx[t][n_win + j] = cmp_pt row of the j-th selected entry (ascending
+ *                       entry order), or -1 past the selected count.
+ *
+ * logits: [T, N] fp32 (row stride stride_t), candidates as for
+ * sap_topk_select (n_valid may be NULL); pos, seq: [T] int32; page tables as
+ * for sap_build_sparse_idx (cmp_pt required, win_pt when n_win > 0);
+ * idx: [T, >= n_win + k] int32.  workspace: sap_topk_workspace_bytes(T, N, k)
+ * bytes.  Limits as sap_topk_select.
+ * Errors: SAP_ERR_NULL, SAP_ERR_ALIGN, SAP_ERR_SHAPE, SAP_ERR_WORKSPACE,
+ * SAP_ERR_LAUNCH.
+ * ------------------------------------------------------------------------- */
+int sap_topk_sparse_idx(const float *logits, int64_t stride_t, const int32_t *n_valid, int T, int N, int k,
+                        const int32_t *pos, const int32_t *seq, int n_win,
+                        const int32_t *win_pt, int64_t win_pt_stride, const int32_t *cmp_pt, int64_t cmp_pt_stride,
+                        int page, int32_t *idx, int64_t idx_stride,
+                        void *workspace, size_t workspace_bytes, sap_stream_t stream);
+
+/* -------------------------------------------------------------------------
  * Format hooks: run the device decode functions of the hot path over every
  * code, so tests can compare them bit for bit with the format definitions.
  *

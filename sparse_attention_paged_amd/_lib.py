@@ -30,6 +30,8 @@ SIGNATURES = {
     "sap_gated_pool": (_I, [_P, _I, _I64, _I64, _P, _I, _I64, _I64, _P, _I, _I64, _I, _I, _I, _P]),
     "sap_topk_workspace_bytes": (_SZ, [_I, _I, _I]),
     "sap_topk_select": (_I, [_P, _I64, _P, _I, _I, _I, _P, _I64, _P, _SZ, _P]),
+    "sap_topk_sparse_idx": (_I, [_P, _I64, _P, _I, _I, _I, _P, _P, _I, _P, _I64, _P, _I64, _I, _P, _I64, _P,
+                                 _SZ, _P]),
     "sap_debug_e4m3_table": (_I, [_P, _P, _P]),
     "sap_debug_fp4_table": (_I, [_P, _P]),
 }

@@ -203,6 +203,25 @@ def topk_select(logits, k: int, n_valid=None, out=None, workspace=None) -> torch
     return out
 
 
+def topk_sparse_idx(logits, k: int, pos, seq, n_win: int, win_pt, cmp_pt, page: int, n_valid=None, out=None,
+                    workspace=None) -> torch.Tensor:
+    """Top-k of logits [T, N] fused with the index build -> int32 [T, n_win + k]
+    attention column rows (window rows, then the selected entries' rows)."""
+    _dev(logits, pos, seq, win_pt, cmp_pt, n_valid, out, workspace)
+    T, N = logits.shape
+    if out is None:
+        out = torch.empty((T, n_win + k), dtype=torch.int32, device=logits.device)
+    need = topk_workspace_bytes(T, N, k)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    rc = lib().sap_topk_sparse_idx(
+        _p(logits), logits.stride(0), _p(n_valid), T, N, k, _p(pos), _p(seq), n_win,
+        _p(win_pt), win_pt.stride(0) if win_pt is not None else 0, _p(cmp_pt), cmp_pt.stride(0), page,
+        _p(out), out.stride(0), _p(workspace), 0 if workspace is None else workspace.numel(), _stream(logits))
+    check(rc, "sap_topk_sparse_idx")
+    return out
+
+
 def debug_e4m3_table(device="cuda"):
     """(uint16 [256] bf16 bits from the attention row loader, fold factor)."""
     out = torch.empty(256, dtype=torch.int16, device=device)

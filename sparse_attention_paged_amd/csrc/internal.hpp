@@ -95,6 +95,15 @@ struct TopkParams {
     int32_t *out;
     int64_t out_sb;
     void *workspace;                 // topk_workspace_bytes(B, N, k) bytes
+    // fused index build (idx != null): row b of idx [B, n_win + k] receives
+    // the window rows of position pos[b] and the selected entries mapped
+    // through page table row seq[b] (out is unused)
+    int32_t *idx;
+    int64_t idx_st;
+    const int32_t *pos, *seq;
+    int n_win, page;
+    const int32_t *win_pt, *cmp_pt;
+    int64_t win_pt_sb, cmp_pt_sb;
 };
 size_t topk_workspace_bytes(int B, int N, int k);
 hipError_t launch_topk(const TopkParams &p, hipStream_t s);

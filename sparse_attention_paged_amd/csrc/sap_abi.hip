@@ -390,6 +390,42 @@ int sap_topk_select(const float *logits, int64_t stride_b, const int32_t *n_vali
     return launched(sap::launch_topk(p, (hipStream_t)stream));
 }
 
+int sap_topk_sparse_idx(const float *logits, int64_t stride_t, const int32_t *n_valid, int T, int N, int k,
+                        const int32_t *pos, const int32_t *seq, int n_win,
+                        const int32_t *win_pt, int64_t win_pt_stride, const int32_t *cmp_pt, int64_t cmp_pt_stride,
+                        int page, int32_t *idx, int64_t idx_stride,
+                        void *workspace, size_t workspace_bytes, sap_stream_t stream)
+{
+    if (T < 0 || N < 0 || k < 1 || k > 4096 || n_win < 0 || page <= 0) return SAP_ERR_SHAPE;
+    if (T == 0) return SAP_OK;
+    if (!idx || !pos || !seq || !cmp_pt || (N > 0 && !logits)) return SAP_ERR_NULL;
+    if (n_win > 0 && !win_pt) return SAP_ERR_NULL;
+    if (idx_stride < (int64_t)n_win + k || (N > 0 && stride_t < N) || win_pt_stride < 0 || cmp_pt_stride < 0)
+        return SAP_ERR_SHAPE;
+    if (!aligned(idx, 4) || (logits && !aligned(logits, 4))) return SAP_ERR_ALIGN;
+    const size_t need = sap_topk_workspace_bytes(T, N, k);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return SAP_ERR_WORKSPACE;
+    sap::TopkParams p{};
+    p.x = logits;
+    p.x_sb = stride_t;
+    p.n_valid = n_valid;
+    p.B = T;
+    p.N = N;
+    p.k = k;
+    p.workspace = workspace;
+    p.idx = idx;
+    p.idx_st = idx_stride;
+    p.pos = pos;
+    p.seq = seq;
+    p.n_win = n_win;
+    p.page = page;
+    p.win_pt = win_pt;
+    p.win_pt_sb = win_pt_stride;
+    p.cmp_pt = cmp_pt;
+    p.cmp_pt_sb = cmp_pt_stride;
+    return launched(sap::launch_topk(p, (hipStream_t)stream));
+}
+
 int sap_debug_e4m3_table(uint16_t *out, float *fold_factor, sap_stream_t stream)
 {
     if (!out || !fold_factor) return SAP_ERR_NULL;

@@ -184,12 +184,88 @@ __device__ Sel radix_select(ForEach for_each, int k, Shared &s)
 __device__ __forceinline__ bool sel_gt(uint32_t key, const Sel &q) { return key && (key & q.M) > q.P; }
 __device__ __forceinline__ bool sel_eq(uint32_t key, const Sel &q) { return key && (key & q.M) == q.P; }
 
+// Where the selected positions go.  IndexList: out[b][slot] = position.
+// SparseIdx (the decode step's fused index build): the selection of token b
+// becomes columns n_win + slot of its attention index row, each entry mapped
+// to its compressed-pool row through the token's page table; the kernel also
+// writes the window columns 0 .. n_win-1 (positions pos-n_win+1 .. pos).
+struct IndexList {
+    int32_t *out;
+    __device__ IndexList(const TopkParams &p, int b) : out(p.out + (int64_t)b * p.out_sb) {}
+    __device__ int value(int position) const { return position; }
+    // values of a run of n consecutive positions from p0, prepared ahead
+    struct Run {
+        int p0;
+    };
+    __device__ Run run(int p0, int, int) const { return Run{p0}; }
+    __device__ int value_in(const Run &, int position) const { return position; }
+    __device__ void put(int slot, int v) const { out[slot] = v; }
+    __device__ void pad(int slot) const { out[slot] = -1; }
+    __device__ void window() const {}
+};
+struct SparseIdx {
+    int32_t *row;
+    const int32_t *cmp_pt, *win_pt;
+    int n_win, page, pos, sh;   // sh = log2(page) for power-of-two pages, else -1
+    __device__ SparseIdx(const TopkParams &p, int b)
+    {
+        const int sq = p.seq[b];
+        row = p.idx + (int64_t)b * p.idx_st;
+        cmp_pt = p.cmp_pt + (int64_t)sq * p.cmp_pt_sb;
+        win_pt = p.win_pt + (int64_t)sq * p.win_pt_sb;
+        n_win = p.n_win;
+        page = p.page;
+        pos = p.pos[b];
+        sh = (page & (page - 1)) == 0 ? 31 - __builtin_clz((uint32_t)page) : -1;
+    }
+    __device__ int value(int L) const
+    {
+        if (sh >= 0) return (cmp_pt[L >> sh] << sh) + (L & (page - 1));
+        return cmp_pt[L / page] * page + L % page;
+    }
+    // a run of n <= page consecutive positions from p0 (below N) lies in the
+    // page starting at base and the next one: their two page-table entries
+    // are loaded up front, and no position needs a division
+    struct Run {
+        int base, n, e0, e1;
+    };
+    __device__ Run run(int p0, int n, int N) const
+    {
+        Run r{p0 - (sh >= 0 ? p0 & (page - 1) : p0 % page), n, 0, 0};
+        if (p0 < N && n <= page) {
+            const int last = min(p0 + n, N) - 1;
+            r.e0 = cmp_pt[sh >= 0 ? p0 >> sh : p0 / page];
+            r.e1 = cmp_pt[sh >= 0 ? last >> sh : last / page];
+        }
+        return r;
+    }
+    __device__ int value_in(const Run &r, int L) const
+    {
+        if (r.n > page) return value(L);   // pages shorter than a run: look each up
+        const int off = L - r.base;
+        return off < page ? r.e0 * page + off : r.e1 * page + (off - page);
+    }
+    __device__ void put(int slot, int v) const { row[n_win + slot] = v; }
+    __device__ void pad(int slot) const { row[n_win + slot] = -1; }
+    __device__ void window() const
+    {
+        for (int j = (int)threadIdx.x; j < n_win; j += kT) {
+            const int64_t q = (int64_t)pos - (n_win - 1) + j;
+            int32_t r = -1;
+            if (q >= 0)
+                r = sh >= 0 ? (win_pt[q >> sh] << sh) + (int32_t)(q & (page - 1))
+                            : win_pt[q / page] * page + (int32_t)(q % page);
+            row[j] = r;
+        }
+    }
+};
+
 // Writes the selected positions of a block of KPT keys per thread in
 // position order: a selected key's slot is the number of greater keys before
 // it plus min(equal keys before it, rem).  One scan of both counts (16 bits
 // each) gives both.  gt_seen / eq_seen carry the counts of earlier blocks.
-template <int KPT, class IdxOf>
-__device__ void emit_block(const uint32_t (&key)[KPT], IdxOf idx_of, const Sel &q, int32_t *out, int &gt_seen,
+template <int KPT, class ValOf, class Out>
+__device__ void emit_block(const uint32_t (&key)[KPT], ValOf val_of, const Sel &q, const Out &out, int &gt_seen,
                            int &eq_seen, Shared &s)
 {
     int n_gt = 0, n_eq = 0;
@@ -198,16 +274,21 @@ __device__ void emit_block(const uint32_t (&key)[KPT], IdxOf idx_of, const Sel &
         n_gt += sel_gt(key[j], q);
         n_eq += sel_eq(key[j], q);
     }
+    // values of the candidate positions first (any loads they need are in
+    // flight together), then the stores
+    int val[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) val[j] = (sel_gt(key[j], q) || sel_eq(key[j], q)) ? val_of(j) : 0;
     int tot;
     const int before = block_excl_scan(n_gt | (n_eq << 16), s, tot);
     int g = gt_seen + (before & 0xFFFF), e = eq_seen + (before >> 16);
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         if (sel_gt(key[j], q)) {
-            out[g + min(e, q.rem)] = idx_of(j);
+            out.put(g + min(e, q.rem), val[j]);
             ++g;
         } else if (sel_eq(key[j], q)) {
-            if (e < q.rem) out[g + e] = idx_of(j);
+            if (e < q.rem) out.put(g + e, val[j]);
             ++e;
         }
     }
@@ -215,9 +296,10 @@ __device__ void emit_block(const uint32_t (&key)[KPT], IdxOf idx_of, const Sel &
     eq_seen += tot >> 16;
 }
 
-__device__ void pad_out(int32_t *out, int from, int k)
+template <class Out>
+__device__ void pad_out(const Out &out, int from, int k)
 {
-    for (int i = from + (int)threadIdx.x; i < k; i += kT) out[i] = -1;
+    for (int i = from + (int)threadIdx.x; i < k; i += kT) out.pad(i);
 }
 
 // KPT consecutive keys of positions base + tid*KPT .. from row x (n valid)
@@ -242,7 +324,8 @@ __device__ void load_keys(const float *x, int64_t base, int n, uint32_t (&key)[K
 }
 
 // the whole row streamed from memory: every pass reads it again
-__device__ void select_streaming(const float *x, int nv, int k, int32_t *out, Shared &s)
+template <class Out>
+__device__ void select_streaming(const float *x, int nv, int k, const Out &out, Shared &s)
 {
     constexpr int KPT = 8;
     constexpr int BLK = kT * KPT;
@@ -262,34 +345,35 @@ __device__ void select_streaming(const float *x, int nv, int k, int32_t *out, Sh
             uint32_t key[KPT];
             load_keys<KPT>(x, base, nv, key);
             const int p0 = base + (int)threadIdx.x * KPT;
-            emit_block<KPT>(key, [&](int j) { return p0 + j; }, q, out, gt_seen, eq_seen, s);
+            const auto run = out.run(p0, KPT, nv);
+            emit_block<KPT>(key, [&](int j) { return out.value_in(run, p0 + j); }, q, out, gt_seen, eq_seen, s);
         }
     }
     pad_out(out, kk, k);
 }
 
 // rows of at most kT * KPT positions, keys in registers
-template <int KPT>
+template <int KPT, class Out>
 __global__ __launch_bounds__(kT) void topk_direct_kernel(TopkParams p)
 {
     __shared__ Shared s;
     const int b = blockIdx.x;
     const float *x = p.x + (int64_t)b * p.x_sb;
-    int32_t *out = p.out + (int64_t)b * p.out_sb;
+    const Out out(p, b);
     int nv = p.n_valid ? p.n_valid[b] : p.N;
     nv = min(max(nv, 0), p.N);
     uint32_t key[KPT];
     load_keys<KPT>(x, 0, nv, key);
+    const int p0 = (int)threadIdx.x * KPT;
+    const auto run = out.run(p0, KPT, nv);
+    out.window();
     auto for_each = [&](auto f) {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) f(key[j]);
     };
     const Sel q = radix_select(for_each, p.k, s);
     int gt_seen = 0, eq_seen = 0;
-    if (q.kk > 0) {
-        const int p0 = (int)threadIdx.x * KPT;
-        emit_block<KPT>(key, [&](int j) { return p0 + j; }, q, out, gt_seen, eq_seen, s);
-    }
+    if (q.kk > 0) emit_block<KPT>(key, [&](int j) { return out.value_in(run, p0 + j); }, q, out, gt_seen, eq_seen, s);
     pad_out(out, q.kk, p.k);
 }
 
@@ -383,6 +467,7 @@ __global__ __launch_bounds__(kT) void topk_filter_kernel(TopkParams p, int nch)
 }
 
 // select launch: grid (B)
+template <class Out>
 __global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
 {
     constexpr int KPT = kDirectMax / kT;
@@ -392,7 +477,8 @@ __global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
     __shared__ int offs[kMaxChunks];
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const float *x = p.x + (int64_t)b * p.x_sb;
-    int32_t *out = p.out + (int64_t)b * p.out_sb;
+    const Out out(p, b);
+    out.window();
     int nv = p.n_valid ? p.n_valid[b] : p.N;
     nv = min(max(nv, 0), p.N);
     const TopkWs ws = topk_ws(p.workspace, p.B, nch);
@@ -449,18 +535,21 @@ __global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
             for (int j = 0; j < KPT; ++j) f(key[j]);
         };
         const Sel q = radix_select(for_each, kk, s);
-        emit_block<KPT>(key, [&](int j) { return cpos[tid * KPT + j]; }, q, out, gt_seen, eq_seen, s);
+        emit_block<KPT>(key, [&](int j) { return out.value(cpos[tid * KPT + j]); }, q, out, gt_seen, eq_seen, s);
     }
     pad_out(out, kk, p.k);
 }
 
+template <class Out>
 __global__ __launch_bounds__(kT) void topk_stream_kernel(TopkParams p)
 {
     __shared__ Shared s;
     const int b = blockIdx.x;
     int nv = p.n_valid ? p.n_valid[b] : p.N;
     nv = min(max(nv, 0), p.N);
-    select_streaming(p.x + (int64_t)b * p.x_sb, nv, p.k, p.out + (int64_t)b * p.out_sb, s);
+    const Out out(p, b);
+    out.window();
+    select_streaming(p.x + (int64_t)b * p.x_sb, nv, p.k, out, s);
 }
 
 int n_chunks(int N) { return (N + kChunk - 1) / kChunk; }
@@ -474,25 +563,35 @@ size_t topk_workspace_bytes(int B, int N, int k)
     return topk_ws_size(B, n_chunks(N));
 }
 
-hipError_t launch_topk(const TopkParams &p, hipStream_t st)
+namespace {
+
+template <class Out>
+hipError_t launch_topk_t(const TopkParams &p, hipStream_t st)
 {
     if (p.B == 0) return hipSuccess;
     if (p.N <= kDirectMax) {
-        if (p.N <= 8 * kT) hipLaunchKernelGGL(topk_direct_kernel<8>, dim3((unsigned)p.B), dim3(kT), 0, st, p);
-        else if (p.N <= 16 * kT) hipLaunchKernelGGL(topk_direct_kernel<16>, dim3((unsigned)p.B), dim3(kT), 0, st, p);
-        else hipLaunchKernelGGL(topk_direct_kernel<32>, dim3((unsigned)p.B), dim3(kT), 0, st, p);
+        if (p.N <= 8 * kT) hipLaunchKernelGGL((topk_direct_kernel<8, Out>), dim3((unsigned)p.B), dim3(kT), 0, st, p);
+        else if (p.N <= 16 * kT) hipLaunchKernelGGL((topk_direct_kernel<16, Out>), dim3((unsigned)p.B), dim3(kT), 0, st, p);
+        else hipLaunchKernelGGL((topk_direct_kernel<32, Out>), dim3((unsigned)p.B), dim3(kT), 0, st, p);
         return hipGetLastError();
     }
     const int nch = n_chunks(p.N);
     if (nch > kMaxChunks) {
-        hipLaunchKernelGGL(topk_stream_kernel, dim3((unsigned)p.B), dim3(kT), 0, st, p);
+        hipLaunchKernelGGL((topk_stream_kernel<Out>), dim3((unsigned)p.B), dim3(kT), 0, st, p);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)nch, (unsigned)p.B), dim3(kT), 0, st, p, nch);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)p.B), dim3(kT), 0, st, p, nch);
+    hipLaunchKernelGGL((topk_select_kernel<Out>), dim3((unsigned)p.B), dim3(kT), 0, st, p, nch);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_topk(const TopkParams &p, hipStream_t st)
+{
+    return p.idx ? launch_topk_t<SparseIdx>(p, st) : launch_topk_t<IndexList>(p, st);
 }
 
 }  // namespace sap

@@ -11,7 +11,9 @@ from gpu_helpers import dev, need_gpu, say
 pytestmark = pytest.mark.gpu
 
 
-def test_decode_step_graph_replays_match_eager():
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_step_graph_replays_match_eager(fused):
+    """fused: the selection runs as one top-k + index build launch."""
     need_gpu()
     c = W.decode_case(B=2, pos=4095, ratio=4, seed=W.SEED_BASE + 900)
     g = W.make_generator(W.SEED_BASE + 901)
@@ -31,8 +33,11 @@ def test_decode_step_graph_replays_match_eager():
 
     def step():
         sap.indexer_logits_packed(qi, wi, keys, cmp_pt, c.page, n_c, n_keys=nv, out=logits)
-        sap.topk_select(logits, c.n_cmp, out=sel)
-        sap.build_sparse_idx(pos, seq, c.n_win, win_pt, c.page, sel, cmp_pt, out=idx)
+        if fused:
+            sap.topk_sparse_idx(logits, c.n_cmp, pos, seq, c.n_win, win_pt, cmp_pt, c.page, out=idx)
+        else:
+            sap.topk_select(logits, c.n_cmp, out=sel)
+            sap.build_sparse_idx(pos, seq, c.n_win, win_pt, c.page, sel, cmp_pt, out=idx)
         sap.sparse_attn_paged(q, win, cmp, idx, c.n_win, c.sm_scale, out=out, workspace=ws)
 
     step()
@@ -55,5 +60,7 @@ def test_decode_step_graph_replays_match_eager():
         graph.replay()
         torch.cuda.synchronize()
         for name, a, b in zip(("logits", "top-k", "idx", "out"), (logits, sel, idx, out), ref):
+            if fused and name == "top-k":
+                continue   # the fused selection writes the index rows only
             assert torch.equal(a, b), f"replay {r}: {name} differs from the eager step"
         say(f"  replay {r}: identical to eager")

@@ -175,3 +175,45 @@ def test_chain_indexer_topk_attention_small():
     assert torch.equal(idx.cpu(), oidx)
     ref = oracle.sparse_attn(q, wp, cp, oidx, case.n_win, case.sm_scale)
     assert_attn_close(out, ref, "chain")
+
+
+def _tk_idx_inputs(T, N, n_win, nv, seed, page=64):
+    g = torch.Generator().manual_seed(seed)
+    x = (torch.randn(T, N, generator=g) * 8).round() / 8          # many ties
+    x[torch.rand(T, N, generator=g) < 0.01] = -float("inf")
+    x[torch.rand(T, N, generator=g) < 0.002] = float("nan")
+    S = max(1, (T + 1) // 2)
+    seq = (torch.arange(T) % S).to(torch.int32)
+    pos = torch.randint(0, 3 * n_win + 1, (T,), generator=g).to(torch.int32)   # some windows start below 0
+    pos[0] = 5000
+    wpages = (int(pos.max()) + page) // page
+    win_pt = torch.randperm(S * wpages, generator=g).to(torch.int32).view(S, wpages)
+    cpages = (N + page - 1) // page
+    cmp_pt = torch.randperm(S * cpages, generator=g).to(torch.int32).view(S, cpages)
+    n_valid = None if nv is None else torch.tensor(nv, dtype=torch.int32)
+    return x, seq, pos, win_pt, cmp_pt, n_valid
+
+
+@pytest.mark.parametrize("T,N,k,n_win,nv", [
+    (1, 8192, 512, 128, None),             # the decode step's selection
+    (8, 8192, 512, 128, None),
+    (3, 2000, 512, 128, [2000, 300, 0]),   # fewer candidates than k, an empty row
+    (2, 40000, 512, 64, None),             # filter + select launches
+    (2, 5000, 100, 16, [4999, 17]),
+])
+def test_topk_sparse_idx_matches_oracle(T, N, k, n_win, nv):
+    """The fused selection + index build against the oracle's top-k followed
+    by its index build, and against the two GPU calls, bit for bit."""
+    need_gpu()
+    x, seq, pos, win_pt, cmp_pt, n_valid = _tk_idx_inputs(T, N, n_win, nv, seed=600 + T + N)
+    sel_ref = oracle.topk(x, k, n_valid)
+    idx_ref = oracle.build_idx(pos, seq, n_win, win_pt, 64, sel_ref, k, cmp_pt)
+    got = sap.topk_sparse_idx(dev(x), k, dev(pos), dev(seq), n_win, dev(win_pt), dev(cmp_pt), 64,
+                              n_valid=dev(n_valid))
+    torch.cuda.synchronize()
+    assert torch.equal(got.cpu(), idx_ref), f"T{T} N{N} k{k}: fused index rows differ from the oracle"
+    sel = sap.topk_select(dev(x), k, n_valid=dev(n_valid))
+    two = sap.build_sparse_idx(dev(pos), dev(seq), n_win, dev(win_pt), 64, sel, dev(cmp_pt))
+    torch.cuda.synchronize()
+    assert torch.equal(got, two)
+    say(f"  topk_sparse_idx T{T} N{N} k{k} n_win{n_win}: identical to oracle and to the two calls")
