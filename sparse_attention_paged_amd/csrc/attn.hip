@@ -153,11 +153,22 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p)
     return (uint32_t)(size_t)(const __attribute__((address_space(3))) uint8_t *)p;
 }
 
-template <int D, int KV, int OUT>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+// NW = 4: one wave per SIMD (the roles below); NW = 8: two head groups of
+// four waves for S and the softmax, each wave holding half the Q operand and
+// half the O accumulators, so two waves share each SIMD (D >= 128).
+template <int D, int KV, int OUT, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void attn_kernel(AttnParams p)
 {
     using SH = AttnShape<D>;
+    static_assert(NW == 4 || (NW == 8 && D >= 128), "eight waves need at least two gather rows per wave");
+    constexpr int NT = 64 * NW;            // threads
+    constexpr int G = NW / 4;              // head groups of S / softmax
+    constexpr int JS = 4 / G;              // 16-head tiles a wave computes S for
+    constexpr int JO = JS / 2;             // 16-head tiles whose softmax a wave owns
+    constexpr int RW = kAttnTile / NW;     // gather rows per wave per tile
+    constexpr int NQW = SH::NQ * 4 / NW;   // gather instructions per wave per tile
+    constexpr int PMW = D / (16 * NW);     // PV m-steps over this wave's head_dim range
     using Raw = typename RawRow<KV>::T;
     // bf16 terms per PV weight: e4m3 weights carry the row scale and PV must
     // hold them to fp32-like precision (outputs reach ~1e3 against an
@@ -172,20 +183,20 @@ void attn_kernel(AttnParams p)
     // so that the four waves never issue them in one burst: rows [0, GA)
     // during PV(u-3), rows [GA, GA+GB) during S(u-2), the rest during the
     // softmax of u-2.  Tile u's buffer held tile u-4, free after B1(u-3).
-    constexpr int GA = SH::NQ * 3 / 8, GB = SH::NQ * 3 / 8;
-    static_assert(GA <= SH::PM && GB <= SH::SK, "every gather row needs a PV or S step");
+    constexpr int GA = NQW * 3 / 8, GB = NQW * 3 / 8;
+    static_assert(GA <= PMW && GB <= SH::SK, "every gather row needs a PV or S step");
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[DEPTH][SH::TILE_BYTES];
     __shared__ __attribute__((aligned(16))) float metas[DEPTH][2 * kAttnTile];
     __shared__ __attribute__((aligned(16))) int sidx[kIdxChunk];
-    __shared__ float4 xs[4][2][64];          // partial scores for the partner wave
-    // bf16 P by [term][dq][nt][ch][lane]: the two column halves of one head
-    // tile sit 512 bytes apart, so a lane reads its B operand with one
+    __shared__ float4 xs[NW][JO][64];        // partial scores for the partner wave
+    // bf16 P by [term][head tile][ch][lane]: the two column halves of one
+    // head tile sit 512 bytes apart, so a lane reads its B operand with one
     // ds_read2_b64
-    __shared__ uint2 xp[NP][2][2][2][64];
-    __shared__ uint2 xq[NP][2][2][2][64];    // the same after a max change
-    __shared__ float xm[4][32];              // tile max of each owned head
-    __shared__ float xl[4][32];              // softmax sums at the end
-    __shared__ int xf[4];                    // bit 0: a first max, bit 1: a larger max
+    __shared__ uint2 xp[NP][4][2][64];
+    __shared__ uint2 xq[NP][4][2][64];       // the same after a max change
+    __shared__ float xm[NW][16 * JO];        // tile max of each owned head
+    __shared__ float xl[NW][16 * JO];        // softmax sums at the end
+    __shared__ int xf[NW];                   // bit 0: a first max, bit 1: a larger max
 
     // XCD-aware order: consecutive logical blocks (one token's splits, then
     // neighbouring tokens, which share window rows) stay on one XCD.
@@ -202,7 +213,8 @@ void attn_kernel(AttnParams p)
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-    const int dq = w & 1, ch = w >> 1;
+    // S / softmax role: head group gr, head_dim half dq, column half ch
+    const int gr = w >> 2, dq = w & 1, ch = (w >> 1) & 1;
     const int hbase = blockIdx.y * kAttnHeadsPerBlock;
 
     // The block's 64 q rows are staged in the (still unused) first two tiles
@@ -215,10 +227,10 @@ void attn_kernel(AttnParams p)
     uint8_t *const qstage = KV == 0 ? &tiles[2][0] : &tiles[0][0];
     constexpr int QSW = D >= 128 ? 15 : 7;   // chunk swizzle mask (a row has D/8 chunks)
     {
-        constexpr int QI = 64 * 2 * D / 1024 / 4;   // DMA instructions per wave
+        constexpr int QI = 64 * 2 * D / 1024 / NW;   // DMA instructions per wave
 #pragma unroll
         for (int k = 0; k < QI; ++k) {
-            const int u = 4 * k + w;                  // 1 KiB block of the staging area
+            const int u = NW * k + w;                 // 1 KiB block of the staging area
             const int f = 1024 * u + 16 * lane;       // byte of the staging area this lane fills
             const int h = f / (2 * D), c = (f % (2 * D)) / 16;
             const int head = hbase + h < p.H ? hbase + h : hbase;   // rows past H: finite stand-in
@@ -242,9 +254,9 @@ void attn_kernel(AttnParams p)
     // 8w + q*RPI .. + RPI-1; this lane reads row grow(q), chunk slot gpos
     const int32_t *idx_row = p.idx + (int64_t)t * p.idx_st;
     const int gpos = lane % SH::CH;
-    auto grow = [&](int q) __attribute__((always_inline)) { return 8 * w + q * SH::RPI + lane / SH::CH; };
-    Raw raw[SH::NQ];       // e4m3 only: codes of the issued tile, widened when landed
-    float rsc[SH::NQ];
+    auto grow = [&](int q) __attribute__((always_inline)) { return RW * w + q * SH::RPI + lane / SH::CH; };
+    Raw raw[NQW];          // e4m3 only: codes of the issued tile, widened when landed
+    float rsc[NQW];
     int cc = c_begin;      // first column of the current chunk
     int n_tiles = 0;       // tiles of the current chunk
 
@@ -254,21 +266,21 @@ void attn_kernel(AttnParams p)
         int iv[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int i = tid + u * kThreads;
+            const int i = tid + u * NT;
             iv[u] = i < c_end - c_begin ? idx_row[c_begin + i] : -1;
         }
         const int n0 = (min(c_end - c_begin, kIdxChunk) + kAttnTile - 1) / kAttnTile * kAttnTile;
         wait_vm<0>();
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int i = tid + u * kThreads;
+            const int i = tid + u * NT;
             if (i < n0) sidx[i] = iv[u];
         }
     }
     __syncthreads();
     // Q as the B operand of S^T over head_dim half dq, read from the staging
-    // area below: qf[j][s] = q[t, hbase + 16j + l16, D/2*dq + 32s + 8g .. +7]
-    uint4 qf[4][SH::SK];
+    // area below: qf[j][s] = q[t, hbase + 16(JS gr + j) + l16, D/2*dq + 32s + 8g .. +7]
+    uint4 qf[JS][SH::SK];
 
     // issue gather instruction q of tile `tile` (of the current chunk) into
     // buffer `bf`; the row index comes from the staged chunk
@@ -285,7 +297,7 @@ void attn_kernel(AttnParams p)
         const int j = gpos ^ rswz(rho);
         if constexpr (KV == 0) {
             const uint8_t *src = r >= 0 ? base + (int64_t)r * rs + 16 * j : safe_src + 16 * gpos;
-            dma16(src, lds_offset(bf + (8 * w + q * SH::RPI) * 2 * D));
+            dma16(src, lds_offset(bf + (RW * w + q * SH::RPI) * 2 * D));
         } else {
             // unused columns: load the stand-in bytes but keep zero codes,
             // since arbitrary bytes read as e4m3 may be NaN encodings
@@ -298,46 +310,63 @@ void attn_kernel(AttnParams p)
     };
     // the row indices of this wave's 8 rows of a tile, wave-uniform (RPI == 1)
     struct Rows {
-        int r[SH::NQ];
+        int r[NQW];
     };
     auto rows_of = [&](int tile, Rows &rw) __attribute__((always_inline)) {
         if constexpr (SH::RPI == 1) {
-            // two 16-byte LDS reads (the address is wave-uniform)
-            const int4 *src = (const int4 *)(sidx + tile * kAttnTile + 8 * w);
-            const int4 a = src[0], b = src[1];
-            const int v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            // 16-byte LDS reads of the wave's RW indices (wave-uniform address)
+            const int4 *src = (const int4 *)(sidx + tile * kAttnTile + RW * w);
 #pragma unroll
-            for (int q = 0; q < SH::NQ; ++q) rw.r[q] = __builtin_amdgcn_readfirstlane(v[q]);
+            for (int h = 0; h < RW / 4; ++h) {
+                const int4 a = src[h];
+                const int v[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) rw.r[4 * h + q] = __builtin_amdgcn_readfirstlane(v[q]);
+            }
         }
     };
     auto issue = [&](uint8_t *bf, float *meta, int tile) __attribute__((always_inline)) {
         Rows rw;
         rows_of(tile, rw);
 #pragma unroll
-        for (int q = 0; q < SH::NQ; ++q) issue_row(bf, meta, tile, q, rw.r[q]);
+        for (int q = 0; q < NQW; ++q) issue_row(bf, meta, tile, q, rw.r[q]);
     };
     // e4m3: widen the registers of the issued tile into its buffer
     auto land = [&](uint8_t *bf, float *meta) __attribute__((always_inline)) {
         if constexpr (KV == 2) {
             float *scl = meta + kAttnTile;
 #pragma unroll
-            for (int q = 0; q < SH::NQ; ++q) {
-                *(uint4 *)(bf + (8 * w + q * SH::RPI) * 2 * D + 16 * lane) = e4m3x8_to_bf16x8(raw[q]);
+            for (int q = 0; q < NQW; ++q) {
+                *(uint4 *)(bf + (RW * w + q * SH::RPI) * 2 * D + 16 * lane) = e4m3x8_to_bf16x8(raw[q]);
                 if (gpos == 0) scl[grow(q)] = rsc[q];
             }
         }
     };
 
-    // O^T accumulators: acc[m][j] = O^T[d = D/4*w + 16m + 4g + i][head 16j + l16]
-    f32x4 acc[SH::PM][4];
+    // O^T accumulators: acc[m][j] = O^T[d = D/NW*w + 16m + 4g + i][head 16j + l16]
+    f32x4 acc[PMW][4];
 #pragma unroll
-    for (int m = 0; m < SH::PM; ++m)
+    for (int m = 0; m < PMW; ++m)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     // running max of heads 16j + l16 (identical in every wave), and the sum
-    // over this lane's columns of the owned heads 32dq + 16nt + l16
-    float m_run[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    float l_run[2] = {0.0f, 0.0f};
+    // over this lane's columns of the owned heads: tile J = JS gr + JO dq + nt
+    // (a vector value, not an array: no access can turn into an address)
+    f32x4 m_run = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    float l_run[JO];
+#pragma unroll
+    for (int nt = 0; nt < JO; ++nt) l_run[nt] = 0.0f;
+    // the head tile of owned tile nt, and the waves owning head tile j
+    auto own_tile = [&](int nt) __attribute__((always_inline)) { return JS * gr + JO * dq + nt; };
+    auto owner = [](int j) { return 4 * (j / JS) + (j % JS) / JO; };   // its ch = 0 wave; ch = 1 is +2
+    // m_run of the wave-uniform tile index J, through selects of its
+    // elements (an array indexed at run time would live in scratch memory)
+    auto m_of = [&](int J) __attribute__((always_inline)) {
+        float r = m_run[0];
+#pragma unroll
+        for (int k = 1; k < 4; ++k) r = J == k ? m_run[k] : r;
+        return r;
+    };
 
     // LDS byte offsets within a tile.  S reads chunk (D/16)dq + 4s + g of row
     // 16ch + l16; PV reads rows 16h + 4g + l16/4 at head_dim D/4*w + 16m +
@@ -351,24 +380,24 @@ void attn_kernel(AttnParams p)
     }
     // (rows r and r + 16 have the same swizzle, so the second PV row is the
     // first plus a constant)
-    constexpr int VB = SH::PM < 4 ? SH::PM : 4;
+    constexpr int VB = PMW < 4 ? PMW : 4;
     int vb[VB];
     {
         const int dsub = 4 * (l16 & 3);
         const int r = 4 * g + (l16 >> 2), vs = rswz(r);
 #pragma unroll
         for (int mm = 0; mm < VB; ++mm) {
-            const int d = (D / 4) * w + 16 * mm + dsub;
+            const int d = (D / NW) * w + 16 * mm + dsub;
             vb[mm] = r * 2 * D + 16 * ((d >> 3) ^ vs) + 2 * (d & 7);
         }
     }
 
     // --- S^T over head_dim half dq for columns 16ch .. 16ch+15:
-    //     sacc[j] = S^T[col 16ch + 4g + i][head 16j + l16] (partial)
-    auto s_part = [&](const uint8_t *bf, f32x4 (&sacc)[4], int dma_tile, uint8_t *nb2, float *nm2, const Rows &r2,
+    //     sacc[j] = S^T[col 16ch + 4g + i][head 16(JS gr + j) + l16] (partial)
+    auto s_part = [&](const uint8_t *bf, f32x4 (&sacc)[JS], int dma_tile, uint8_t *nb2, float *nm2, const Rows &r2,
                       auto hook) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < JS; ++j) sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         auto kfrag = [&](int s) __attribute__((always_inline)) { return lds_b128(bf + kb[s & 1] + 128 * (s >> 1)); };
         uint4 f[2];   // fragment ring: step s+1 is read while step s multiplies
         f[0] = kfrag(0);
@@ -377,7 +406,7 @@ void attn_kernel(AttnParams p)
             if (s + 1 < SH::SK) f[(s + 1) % 2] = kfrag(s + 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sacc[j] = mfma16x16x32(f[s % 2], qf[j][s], sacc[j]);
+            for (int j = 0; j < JS; ++j) sacc[j] = mfma16x16x32(f[s % 2], qf[j][s], sacc[j]);
             if constexpr (KV == 0) {
                 // GB gathers of tile t+2, at k-steps spread over the loop
                 constexpr int STEP = GB > 0 ? SH::SK / GB : 1;   // GB <= SK: rows at s = STEP-1, 2 STEP-1, ...
@@ -393,11 +422,11 @@ void attn_kernel(AttnParams p)
     // weights of the owned heads against the current max: per head tile nt,
     // 4 columns packed as bf16 (e4m3: NP terms, each the bf16 rounding of
     // what the previous terms left)
-    auto weights = [&](const float (&x)[2][4], const float (&csc)[4], float (&pr)[2][4],
-                       uint2 (&pt)[NP][2]) __attribute__((always_inline)) {
+    auto weights = [&](const float (&x)[JO][4], const float (&csc)[4], float (&pr)[JO][4],
+                       uint2 (&pt)[NP][JO]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const float mr = dq ? m_run[2 + nt] : m_run[nt];
+        for (int nt = 0; nt < JO; ++nt) {
+            const float mr = m_of(own_tile(nt));
             const float msub = mr == -INFINITY ? 0.0f : mr;
 #pragma unroll
             for (int i = 0; i < 4; ++i) pr[nt][i] = fast_exp2(x[nt][i] - msub);
@@ -416,23 +445,23 @@ void attn_kernel(AttnParams p)
             }
         }
     };
-    auto put_p = [&](uint2 (*px)[2][2][2][64], const uint2 (&pt)[NP][2]) __attribute__((always_inline)) {
+    auto put_p = [&](uint2 (*px)[4][2][64], const uint2 (&pt)[NP][JO]) __attribute__((always_inline)) {
 #pragma unroll
         for (int e = 0; e < NP; ++e)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) px[e][dq][nt][ch][lane] = pt[e][nt];
+            for (int nt = 0; nt < JO; ++nt) px[e][own_tile(nt)][ch][lane] = pt[e][nt];
     };
 
-    // --- O^T += V^T P^T for head_dim quarter w; P^T of head tile j comes from
-    //     the owners (j/2, ch = 0) and (j/2, ch = 1)
-    auto pv = [&](const uint8_t *bf, const uint2 (*px)[2][2][2][64], int dma_tile, uint8_t *nb3, float *nm3,
+    // --- O^T += V^T P^T for head_dim range w (D/NW wide); P^T of head tile j
+    //     comes from its two column-half owners
+    auto pv = [&](const uint8_t *bf, const uint2 (*px)[4][2][64], int dma_tile, uint8_t *nb3, float *nm3,
                   const Rows &r3) __attribute__((always_inline)) {
         uint4 pb[NP][4];
 #pragma unroll
         for (int e = 0; e < NP; ++e)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint2 a = px[e][j >> 1][j & 1][0][lane], b = px[e][j >> 1][j & 1][1][lane];
+                const uint2 a = px[e][j][0][lane], b = px[e][j][1][lane];
                 pb[e][j] = make_uint4(a.x, a.y, b.x, b.y);
             }
         auto vfrag = [&](int m) __attribute__((always_inline)) {
@@ -442,10 +471,10 @@ void attn_kernel(AttnParams p)
         };
         uint4 vr[3];
         vr[0] = vfrag(0);
-        if (SH::PM > 1) vr[1] = vfrag(1);
+        if (PMW > 1) vr[1] = vfrag(1);
 #pragma unroll
-        for (int m = 0; m < SH::PM; ++m) {
-            if (m + 2 < SH::PM) vr[(m + 2) % 3] = vfrag(m + 2);
+        for (int m = 0; m < PMW; ++m) {
+            if (m + 2 < PMW) vr[(m + 2) % 3] = vfrag(m + 2);
             __builtin_amdgcn_sched_barrier(0);
             const uint4 a = vr[m % 3];
 #pragma unroll
@@ -458,7 +487,7 @@ void attn_kernel(AttnParams p)
             // m-step, so the memory pipeline fills while the MFMAs run
             if constexpr (KV == 0) {
                 // GA gathers of tile t+3, at m-steps spread over the loop
-                constexpr int STEP = GA > 0 ? SH::PM / GA : 1;   // GA <= PM
+                constexpr int STEP = GA > 0 ? PMW / GA : 1;   // GA <= PMW
                 if (GA > 0 && m % STEP == STEP - 1 && m / STEP < GA && dma_tile < n_tiles)
                     issue_row(nb3, nm3, dma_tile, m / STEP, r3.r[m / STEP]);
             }
@@ -468,54 +497,56 @@ void attn_kernel(AttnParams p)
 
     // softmax inputs of the current tile, kept between the two halves of a step
     struct Soft {
-        float x[2][4], csc[4], psum[2];   // scores, e4m3 scales, sums of this lane's weights
+        float x[JO][4], csc[4], psum[JO];   // scores, e4m3 scales, sums of this lane's weights
     };
 
-    // --- softmax of heads 32dq + 16nt + l16, columns 16ch + 4g + i, in three
-    //     pieces so they can be placed between the MFMAs of the next tile's S
+    // --- softmax of the owned heads (tiles JS gr + JO dq + nt), columns
+    //     16ch + 4g + i, in three pieces so they can be placed between the
+    //     MFMAs of the next tile's S
     // (a) the partner's partial scores and the tile's bias / scales -> scores
-    auto soft_a = [&](const float *cm, const f32x4 (&mine)[2], Soft &st) __attribute__((always_inline)) {
-        const float4 o0 = xs[w ^ 1][0][lane], o1 = xs[w ^ 1][1][lane];
+    auto soft_a = [&](const float *cm, const f32x4 (&mine)[JO], Soft &st) __attribute__((always_inline)) {
         const float4 b4 = *(const float4 *)(cm + 16 * ch + 4 * g);
         const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
         if constexpr (KV == 2) {
             const float4 s4 = *(const float4 *)(cm + kAttnTile + 16 * ch + 4 * g);
             st.csc[0] = s4.x; st.csc[1] = s4.y; st.csc[2] = s4.z; st.csc[3] = s4.w;
         }
-        const float ov[2][4] = {{o0.x, o0.y, o0.z, o0.w}, {o1.x, o1.y, o1.z, o1.w}};
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < JO; ++nt) {
+            const float4 o4 = xs[w ^ 1][nt][lane];
+            const float ov[4] = {o4.x, o4.y, o4.z, o4.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float v = (mine[nt][i] + ov[nt][i]) * sl2;
+                float v = (mine[nt][i] + ov[i]) * sl2;
                 if constexpr (KV == 2) v *= st.csc[i];
                 st.x[nt][i] = v + bb[i];
             }
+        }
     };
     // (b) tile maxima of the owned heads and the flags (bit 0: a first
     //     valid column, bit 1: a max beyond the slack)
-    auto soft_b = [&](const Soft &st, float (&tmax)[2]) __attribute__((always_inline)) {
+    auto soft_b = [&](const Soft &st, float (&tmax)[JO]) __attribute__((always_inline)) {
         int flag = 0;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < JO; ++nt) {
             tmax[nt] = group4_max(fmaxf(fmaxf(st.x[nt][0], st.x[nt][1]), fmaxf(st.x[nt][2], st.x[nt][3])));
-            const float mr = dq ? m_run[2 + nt] : m_run[nt];
+            const float mr = m_of(own_tile(nt));
             if (mr == -INFINITY) flag |= tmax[nt] > -INFINITY ? 1 : 0;
             else flag |= tmax[nt] > mr + kRescaleSlack ? 2 : 0;
         }
         return flag;
     };
     // (c) weights against the current max, published with the maxima and flags
-    auto soft_c = [&](Soft &st, const float (&tmax)[2], int flag) __attribute__((always_inline)) {
-        uint2 pt[NP][2];
-        float pr[2][4];
+    auto soft_c = [&](Soft &st, const float (&tmax)[JO], int flag) __attribute__((always_inline)) {
+        uint2 pt[NP][JO];
+        float pr[JO][4];
         weights(st.x, st.csc, pr, pt);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) st.psum[nt] = (pr[nt][0] + pr[nt][1]) + (pr[nt][2] + pr[nt][3]);
+        for (int nt = 0; nt < JO; ++nt) st.psum[nt] = (pr[nt][0] + pr[nt][1]) + (pr[nt][2] + pr[nt][3]);
         put_p(xp, pt);
         if (g == 0) {
-            xm[w][l16] = tmax[0];
-            xm[w][16 + l16] = tmax[1];
+#pragma unroll
+            for (int nt = 0; nt < JO; ++nt) xm[w][16 * nt + l16] = tmax[nt];
         }
         const int wf = (__builtin_amdgcn_ballot_w64((flag & 1) != 0) ? 1 : 0) |
                        (__builtin_amdgcn_ballot_w64((flag & 2) != 0) ? 2 : 0);
@@ -524,15 +555,13 @@ void attn_kernel(AttnParams p)
 
     // S^T partials of a tile: send the partner's heads, keep mine (register
     // arrays are only indexed by constants; the wave-uniform choice is a select)
-    auto send_scores = [&](const f32x4 (&sacc)[4], f32x4 (&mine)[2]) __attribute__((always_inline)) {
-        f32x4 theirs[2];
+    auto send_scores = [&](const f32x4 (&sacc)[JS], f32x4 (&mine)[JO]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            mine[nt] = dq ? sacc[2 + nt] : sacc[nt];
-            theirs[nt] = dq ? sacc[nt] : sacc[2 + nt];
+        for (int nt = 0; nt < JO; ++nt) {
+            mine[nt] = dq ? sacc[JO + nt] : sacc[nt];
+            const f32x4 th = dq ? sacc[nt] : sacc[JO + nt];
+            xs[w][nt][lane] = make_float4(th[0], th[1], th[2], th[3]);
         }
-        xs[w][0][lane] = make_float4(theirs[0][0], theirs[0][1], theirs[0][2], theirs[0][3]);
-        xs[w][1][lane] = make_float4(theirs[1][0], theirs[1][1], theirs[1][2], theirs[1][3]);
     };
 
     // One tile t, software pipelined: S of tile t+1 on the MFMAs while the
@@ -543,14 +572,14 @@ void attn_kernel(AttnParams p)
     // previous tile).  Gathers: all of tile t+3 (bf16) or tile t+2 (e4m3).
     // Returns the workgroup's combined flags.
     auto front = [&](int tile, const float *cm, const uint8_t *nb1, uint8_t *nb2, float *nm2, uint8_t *nb3,
-                     float *nm3, Soft &st, f32x4 (&mine)[2], Rows &r3) __attribute__((always_inline)) {
+                     float *nm3, Soft &st, f32x4 (&mine)[JO], Rows &r3) __attribute__((always_inline)) {
         const bool more1 = tile + 1 < n_tiles;
         if constexpr (KV == 0) {
             if (tile + 3 < n_tiles) rows_of(tile + 3, r3);
         } else {
             if (tile + 2 < n_tiles) issue(nb2, nm2, tile + 2);   // into registers; landed at the tail
         }
-        float tmax[2];
+        float tmax[JO];
         int flag = 0;
         auto hook = [&](int s) __attribute__((always_inline)) {
             constexpr int SK = SH::SK;
@@ -560,14 +589,14 @@ void attn_kernel(AttnParams p)
                     // the last gathers of tile t+3 (the rest go out in S and PV)
                     if (tile + 3 < n_tiles) {
 #pragma unroll
-                        for (int q = GA + GB; q < SH::NQ; ++q) issue_row(nb3, nm3, tile + 3, q, r3.r[q]);
+                        for (int q = GA + GB; q < NQW; ++q) issue_row(nb3, nm3, tile + 3, q, r3.r[q]);
                     }
                 }
             }
             if (s == (SK - 1) / 2) flag = soft_b(st, tmax);
             if (s == SK - 1) soft_c(st, tmax, flag);
         };
-        f32x4 sacc[4];
+        f32x4 sacc[JS];
         if (more1) {
             s_part(nb1, sacc, tile + 3, nb3, nm3, r3, hook);
         } else {
@@ -575,7 +604,10 @@ void attn_kernel(AttnParams p)
             for (int s = 0; s < SH::SK; ++s) hook(s);   // the same pieces, no S
         }
         __syncthreads();
-        const int any = __builtin_amdgcn_readfirstlane(xf[0] | xf[1] | xf[2] | xf[3]);
+        int any = 0;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) any |= xf[k];
+        any = __builtin_amdgcn_readfirstlane(any);
         if (more1) send_scores(sacc, mine);
         return any;
     };
@@ -586,7 +618,7 @@ void attn_kernel(AttnParams p)
         if constexpr (KV == 0) {
             // only the gathers of tile t+3 (all issued after those of t+2)
             // may stay in flight
-            if (tile + 3 < n_tiles) wait_vm<SH::NQ>();
+            if (tile + 3 < n_tiles) wait_vm<NQW>();
             else wait_vm<0>();
         } else {
             wait_vm<0>();
@@ -603,7 +635,8 @@ void attn_kernel(AttnParams p)
         if (any) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float mt = fmaxf(xm[j >> 1][16 * (j & 1) + l16], xm[(j >> 1) + 2][16 * (j & 1) + l16]);
+                const int ow = owner(j), oi = 16 * ((j % JS) % JO) + l16;
+                const float mt = fmaxf(xm[ow][oi], xm[ow + 2][oi]);
                 const float mr = m_run[j];
                 if constexpr (RESCALE) {
                     const bool up = mt > mr + kRescaleSlack;   // also from -inf
@@ -612,26 +645,28 @@ void attn_kernel(AttnParams p)
                     m_run[j] = m_new;
                     if (__builtin_amdgcn_ballot_w64(up && mr != -INFINITY) != 0) {
 #pragma unroll
-                        for (int m = 0; m < SH::PM; ++m) acc[m][j] *= alpha;
+                        for (int m = 0; m < PMW; ++m) acc[m][j] *= alpha;
                     }
-                    if ((j >> 1) == dq) l_run[j & 1] *= alpha;
+#pragma unroll
+                    for (int nt = 0; nt < JO; ++nt)
+                        if (own_tile(nt) == j) l_run[nt] *= alpha;
                 } else {
                     // only first maxima here: O and the sums of such a head
                     // are still zero, nothing to rescale
                     if (mr == -INFINITY && mt > -INFINITY) m_run[j] = mt;
                 }
             }
-            uint2 pt[NP][2];
-            float pr[2][4];
+            uint2 pt[NP][JO];
+            float pr[JO][4];
             weights(st.x, st.csc, pr, pt);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) st.psum[nt] = (pr[nt][0] + pr[nt][1]) + (pr[nt][2] + pr[nt][3]);
+            for (int nt = 0; nt < JO; ++nt) st.psum[nt] = (pr[nt][0] + pr[nt][1]) + (pr[nt][2] + pr[nt][3]);
             put_p(xq, pt);
             __syncthreads();
         }
         pv(cb, any ? xq : xp, dma_tile, nb3, nm3, r3);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) l_run[nt] += st.psum[nt];
+        for (int nt = 0; nt < JO; ++nt) l_run[nt] += st.psum[nt];
     };
 
     // bf16: the first chunk's first two tiles go out now; their gathers are
@@ -643,13 +678,14 @@ void attn_kernel(AttnParams p)
         if (n_tiles > 1) issue(tiles[1], metas[1], 1);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const bool ok = hbase + 16 * j + l16 < p.H;
-        const uint8_t *row = qstage + (16 * j + l16) * 2 * D;
+    for (int j = 0; j < JS; ++j) {
+        const int hr = 16 * (JS * gr + j) + l16;   // staging row (head within the block)
+        const bool ok = hbase + hr < p.H;
+        const uint8_t *row = qstage + hr * 2 * D;
 #pragma unroll
         for (int s = 0; s < SH::SK; ++s) {
             const int c = (D / 16) * dq + 4 * s + g;
-            qf[j][s] = ok ? *(const uint4 *)(row + 16 * (c ^ (l16 & QSW))) : make_uint4(0, 0, 0, 0);
+            qf[j][s] = ok ? *(const uint4 *)(row + 16 * (c ^ (hr & QSW))) : make_uint4(0, 0, 0, 0);
         }
     }
 
@@ -663,16 +699,16 @@ void attn_kernel(AttnParams p)
         // four loads in flight per thread before their stores (up to 1024
         // columns per memory round trip)
         // (the first 4 x 256 of the first chunk were staged with q)
-        for (int i0 = cc == c_begin ? 4 * kThreads : 0; i0 < n_tiles * kAttnTile; i0 += 4 * kThreads) {
+        for (int i0 = cc == c_begin ? 4 * NT : 0; i0 < n_tiles * kAttnTile; i0 += 4 * NT) {
             int iv[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int i = i0 + tid + u * kThreads;
+                const int i = i0 + tid + u * NT;
                 iv[u] = i < cn ? idx_row[cc + i] : -1;
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int i = i0 + tid + u * kThreads;
+                const int i = i0 + tid + u * NT;
                 if (i < n_tiles * kAttnTile) sidx[i] = iv[u];
             }
         }
@@ -699,10 +735,10 @@ void attn_kernel(AttnParams p)
             wait_vm<0>();
         }
         __syncthreads();
-        f32x4 mine[2];
+        f32x4 mine[JO];
         {
             Rows none;
-            f32x4 sacc[4];
+            f32x4 sacc[JS];
             s_part(tiles[0], sacc, -1, tiles[0], metas[0], none, [](int) {});
             send_scores(sacc, mine);
         }
@@ -747,7 +783,7 @@ void attn_kernel(AttnParams p)
     // softmax sums: owners reduce over their columns, everyone adds the two
     // column halves of each head in a fixed order
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < JO; ++nt) {
         const float ls = group4_sum(l_run[nt]);
         if (g == 0) xl[w][16 * nt + l16] = ls;
     }
@@ -755,22 +791,23 @@ void attn_kernel(AttnParams p)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int head = hbase + 16 * j + l16;
-        const float l_tot = xl[j >> 1][16 * (j & 1) + l16] + xl[(j >> 1) + 2][16 * (j & 1) + l16];
+        const int ow = owner(j), oi = 16 * ((j % JS) % JO) + l16;
+        const float l_tot = xl[ow][oi] + xl[ow + 2][oi];
         if (head >= p.H) continue;
-        const int d0 = (D / 4) * w + 4 * g;
+        const int d0 = (D / NW) * w + 4 * g;
         if (p.num_splits == 1) {
             const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
             if constexpr (OUT == 1) {
                 float *o = (float *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d0;
 #pragma unroll
-                for (int m = 0; m < SH::PM; ++m) {
+                for (int m = 0; m < PMW; ++m) {
                     const f32x4 v = acc[m][j] * inv;
                     *(float4 *)(o + 16 * m) = make_float4(v[0], v[1], v[2], v[3]);
                 }
             } else {
                 uint16_t *o = (uint16_t *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d0;
 #pragma unroll
-                for (int m = 0; m < SH::PM; ++m) {
+                for (int m = 0; m < PMW; ++m) {
                     const f32x4 v = acc[m][j] * inv;
                     *(uint2 *)(o + 16 * m) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
                 }
@@ -780,10 +817,10 @@ void attn_kernel(AttnParams p)
             // [t][split][head block][w][m][j][lane] x 4 floats: each store
             // instruction writes 1 KiB of consecutive bytes
             const int64_t slot = ((int64_t)t * p.num_splits + split) * p.H + head;
-            const int64_t pb = (((int64_t)t * p.num_splits + split) * gridDim.y + blockIdx.y) * 4 + w;
+            const int64_t pb = (((int64_t)t * p.num_splits + split) * gridDim.y + blockIdx.y) * NW + w;
 #pragma unroll
-            for (int m = 0; m < SH::PM; ++m)
-                *(float4 *)(p.part_o + (((pb * SH::PM + m) * 4 + j) * 64 + lane) * 4) =
+            for (int m = 0; m < PMW; ++m)
+                *(float4 *)(p.part_o + (((pb * PMW + m) * 4 + j) * 64 + lane) * 4) =
                     make_float4(acc[m][j][0], acc[m][j][1], acc[m][j][2], acc[m][j][3]);
             if (g == 0 && w == 0) *(float2 *)(p.part_ml + slot * 2) = make_float2(m_run[j], l_tot);
         }
@@ -793,26 +830,27 @@ void attn_kernel(AttnParams p)
 // out[t, h, :] = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j over the splits
 // j in order; zero when every split was empty.  The partial outputs are in
 // the split kernel's accumulator layout [t][split][head block][w][m][j][lane]
-// x 4 floats: one wave of this kernel takes one (head block, w, m, j) group,
-// lane l owning head 16j + l%16 and head_dim 16m + 4(l/16) .. +3 of quarter w,
+// x 4 floats (NW split-kernel waves): one wave of this kernel takes one
+// (head block, w, m, j) group, lane l owning head 16j + l%16 and head_dim
+// 16m + 4(l/16) .. +3 of the split wave's range w,
 // so its partial loads are 1 KiB contiguous per split.  The loads of up to 16
 // splits are issued before any is used (one memory round trip at the usual
 // split counts).
-template <int D, int OUT>
+template <int D, int OUT, int NW>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p)
 {
     constexpr int U = 16;
-    constexpr int PM = D / 64;
+    constexpr int PM = D / (16 * NW);   // the split kernel's m-steps per wave
     const int t = blockIdx.x;
     const int grp = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int HB = (p.H + kAttnHeadsPerBlock - 1) / kAttnHeadsPerBlock;
-    if (grp >= HB * 4 * PM * 4) return;
-    const int j = grp % 4, m = (grp / 4) % PM, w = (grp / (4 * PM)) % 4, hb = grp / (16 * PM);
+    if (grp >= HB * NW * PM * 4) return;
+    const int j = grp % 4, m = (grp / 4) % PM, w = (grp / (4 * PM)) % NW, hb = grp / (4 * NW * PM);
     const int head = hb * kAttnHeadsPerBlock + 16 * j + (lane & 15);
     if (head >= p.H) return;
-    const int d = (D / 4) * w + 16 * m + 4 * (lane >> 4);
+    const int d = (D / NW) * w + 16 * m + 4 * (lane >> 4);
     const int S = p.num_splits;
-    const int64_t pstride = (int64_t)HB * 4 * PM * 4 * 64;   // float4 slots per split
+    const int64_t pstride = (int64_t)HB * NW * PM * 4 * 64;   // float4 slots per split
     const float4 *po = (const float4 *)p.part_o + ((int64_t)t * S) * pstride + (int64_t)grp * 64 + lane;
     const float2 *pml = (const float2 *)p.part_ml + ((int64_t)t * S) * p.H + head;
     // one pass: each batch's (max, sum) and partial loads go out together and
@@ -858,8 +896,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p)
 template <int D, int KV, int OUT>
 hipError_t launch_attn_t(const AttnParams &p, hipStream_t s)
 {
+    constexpr int NW = attn_waves(D, KV);
     const dim3 grid((unsigned)(p.T * p.num_splits), (unsigned)((p.H + kAttnHeadsPerBlock - 1) / kAttnHeadsPerBlock));
-    hipLaunchKernelGGL((attn_kernel<D, KV, OUT>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attn_kernel<D, KV, OUT, NW>), grid, dim3(64 * NW), 0, s, p);
     return hipGetLastError();
 }
 
@@ -870,15 +909,22 @@ hipError_t launch_attn_d(const AttnParams &p, int kv, int out, hipStream_t s)
     return out == 1 ? launch_attn_t<D, 2, 1>(p, s) : launch_attn_t<D, 2, 0>(p, s);
 }
 
-template <int D>
-hipError_t launch_merge_d(const AttnParams &p, int out, hipStream_t s)
+template <int D, int NW>
+hipError_t launch_merge_t(const AttnParams &p, int out, hipStream_t s)
 {
     // one wave per (head block, w, m, j) group of the partial layout
     const int HB = (p.H + kAttnHeadsPerBlock - 1) / kAttnHeadsPerBlock;
-    const dim3 grid((unsigned)p.T, (unsigned)(HB * (D / 64) * 4));
-    if (out == 1) hipLaunchKernelGGL((attn_merge_kernel<D, 1>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((attn_merge_kernel<D, 0>), grid, dim3(256), 0, s, p);
+    // (HB * NW * PMW * 4 groups, 4 per workgroup; NW * PMW = D / 16)
+    const dim3 grid((unsigned)p.T, (unsigned)(HB * (D / 16)));
+    if (out == 1) hipLaunchKernelGGL((attn_merge_kernel<D, 1, NW>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((attn_merge_kernel<D, 0, NW>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_merge_d(const AttnParams &p, int kv, int out, hipStream_t s)
+{
+    return attn_waves(D, kv) == 8 ? launch_merge_t<D, 8>(p, out, s) : launch_merge_t<D, 4>(p, out, s);
 }
 
 }  // namespace
@@ -894,13 +940,13 @@ hipError_t launch_attn(const AttnParams &p, int D, int kv, int out, hipStream_t 
     }
 }
 
-hipError_t launch_attn_merge(const AttnParams &p, int D, int out, hipStream_t s)
+hipError_t launch_attn_merge(const AttnParams &p, int D, int kv, int out, hipStream_t s)
 {
     switch (D) {
-    case 64: return launch_merge_d<64>(p, out, s);
-    case 128: return launch_merge_d<128>(p, out, s);
-    case 256: return launch_merge_d<256>(p, out, s);
-    case 512: return launch_merge_d<512>(p, out, s);
+    case 64: return launch_merge_d<64>(p, kv, out, s);
+    case 128: return launch_merge_d<128>(p, kv, out, s);
+    case 256: return launch_merge_d<256>(p, kv, out, s);
+    case 512: return launch_merge_d<512>(p, kv, out, s);
     default: return hipErrorInvalidValue;
     }
 }

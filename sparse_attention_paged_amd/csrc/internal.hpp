@@ -32,7 +32,10 @@ struct AttnParams {
 
 // kv: 0 = bf16, 2 = e4m3.  out: 0 = bf16, 1 = f32.
 hipError_t launch_attn(const AttnParams &p, int D, int kv, int out_dtype, hipStream_t s);
-hipError_t launch_attn_merge(const AttnParams &p, int D, int out_dtype, hipStream_t s);
+hipError_t launch_attn_merge(const AttnParams &p, int D, int kv, int out_dtype, hipStream_t s);
+// waves per attention workgroup: 8 (two head groups, two waves per SIMD)
+// for bf16 rows at head_dim 512, else 4; the split partials follow its layout
+constexpr int attn_waves(int D, int kv) { return D == 512 && kv == 0 ? 8 : 4; }
 
 struct IndexerParams {
     const uint16_t *q;               // bf16 [B, Hi, 128]

@@ -197,7 +197,7 @@ int sap_sparse_attn_paged(const void *q, sap_dtype q_dtype, int64_t q_stride_t, 
     const int kv = kv_dtype == SAP_FP8_E4M3 ? 2 : 0;
     const int od = out_dtype == SAP_F32 ? 1 : 0;
     hipError_t e = sap::launch_attn(p, D, kv, od, (hipStream_t)stream);
-    if (e == hipSuccess && sp.splits > 1) e = sap::launch_attn_merge(p, D, od, (hipStream_t)stream);
+    if (e == hipSuccess && sp.splits > 1) e = sap::launch_attn_merge(p, D, kv, od, (hipStream_t)stream);
     return launched(e);
 }
 
