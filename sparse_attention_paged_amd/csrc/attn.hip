@@ -196,7 +196,7 @@ void attn_kernel(AttnParams p)
     __shared__ uint2 xq[NP][4][2][64];       // the same after a max change
     __shared__ float xm[NW][16 * JO];        // tile max of each owned head
     __shared__ float xl[NW][16 * JO];        // softmax sums at the end
-    __shared__ int xf[NW];                   // bit 0: a first max, bit 1: a larger max
+    __shared__ __attribute__((aligned(16))) int xf[NW];   // bit 0: a first max, bit 1: a larger max
 
     // XCD-aware order: consecutive logical blocks (one token's splits, then
     // neighbouring tokens, which share window rows) stay on one XCD.
@@ -604,9 +604,13 @@ void attn_kernel(AttnParams p)
             for (int s = 0; s < SH::SK; ++s) hook(s);   // the same pieces, no S
         }
         __syncthreads();
+        // the waves' flags in 16-byte reads
         int any = 0;
 #pragma unroll
-        for (int k = 0; k < NW; ++k) any |= xf[k];
+        for (int k = 0; k < NW / 4; ++k) {
+            const int4 f4 = ((const int4 *)xf)[k];
+            any |= f4.x | f4.y | f4.z | f4.w;
+        }
         any = __builtin_amdgcn_readfirstlane(any);
         if (more1) send_scores(sacc, mine);
         return any;
