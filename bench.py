@@ -188,6 +188,16 @@ def roofline(bound, achieved, peak, unit, traffic=None):
             "frac": round(achieved / peak, 5), "traffic": traffic}
 
 
+# the pages' attention shapes ("perf(kernel): keep 16-byte kv loads ...", All
+# shapes): H100 80GB time of the final Triton kernel, as context only
+PAGES_H100_US = {
+    "prefill_s2048_r4": 2887.86, "prefill_s8192_r4": 11399.31, "prefill_s4096_at28672_r4": 5762.74,
+    "prefill_s8192_r128": 3672.89, "prefill_s8192_r0": 2561.59,
+    "decode_b1_r4": 16.83, "decode_b1_r128": 15.98, "decode_b1_r0": 13.37,
+    "decode_b8_r4": 20.81, "decode_b8_r128": 17.73, "decode_b8_r0": 13.89,
+}
+
+
 def prefill_secondary(iters, kv="bf16"):
     if kv == "e4m3":
         case = W.prefill_case(T=8192, ratio=4, kv_dtype="e4m3", q_scale=2.0 ** -7, seed=W.SEED_BASE + 35)
@@ -207,7 +217,8 @@ def prefill_secondary(iters, kv="bf16"):
     tf = flops / (ms * 1e-3) / 1e12
     key = f"prefill_s8192_r4_{kv}"
     # e4m3 rows are widened to bf16 tiles: the MFMAs are bf16 (P as three bf16 terms triples PV)
-    return {"workload": key, "us": round(ms * 1e3, 2), "tflops": round(tf, 2),
+    ctx = {"pages_h100_us": PAGES_H100_US["prefill_s8192_r4"]} if kv == "bf16" else {}
+    return {"workload": key, "us": round(ms * 1e3, 2), "tflops": round(tf, 2), **ctx,
             "gflop": round(flops / 1e9, 2),
             "roofline": roofline("mfma", tf, BF16_PEAK_TFLOPS, "TFLOP/s", traffic=counted_traffic(key))}
 
@@ -218,10 +229,44 @@ def decode_secondary(B, kv, iters):
     ms_attn = time_graph(st.attend, iters // GRAPH_CALLS, 1, GRAPH_CALLS)
     ms_step = time_graph(st.step, iters // GRAPH_CALLS, 1, GRAPH_CALLS)
     gb = st.attn_alg_bytes() / (ms_attn * 1e-3) / 1e9
-    return {"workload": f"decode_b{B}_pos32767_r4_{kv}", "attn_us": round(ms_attn * 1e3, 2),
+    ctx = {"pages_h100_us": PAGES_H100_US[f"decode_b{B}_r4"]} if kv == "bf16" else {}
+    return {"workload": f"decode_b{B}_pos32767_r4_{kv}", "attn_us": round(ms_attn * 1e3, 2), **ctx,
             "step_us": round(ms_step * 1e3, 2),
             "gathered_GBs_attn": round(st.gathered_bytes() / (ms_attn * 1e-3) / 1e9, 1),
             "splits": st.splits, "roofline": roofline("hbm", gb, HBM_PEAK_GBS, "GB/s")}
+
+
+def pages_shapes_secondary(iters):
+    """Attention alone (split-K + merge for decode) at every shape of the
+    pages' table, bf16 pools, fp32 output."""
+    d = torch.device("cuda")
+    res = []
+    for name, (T, start, ratio) in (("prefill_s2048_r4", (2048, 0, 4)), ("prefill_s4096_at28672_r4", (4096, 28672, 4)),
+                                    ("prefill_s8192_r128", (8192, 0, 128)), ("prefill_s8192_r0", (8192, 0, 0))):
+        case = W.prefill_case(T=T, start=start, ratio=ratio)
+        q, win = case.q.to(d), case.win_pool.to(d)
+        cmp = case.cmp_pool.to(d) if case.n_cmp > 0 else None
+        idx = sap.build_sparse_idx(case.pos.to(d), case.seq.to(d), case.n_win, case.win_pt.to(d), case.page,
+                                   case.cmp_logical.to(d) if case.n_cmp > 0 else None,
+                                   case.cmp_pt.to(d) if case.n_cmp > 0 else None)
+        out = torch.empty((case.T, 64, 512), dtype=torch.float32, device=d)
+        valid = (idx >= 0).sum().item()
+        ms = time_loop(lambda: sap.sparse_attn_paged(q, win, cmp, idx, case.n_win, case.sm_scale, out=out,
+                                                     num_splits=1), iters, 2)
+        tf = valid * 64 * 512 * 4.0 / (ms * 1e-3) / 1e12
+        res.append({"workload": name, "us": round(ms * 1e3, 2), "tflops": round(tf, 2),
+                    "pages_h100_us": PAGES_H100_US[name],
+                    "roofline": roofline("mfma", tf, BF16_PEAK_TFLOPS, "TFLOP/s")})
+    for B in (1, 8):
+        for ratio in (128, 0):
+            st = DecodeStep(B=B, ratio=ratio)
+            st.select()
+            ms = time_graph(st.attend, 100 // GRAPH_CALLS, 1, GRAPH_CALLS)
+            name = f"decode_b{B}_r{ratio}"
+            res.append({"workload": name + "_pos32767_bf16", "attn_us": round(ms * 1e3, 2),
+                        "pages_h100_us": PAGES_H100_US[name], "splits": st.splits,
+                        "roofline": roofline("hbm", st.attn_alg_bytes() / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s")})
+    return res
 
 
 def indexer_secondary(B, iters):
@@ -345,6 +390,8 @@ def main():
         "timing": f"HIP-graph replays ({GRAPH_CALLS} steps per graph), HIP events around the timed replays",
         "eager_ms_per_step": round(ms_step_eager, 5),
         "attn_us": round(ms_attn * 1e3, 3), "select_us": round(ms_sel * 1e3, 3), "splits": st.splits,
+        "context": {"pages_h100_attn_us": PAGES_H100_US["decode_b1_r4"],
+                    "note": "the pages' H100 Triton time for this attention call alone; another machine"},
         "roofline": roofline("hbm", attn_gbs, HBM_PEAK_GBS, "GB/s",
                              traffic=counted_traffic("decode_b1_r4_bf16_attention_pair")),
     }
@@ -371,6 +418,8 @@ def main():
         for B, R in ((1, 128), (8, 128), (8, 8)):
             log(f"secondary: gated pool B{B} R{R} D512")
             sec.append(gated_pool_secondary(B, R, 512, 100))
+        log("secondary: the pages' other attention shapes")
+        sec.extend(pages_shapes_secondary(5))
         res["secondary"] = sec
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the same decode step")

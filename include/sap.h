@@ -104,7 +104,9 @@ int sap_build_sparse_idx(const int32_t *pos, const int32_t *seq, int T, int n_wi
  *           offset are fine when they keep that alignment.
  * win_scale, cmp_scale: [Nw], [Nc] fp32 per-row scales; required for
  *           SAP_FP8_E4M3 (the pool that has columns), ignored otherwise.
- * idx:      [T, n_win + n_cmp] int32 physical rows, row stride idx_stride.
+ * idx:      [T, n_win + n_cmp] int32 physical rows (below 2^31 - 1), -1 =
+ *           no column; row stride idx_stride.  Columns marked -1 cost no
+ *           gather or MFMA work.
  * out:      [T, H, D] of out_dtype (SAP_F32 or SAP_BF16), strides
  *           out_stride_t, out_stride_h; 16-byte aligned like q.
  * D:        64, 128, 256 or 512.  H >= 1.  n_win + n_cmp <= 65536.

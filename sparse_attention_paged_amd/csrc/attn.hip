@@ -188,6 +188,7 @@ void attn_kernel(AttnParams p)
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[DEPTH][SH::TILE_BYTES];
     __shared__ __attribute__((aligned(16))) float metas[DEPTH][2 * kAttnTile];
     __shared__ __attribute__((aligned(16))) int sidx[kIdxChunk];
+    __shared__ int xscan[NW];                // wave totals of the column compaction
     __shared__ float4 xs[NW][JO][64];        // partial scores for the partner wave
     // bf16 P by [term][head tile][ch][lane]: the two column halves of one
     // head tile sit 512 bytes apart, so a lane reads its B operand with one
@@ -260,22 +261,56 @@ void attn_kernel(AttnParams p)
     int cc = c_begin;      // first column of the current chunk
     int n_tiles = 0;       // tiles of the current chunk
 
-    // row indices of the first 4 x 256 columns, loaded while q lands and
-    // staged for the first chunk
+    // Column staging: a chunk's valid columns are packed to the front of sidx
+    // in column order, so tiles of unused (-1) columns are never gathered or
+    // scored; each entry is its pool row, with bit 31 set for the compressed
+    // pool, and -1 pads the last tile.  Each thread takes 4 consecutive
+    // columns per batch of 4 NT.
+    int nval = 0;   // columns of the current chunk staged so far
+    auto load4 = [&](int cbase, int cn, int i0, int (&iv)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + 4 * tid + u;
+            iv[u] = i < cn ? idx_row[cbase + i] : -1;
+        }
+    };
+    auto stage4 = [&](int cbase, int i0, const int (&iv)[4]) __attribute__((always_inline)) {
+        int cnt = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cnt += iv[u] >= 0 ? 1 : 0;
+        const int incl = wave_incl_sum(cnt);
+        if (lane == 63) xscan[w] = incl;
+        __syncthreads();
+        int before = 0, tot = 0;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) {
+            const int v = xscan[k];
+            before += k < w ? v : 0;
+            tot += v;
+        }
+        int at = nval + before + incl - cnt;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (iv[u] >= 0) {
+                const bool win = cbase + i0 + 4 * tid + u < n_win;
+                sidx[at++] = win ? iv[u] : (int)((uint32_t)iv[u] | 0x80000000u);
+            }
+        }
+        nval += tot;
+        __syncthreads();   // xscan is rewritten by the next batch
+    };
+    auto pad = [&]() __attribute__((always_inline)) {
+        n_tiles = (nval + kAttnTile - 1) / kAttnTile;
+        for (int i = nval + tid; i < n_tiles * kAttnTile; i += NT) sidx[i] = -1;
+    };
+    // the first batch of the first chunk loads while q lands
+    const int cn0 = min(c_end - c_begin, kIdxChunk);
     {
         int iv[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = tid + u * NT;
-            iv[u] = i < c_end - c_begin ? idx_row[c_begin + i] : -1;
-        }
-        const int n0 = (min(c_end - c_begin, kIdxChunk) + kAttnTile - 1) / kAttnTile * kAttnTile;
+        load4(c_begin, cn0, 0, iv);
         wait_vm<0>();
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = tid + u * NT;
-            if (i < n0) sidx[i] = iv[u];
-        }
+        stage4(c_begin, 0, iv);
+        if (cn0 <= 4 * NT) pad();   // the whole first chunk is staged
     }
     __syncthreads();
     // Q as the B operand of S^T over head_dim half dq, read from the staging
@@ -289,24 +324,25 @@ void attn_kernel(AttnParams p)
     // read); otherwise each lane reads its own row's index here
     auto issue_row = [&](uint8_t *bf, float *meta, int tile, int q, int rr) __attribute__((always_inline)) {
         const int rho = grow(q);
-        const int c = cc + tile * kAttnTile + rho;
-        const int r = SH::RPI == 1 ? rr : sidx[tile * kAttnTile + rho];
-        const bool win = c < n_win;
+        const int e = SH::RPI == 1 ? rr : sidx[tile * kAttnTile + rho];   // staged entry
+        const bool ok = e != -1;
+        const bool win = e >= 0;
+        const int r = e & 0x7FFFFFFF;
         const uint8_t *base = win ? win_pool : cmp_pool;
         const int64_t rs = win ? win_rs : cmp_rs;
         const int j = gpos ^ rswz(rho);
         if constexpr (KV == 0) {
-            const uint8_t *src = r >= 0 ? base + (int64_t)r * rs + 16 * j : safe_src + 16 * gpos;
+            const uint8_t *src = ok ? base + (int64_t)r * rs + 16 * j : safe_src + 16 * gpos;
             dma16(src, lds_offset(bf + (RW * w + q * SH::RPI) * 2 * D));
         } else {
             // unused columns: load the stand-in bytes but keep zero codes,
             // since arbitrary bytes read as e4m3 may be NaN encodings
-            const uint8_t *src = r >= 0 ? base + (int64_t)r * rs + 8 * j : safe_src + 8 * gpos;
+            const uint8_t *src = ok ? base + (int64_t)r * rs + 8 * j : safe_src + 8 * gpos;
             const Raw v = *(const Raw *)src;
-            raw[q] = r >= 0 ? v : Raw{0u, 0u};
-            rsc[q] = r >= 0 ? (win ? win_scale : cmp_scale)[r] : 0.0f;
+            raw[q] = ok ? v : Raw{0u, 0u};
+            rsc[q] = ok ? (win ? win_scale : cmp_scale)[r] : 0.0f;
         }
-        if (gpos == 0) meta[rho] = r >= 0 ? 0.0f : -INFINITY;
+        if (gpos == 0) meta[rho] = ok ? 0.0f : -INFINITY;
     };
     // the row indices of this wave's 8 rows of a tile, wave-uniform (RPI == 1)
     struct Rows {
@@ -675,9 +711,8 @@ void attn_kernel(AttnParams p)
 
     // bf16: the first chunk's first two tiles go out now; their gathers are
     // in flight while the q fragments are read
-    const bool early = KV == 0 && c_end > c_begin;
+    const bool early = KV == 0 && c_end > c_begin && cn0 <= 4 * NT && n_tiles > 0;
     if (early) {
-        n_tiles = (min(c_end - c_begin, kIdxChunk) + kAttnTile - 1) / kAttnTile;
         issue(tiles[0], metas[0], 0);
         if (n_tiles > 1) issue(tiles[1], metas[1], 1);
     }
@@ -698,28 +733,21 @@ void attn_kernel(AttnParams p)
     // columns are taken in chunks whose row indices are staged in LDS
     for (; cc < c_end; cc += kIdxChunk) {
         const int cn = min(c_end - cc, kIdxChunk);
-        n_tiles = (cn + kAttnTile - 1) / kAttnTile;
+        const bool first = cc == c_begin;
         __syncthreads();   // the previous chunk's indices are no longer read
-        // four loads in flight per thread before their stores (up to 1024
-        // columns per memory round trip)
-        // (the first 4 x 256 of the first chunk were staged with q)
-        for (int i0 = cc == c_begin ? 4 * NT : 0; i0 < n_tiles * kAttnTile; i0 += 4 * NT) {
+        if (!first) nval = 0;
+        // (the first 4 NT columns of the first chunk were staged with q)
+        for (int i0 = first ? 4 * NT : 0; i0 < cn; i0 += 4 * NT) {
             int iv[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = i0 + tid + u * NT;
-                iv[u] = i < cn ? idx_row[cc + i] : -1;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = i0 + tid + u * NT;
-                if (i < n_tiles * kAttnTile) sidx[i] = iv[u];
-            }
+            load4(cc, cn, i0, iv);
+            stage4(cc, i0, iv);
         }
+        if (!(first && cn <= 4 * NT)) pad();
         // a wait the compiler sees: Q and the index loads are complete, so no
         // wait for them is left inside the tile loops (s_waitcnt vmcnt(0))
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
+        if (n_tiles == 0) continue;   // no valid column in this chunk
         // prologue: tiles 0 and 1 in LDS (bf16: tile 2 too), S of tile 0 and
         // its partial-score exchange (the first chunk's tiles 0 and 1 went
         // out with the q fragments; the barrier above also freed tile 2,
