@@ -35,7 +35,7 @@ hipError_t launch_attn(const AttnParams &p, int D, int kv, int out_dtype, hipStr
 hipError_t launch_attn_merge(const AttnParams &p, int D, int kv, int out_dtype, hipStream_t s);
 // waves per attention workgroup: 8 (two head groups, two waves per SIMD)
 // for bf16 rows at head_dim 512, else 4; the split partials follow its layout
-constexpr int attn_waves(int D, int kv) { return D == 512 && kv == 0 ? 8 : 4; }
+constexpr int attn_waves(int D, int kv) { return D == 512 ? 8 : 4; }
 
 struct IndexerParams {
     const uint16_t *q;               // bf16 [B, Hi, 128]
