@@ -49,9 +49,10 @@ def check_no_scratch(remarks: str) -> None:
             name = m.group(1)
             continue
         m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
-        if m and name and "attn_kernel" in name and int(m.group(1)) > 0:
-            # kernel template <D, KV, OUT>: KV == 0 is bf16 (mangled ...ILi<D>ELi0E...)
-            if re.search(r"attn_kernelILi\d+ELi0E", name):
+        if m and name and int(m.group(1)) > 0:
+            # attn_kernel<D, KV, OUT, NW>: KV == 0 is bf16 (mangled ...ILi<D>ELi0E...);
+            # attn_d512_kernel is bf16 only
+            if re.search(r"attn_kernelILi\d+ELi0E", name) or "attn_d512_kernel" in name:
                 raise RuntimeError(f"{name} uses scratch memory ({m.group(1)} bytes/lane); "
                                    "its gather wait counts would be wrong")
 
@@ -65,7 +66,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     def compile_one(src):
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
         cmd = [cc, *FLAGS, "-c", src, "-o", obj]
-        guard = os.path.basename(src) == "attn.hip"
+        guard = os.path.basename(src) in ("attn.hip", "attn_d512.hip")
         if guard:
             cmd.append("-Rpass-analysis=kernel-resource-usage")
         if verbose:

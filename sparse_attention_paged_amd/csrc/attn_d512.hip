@@ -1,0 +1,567 @@
+// attn_d512.hip -- top-k sparse attention over bf16 pools at head_dim 512,
+// one workgroup barrier per 32-column tile.
+//
+// What is computed is the same as in attn.hip ("perf(kernel): keep 16-byte kv
+// loads in dsv4 sparse attention and unroll gated pool", Call paths / Kernel
+// time): query token t's H heads share one KV head and attend to the columns
+// of idx[t, :]; column c reads one row of the window pool (c < n_win) or of
+// the compressed pool, and that row is both key and value.
+//
+// One workgroup = 4 waves, one per SIMD with up to 512 registers each, =
+// up to 64 heads of one token over all of its columns (one split per token:
+// the prefill launch), in tiles of 32 columns:
+//  - S: wave w = (hg, cs) = (w & 1, w >> 1) computes S^T = K Q^T for columns
+//    16cs .. 16cs+15 and heads 32hg .. 32hg+31 over all 512 dims on MFMA
+//    16x16x32 bf16; its 32 heads' Q fragments stay in 128 registers, so no
+//    partial score crosses waves.
+//  - softmax (log2 domain): the same wave owns those scores.  Its weights go
+//    to LDS as bf16 in the PV B-operand layout, double-buffered by tile
+//    parity.  The running max of a head only moves when a tile's max exceeds
+//    it by more than 32 (weights stay <= 2^32); the first tile of a column
+//    range, and any later tile whose max went past the slack, take a slow
+//    path in which every wave agrees on the new maxima, O and the sums are
+//    rescaled and the weights of that tile are rewritten.
+//  - PV: wave w computes O^T = V^T P^T for head_dim 128w .. 128w+127 and all
+//    64 heads (128 accumulators); the V^T operand is read from the row-major
+//    tile with ds_read_b64_tr_b16.
+//  - pipeline: iteration i issues the gathers of tile i+3, computes S of tile
+//    i+1, then PV of tile i with the softmax of tile i+1 placed between its
+//    MFMAs, and ends with the one barrier that publishes tile i+1's weights
+//    and tile i+2's rows.
+//  - gathers: each wave moves 8 rows of a tile straight into LDS
+//    (global_load_lds_dwordx4 with a scalar row base and a per-lane 32-bit
+//    offset; one instruction = one 1 KiB row); the 8 row bases come from one
+//    LDS read and a few vector instructions per tile.
+#include "common.hpp"
+#include "internal.hpp"
+#include "attn_common.hpp"
+
+#include <type_traits>
+
+namespace sap {
+namespace {
+
+using namespace attn;
+
+constexpr int kD = 512;
+constexpr int kNW = 4;                        // waves
+constexpr int kNT = 64 * kNW;                 // threads
+constexpr int kTB = kAttnTile * kD * 2;       // bytes of one LDS tile (32 rows)
+constexpr int kDepth = 4;                     // LDS tiles: PV(i), S(i+1), tile i+2 landing, tile i+3 gathering
+constexpr int kRW = kAttnTile / kNW;          // gather rows per wave per tile
+constexpr int kSK = kD / 32;                  // S k-steps over the full head_dim
+constexpr int kPM = kD / (16 * kNW);          // PV m-steps over a wave's head_dim quarter
+
+// lane l moves 16 bytes from base + voff into LDS at lds + 16 l.  The scalar
+// base may come from v_readlane, so the wait states a vector memory
+// instruction needs after a VALU write of its scalar operand are inserted
+// here (the compiler does not see into the assembly).
+__device__ __forceinline__ void dma_row(uint64_t base, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "s_nop 4\n\t"
+                 "global_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+
+// MFMA 16x16x32 bf16 with the register classes pinned: O's 128 accumulators
+// in AGPRs, the 128 registers of Q (the B operand of S) in AGPRs, everything
+// the VALU touches in VGPRs.  Left to the register allocator, both O and Q
+// compete for the AGPRs and values are copied back and forth around every
+// MFMA.  The compiler's hazard tracking does not see into these statements,
+// so: operands come straight from LDS loads (waited for by the compiler); the
+// first S step of a chain starts from 0 rather than from a register the VALU
+// wrote; the VALU reads S only after explicit wait states (s_wait_mfma); and
+// O is read only after the tile loop, behind explicit wait states.
+__device__ __forceinline__ void mfma_acc(f32x4 &c, const uint4 &a, const uint4 &b)
+{
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(as_bf16x8(a)), "v"(as_bf16x8(b)));
+}
+__device__ __forceinline__ f32x4 mfma_s_first(const uint4 &a, const bf16x8 &b)
+{
+    f32x4 c;
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(as_bf16x8(a)), "a"(b));
+    return c;
+}
+__device__ __forceinline__ void mfma_s(f32x4 &c, const uint4 &a, const bf16x8 &b)
+{
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(as_bf16x8(a)), "a"(b));
+}
+// 16 bytes from LDS straight into AGPRs (Q); the caller waits with
+// s_waitcnt lgkmcnt(0) before the first use
+__device__ __forceinline__ bf16x8 lds_b128_agpr(uint32_t addr)
+{
+    bf16x8 v;
+    asm volatile("ds_read_b128 %0, %1" : "=a"(v) : "v"(addr) : "memory");
+    return v;
+}
+// wait states between an MFMA's last write of a VGPR and a VALU read of it
+__device__ __forceinline__ void s_wait_mfma() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory"); }
+
+template <int OUT>
+__global__ __attribute__((amdgpu_flat_work_group_size(kNT, kNT), amdgpu_waves_per_eu(1, 1)))
+void attn_d512_kernel(AttnParams p)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles[kDepth][kTB];
+    __shared__ __attribute__((aligned(16))) int sidx[kIdxChunk];
+    __shared__ int xscan[kNW];
+    // bf16 weights by [tile parity][head tile][column half][lane]: lane l of
+    // column half c holds columns 16c + 4(l/16) .. +3 of head 16 j + l%16, so a
+    // PV lane reads its B operand (8 columns) with one ds_read2_b64
+    __shared__ uint2 xp[2][4][2][64];
+    // per tile (ring of 3): some wave saw a max beyond the slack.  Tile k's
+    // word is set during iteration k-1, read in iteration k and cleared in
+    // iteration k+1, before tile k+3 uses it again.
+    __shared__ int xf[3];
+    __shared__ float xm[kNW][32];     // tile maxima of each wave's 32 heads (slow path)
+    __shared__ float xl[kNW][32];     // softmax sums at the end
+
+    // XCD-aware order: consecutive tokens (which share window rows) stay on
+    // one XCD
+    int lb = blockIdx.x;
+    {
+        const int per = (int)gridDim.x >> 3;
+        if (lb < (per << 3)) lb = (lb & 7) * per + (lb >> 3);
+    }
+    const int t = lb;   // one workgroup per (token, head block): all of the token's columns
+    const int c_begin = 0, c_end = p.n_cols;
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    const int hg = w & 1, cs = w >> 1;
+    const int hbase = blockIdx.y * kAttnHeadsPerBlock;
+    const uint32_t tiles_lds = lds_offset(&tiles[0][0]);
+
+    // The block's 64 q rows land in tiles 2 and 3 with whole-row LDS DMA
+    // (16-byte chunk c of head row h at slot c ^ (h & 15)); tiles 0 and 1 stay
+    // free for the first gathers.
+    uint8_t *const qstage = &tiles[2][0];
+    if (c_end > c_begin) {
+#pragma unroll
+    for (int k = 0; k < kAttnHeadsPerBlock / kNW; ++k) {
+        const int h = kNW * k + w;
+        const int head = hbase + h < p.H ? hbase + h : hbase;   // rows past H: finite stand-in
+        const uint16_t *src = p.q + (int64_t)t * p.q_st + (int64_t)head * p.q_sh + 8 * (lane ^ (h & 15));
+        dma16(src, lds_offset(qstage + 1024 * h));
+    }
+    }
+
+    const uint8_t *const win_pool = p.win, *const cmp_pool = p.cmp;
+    const int64_t win_rs = p.win_rs, cmp_rs = p.cmp_rs;
+    const int n_win = p.n_win;
+    const float sl2 = p.sm_scale_log2;
+    // finite bytes that padding columns load instead of a pool row (their
+    // scores are -inf and their weights 0)
+    const uint64_t safe_src = (uint64_t)(p.q + (int64_t)t * p.q_st);
+    const int32_t *idx_row = p.idx + (int64_t)t * p.idx_st;
+
+    // Column staging: a chunk's valid columns are packed to the front of sidx
+    // in column order; each entry is its pool row, bit 31 set for the
+    // compressed pool; -1 pads the last tile.  4 consecutive columns per
+    // thread per batch.
+    int nval = 0, n_tiles = 0;
+    auto load4 = [&](int cbase, int cn, int i0, int (&iv)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + 4 * tid + u;
+            iv[u] = i < cn ? idx_row[cbase + i] : -1;
+        }
+    };
+    auto stage4 = [&](int cbase, int i0, const int (&iv)[4]) __attribute__((always_inline)) {
+        int cnt = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) cnt += iv[u] >= 0 ? 1 : 0;
+        const int incl = wave_incl_sum(cnt);
+        if (lane == 63) xscan[w] = incl;
+        __syncthreads();
+        int before = 0, tot = 0;
+#pragma unroll
+        for (int k = 0; k < kNW; ++k) {
+            const int v = xscan[k];
+            before += k < w ? v : 0;
+            tot += v;
+        }
+        int at = nval + before + incl - cnt;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (iv[u] >= 0) {
+                const bool win = cbase + i0 + 4 * tid + u < n_win;
+                sidx[at++] = win ? iv[u] : (int)((uint32_t)iv[u] | 0x80000000u);
+            }
+        }
+        nval += tot;
+        __syncthreads();   // xscan is rewritten by the next batch
+    };
+    auto pad = [&]() __attribute__((always_inline)) {
+        n_tiles = (nval + kAttnTile - 1) / kAttnTile;
+        for (int i = nval + tid; i < n_tiles * kAttnTile; i += kNT) sidx[i] = -1;
+    };
+
+    // gathers of a tile: lane k < 8 resolves the wave's row 8w + k from its
+    // staged entry (row_bases), then each row goes out as one instruction
+    // (gather_row).  Tile row rho holds chunk j at slot j ^ rswz(rho), and
+    // rswz(8w + q) = rswz(q).
+    struct RowBases {
+        int lo, hi;
+    };
+    auto row_entry = [&](int tile) __attribute__((always_inline)) {
+        return sidx[tile * kAttnTile + kRW * w + (lane & 7)];
+    };
+    auto row_bases = [&](int e) __attribute__((always_inline)) {
+        const bool ok = e != -1, win = e >= 0;
+        const uint64_t r = (uint32_t)e & 0x7FFFFFFFu;
+        const uint64_t rb = (uint64_t)(win ? win_pool : cmp_pool) + r * (uint64_t)(win ? win_rs : cmp_rs);
+        const uint64_t base = ok ? rb : safe_src;
+        return RowBases{(int)(uint32_t)base, (int)(uint32_t)(base >> 32)};
+    };
+    auto gather_row = [&](const RowBases &rb, int buf, int q) __attribute__((always_inline)) {
+        const uint64_t b = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(rb.hi, q) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane(rb.lo, q);
+        dma_row(b, 16u * (uint32_t)(lane ^ rswz(q)), tiles_lds + (uint32_t)(buf * kTB + (kRW * w + q) * 1024));
+    };
+    auto gather = [&](int buf, int tile) __attribute__((always_inline)) {
+        const RowBases rb = row_bases(row_entry(tile));
+#pragma unroll
+        for (int q = 0; q < kRW; ++q) gather_row(rb, buf, q);
+    };
+
+    // S^T k-step s of this wave: row 16cs + l16, 16-byte chunk 4s + g
+    int kb[2];
+    {
+        const int rho = 16 * cs + l16, sw = rswz(rho);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) kb[e] = rho * 2 * kD + 16 * ((4 * e + g) ^ sw);
+    }
+    // V^T fragments of PV m-step m: rows 4g + l16/4 (+16) at head_dim
+    // 128w + 16m + 4(l16 % 4)
+    int vb[4];
+    {
+        const int dsub = 4 * (l16 & 3);
+        const int r = 4 * g + (l16 >> 2), vs = rswz(r);
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+            const int d = (kD / kNW) * w + 16 * mm + dsub;
+            vb[mm] = r * 2 * kD + 16 * ((d >> 3) ^ vs) + 2 * (d & 7);
+        }
+    }
+
+    // O^T accumulators: acc[m][j] = O^T[d = 128w + 16m + 4g + i][head 16j + l16]
+    f32x4 acc[kPM][4];
+#pragma unroll
+    for (int m = 0; m < kPM; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // running max of heads 16J + l16 (the same in every wave), the maxima of
+    // the owned head tiles 2hg + jj, this lane's sums over its columns of the
+    // owned heads, and the sums of the last softmax not yet added
+    f32x4 m_run = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    float m_own[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f}, psum[2] = {0.f, 0.f};
+    float x[2][4];   // scores of the last softmax'd tile (log2 domain; -inf for padding)
+
+    // softmax pieces.  Scores of tile `tile` from the S accumulators
+    // (column 16cs + 4g + i of the tile is valid iff i < vmax):
+    auto scores = [&](const f32x4 (&sa)[2][2], int tile) __attribute__((always_inline)) {
+        const int vmax = nval - tile * kAttnTile - 16 * cs - 4 * g;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[jj][i] = i < vmax ? (sa[jj][0][i] + sa[jj][1][i]) * sl2 : -INFINITY;
+    };
+    // whether a head's tile max exceeds its running max by more than the slack
+    auto beyond = [&]() __attribute__((always_inline)) {
+        int fl = 0;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const float tm = group4_max(fmaxf(fmaxf(x[jj][0], x[jj][1]), fmaxf(x[jj][2], x[jj][3])));
+            fl |= tm > m_own[jj] + kRescaleSlack ? 1 : 0;
+        }
+        return fl;
+    };
+    // weights of head tile jj against its owned max, packed as bf16
+    auto weights_of = [&](int jj) __attribute__((always_inline)) {
+        const float msub = m_own[jj] == -INFINITY ? 0.0f : m_own[jj];
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(x[jj][i] - msub);
+        psum[jj] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        return make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
+    };
+    auto put_weights = [&](int par, const uint2 (&pk)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) xp[par][2 * hg + jj][cs][lane] = pk[jj];
+    };
+    auto weights = [&](int par) __attribute__((always_inline)) {
+        const uint2 pk[2] = {weights_of(0), weights_of(1)};
+        put_weights(par, pk);
+    };
+    // slow path for the tile whose weights are in xp[par]: every wave agrees
+    // on the new maxima, O and the sums are rescaled, the weights rewritten
+    auto slow = [&](int par) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const float tm = group4_max(fmaxf(fmaxf(x[jj][0], x[jj][1]), fmaxf(x[jj][2], x[jj][3])));
+            if (g == 0) xm[w][16 * jj + l16] = tm;
+        }
+        __syncthreads();
+        float alpha[4];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            const int o = 16 * (J & 1) + l16;
+            const float mt = fmaxf(xm[J >> 1][o], xm[(J >> 1) + 2][o]);
+            const float mr = m_run[J];
+            const bool up = mt > mr + kRescaleSlack;   // also from -inf
+            const float mn = up ? mt : mr;
+            alpha[J] = up ? fast_exp2(mr - mn) : 1.0f;   // 0 from -inf: O and the sums are still zero
+            m_run[J] = mn;
+            if (__builtin_amdgcn_ballot_w64(alpha[J] != 1.0f) != 0) {
+#pragma unroll
+                for (int m = 0; m < kPM; ++m) agpr_scale(acc[m][J], alpha[J]);
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const float a = hg ? alpha[2 + jj] : alpha[jj];
+            l_run[jj] *= a;
+            m_own[jj] = hg ? m_run[2 + jj] : m_run[jj];
+        }
+        weights(par);
+        __syncthreads();
+    };
+
+    // Q fragments of S: qf[jj][s] = q[hbase + 32hg + 16jj + l16, 32s + 8g .. +7]
+    bf16x8 qf[2][kSK];
+    // S^T of the tile in LDS tile `buf`: sa[jj][e] = partial S^T[column 16cs +
+    // 4g + i][head 32hg + 16jj + l16] over the k-steps s with s % 2 == e
+    // (K fragments are read KD steps ahead; hook(s) runs between the MFMAs)
+    auto s_tile = [&](int buf, f32x4 (&sa)[2][2], auto hook) __attribute__((always_inline)) {
+        const uint8_t *bf = &tiles[buf][0];
+        auto kfrag = [&](int s) __attribute__((always_inline)) { return lds_b128(bf + kb[s & 1] + 128 * (s >> 1)); };
+        constexpr int KD = 3;
+        uint4 f[KD];
+#pragma unroll
+        for (int s = 0; s + 1 < KD; ++s) f[s] = kfrag(s);
+#pragma unroll
+        for (int s = 0; s < kSK; ++s) {
+            if (s + KD - 1 < kSK) f[(s + KD - 1) % KD] = kfrag(s + KD - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (s < 2) {
+                sa[0][s] = mfma_s_first(f[s % KD], qf[0][s]);
+                sa[1][s] = mfma_s_first(f[s % KD], qf[1][s]);
+            } else {
+                mfma_s(sa[0][s & 1], f[s % KD], qf[0][s]);
+                mfma_s(sa[1][s & 1], f[s % KD], qf[1][s]);
+            }
+            hook(s);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // O^T += V^T P^T for the tile in LDS tile `buf` with the weights in xp[par]
+    // (V^T fragments are read VD steps ahead; hook(m) runs between the MFMAs)
+    auto pv = [&](int buf, int par, auto hook) __attribute__((always_inline)) {
+        const uint8_t *bf = &tiles[buf][0];
+        auto vfrag = [&](int m) __attribute__((always_inline)) {
+            const uint2 v0 = lds_tr16(bf + vb[m & 3] + 128 * (m >> 2));
+            const uint2 v1 = lds_tr16(bf + vb[m & 3] + 16 * 2 * kD + 128 * (m >> 2));
+            return make_uint4(v0.x, v0.y, v1.x, v1.y);
+        };
+        uint4 pb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint2 a = xp[par][j][0][lane], b = xp[par][j][1][lane];
+            pb[j] = make_uint4(a.x, a.y, b.x, b.y);
+        }
+        constexpr int VD = 3;
+        uint4 vr[VD];
+#pragma unroll
+        for (int m = 0; m + 1 < VD; ++m) vr[m] = vfrag(m);
+#pragma unroll
+        for (int m = 0; m < kPM; ++m) {
+            if (m + VD - 1 < kPM) vr[(m + VD - 1) % VD] = vfrag(m + VD - 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mfma_acc(acc[m][j], vr[m % VD], pb[j]);
+            hook(m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // one chunk of columns whose indices are staged in sidx: prologue (tiles
+    // 0 .. 2 in flight, S of tile 0), then the tile loop.  Tiles 0 and 1 may
+    // have been issued already.
+    auto run_chunk = [&](bool issued01) __attribute__((always_inline)) {
+        const int n = n_tiles;
+        if (!issued01) {
+            gather(0, 0);
+            if (n > 1) gather(1, 1);
+        }
+        if (n > 2) gather(2, 2);
+        if (tid < 3) xf[tid] = 0;
+        if (n > 2) wait_vm<2 * kRW>();
+        else if (n > 1) wait_vm<kRW>();
+        else wait_vm<0>();
+        __syncthreads();
+        {
+            f32x4 sa[2][2];
+            s_tile(0, sa, [](int) {});
+            s_wait_mfma();
+            scores(sa, 0);   // its maxima are agreed on in the slow path below
+        }
+        if (n > 2) wait_vm<kRW>();
+        else wait_vm<0>();
+        __syncthreads();
+        int f0 = 0, f1 = 1, f2 = 2;   // flag slots of tiles i, i+1, i+2
+        // iteration i; G3: tile i+3 exists (its gathers go out), MORE: tile
+        // i+1 exists (its S and softmax run).  Peeled so the steady-state
+        // iterations have no branches besides the slow path.
+        auto body = [&](int i, auto g3_tag, auto more_tag) __attribute__((always_inline)) {
+            constexpr bool G3 = decltype(g3_tag)::value, MORE = decltype(more_tag)::value;
+            const int fw = xf[f0];
+            if (tid == 0) xf[f2] = 0;   // tile i-1's word: tile i+2 sets it next iteration
+            int e3 = -1;
+            if constexpr (G3) e3 = row_entry(i + 3);
+            f32x4 sa[2][2];
+            if constexpr (MORE) {
+                // S of tile i+1; the row bases of tile i+3 are resolved after
+                // the first k-step and its rows go out one per step
+                RowBases rb3{0, 0};
+                s_tile((i + 1) & 3, sa, [&](int s) __attribute__((always_inline)) {
+                    if constexpr (G3) {
+                        if (s == 1) rb3 = row_bases(e3);
+                        if (s >= 2 && s < 2 + kRW) gather_row(rb3, (i + 3) & 3, s - 2);
+                    }
+                });
+            }
+            // tile i: the first of the chunk, or a max beyond the slack
+            const int any = i == 0 ? 1 : __builtin_amdgcn_readfirstlane(fw);
+            if (any) slow(i & 1);
+            l_run[0] += psum[0];
+            l_run[1] += psum[1];
+            // PV of tile i with the softmax of tile i+1 between its MFMAs
+            uint2 pk[2];
+            int fl = 0;
+            pv(i & 3, i & 1, [&](int m) __attribute__((always_inline)) {
+                if constexpr (MORE) {
+                    if (m == 1) {
+                        s_wait_mfma();
+                        scores(sa, i + 1);
+                    }
+                    if (m == 2) fl = beyond();
+                    if (m == 3) pk[0] = weights_of(0);
+                    if (m == 4) pk[1] = weights_of(1);
+                    if (m == 5) {
+                        put_weights((i + 1) & 1, pk);
+                        if (lane == 0 && __builtin_amdgcn_ballot_w64(fl != 0) != 0) atomicOr(&xf[f1], 1);
+                    }
+                }
+            });
+            if constexpr (G3) wait_vm<kRW>();
+            else wait_vm<0>();
+            __syncthreads();
+            const int ft = f0;
+            f0 = f1;
+            f1 = f2;
+            f2 = ft;
+        };
+        using T_ = std::integral_constant<bool, true>;
+        using F_ = std::integral_constant<bool, false>;
+        int i = 0;
+        for (; i + 3 < n; ++i) body(i, T_{}, T_{});
+        for (; i + 1 < n; ++i) body(i, F_{}, T_{});
+        body(i, F_{}, F_{});   // the last tile (n >= 1)
+    };
+    auto stage_chunk = [&](int cc) __attribute__((always_inline)) {
+        const int cn = min(c_end - cc, kIdxChunk);
+        nval = 0;
+        for (int i0 = 0; i0 < cn; i0 += 4 * kNT) {
+            int iv[4];
+            load4(cc, cn, i0, iv);
+            stage4(cc, i0, iv);
+        }
+        pad();
+        // a wait the compiler sees: the index loads (and q) are complete, so
+        // none of its waits is left for the tile loop
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+    };
+
+    if (c_end > c_begin) {
+        // first chunk: its indices load while q lands; its first two tiles
+        // go out while the q fragments are read
+        stage_chunk(c_begin);
+        const int n0 = n_tiles;
+        if (n0 > 0) gather(0, 0);
+        if (n0 > 1) gather(1, 1);
+        // (rows past H read the finite stand-in row staged for them; their
+        // scores are never used)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int hr = 32 * hg + 16 * jj + l16;
+            const uint32_t row = lds_offset(qstage) + (uint32_t)(hr * 2 * kD);
+#pragma unroll
+            for (int s = 0; s < kSK; ++s) qf[jj][s] = lds_b128_agpr(row + 16u * (uint32_t)((4 * s + g) ^ l16));
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __syncthreads();   // tiles 2 and 3 (q) are free
+        if (n0 > 0) run_chunk(true);
+        for (int cc = c_begin + kIdxChunk; cc < c_end; cc += kIdxChunk) {
+            stage_chunk(cc);
+            if (n_tiles > 0) run_chunk(false);
+        }
+    }
+    wait_vm<0>();   // no transfer into LDS outlives the workgroup
+    // wait states between the last accumulating MFMA (inline assembly, which
+    // the compiler's hazard tracking does not see) and the reads of O below
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+
+    // softmax sums: owners reduce over their columns, everyone adds the two
+    // column halves of each head in a fixed order
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const float ls = group4_sum(l_run[jj]);
+        if (g == 0) xl[w][16 * jj + l16] = ls;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int head = hbase + 16 * j + l16;
+        const int o = 16 * (j & 1) + l16;
+        const float l_tot = xl[j >> 1][o] + xl[(j >> 1) + 2][o];
+        if (head >= p.H) continue;
+        const int d0 = (kD / kNW) * w + 4 * g;
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        if constexpr (OUT == 1) {
+            float *dst = (float *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d0;
+#pragma unroll
+            for (int m = 0; m < kPM; ++m) {
+                const f32x4 v = acc[m][j] * inv;
+                *(float4 *)(dst + 16 * m) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        } else {
+            uint16_t *dst = (uint16_t *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d0;
+#pragma unroll
+            for (int m = 0; m < kPM; ++m) {
+                const f32x4 v = acc[m][j] * inv;
+                *(uint2 *)(dst + 16 * m) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            }
+        }
+    }
+}
+
+template <int OUT>
+hipError_t launch_t(const AttnParams &p, hipStream_t s)
+{
+    const dim3 grid((unsigned)p.T, (unsigned)((p.H + kAttnHeadsPerBlock - 1) / kAttnHeadsPerBlock));
+    hipLaunchKernelGGL((attn_d512_kernel<OUT>), grid, dim3(kNT), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_d512(const AttnParams &p, int out, hipStream_t s)
+{
+    if (p.num_splits != 1) return hipErrorInvalidValue;   // one split per token only
+    return out == 1 ? launch_t<1>(p, s) : launch_t<0>(p, s);
+}
+
+}  // namespace sap

@@ -33,8 +33,12 @@ struct AttnParams {
 // kv: 0 = bf16, 2 = e4m3.  out: 0 = bf16, 1 = f32.
 hipError_t launch_attn(const AttnParams &p, int D, int kv, int out_dtype, hipStream_t s);
 hipError_t launch_attn_merge(const AttnParams &p, int D, int kv, int out_dtype, hipStream_t s);
-// waves per attention workgroup: 8 (two head groups, two waves per SIMD)
-// for bf16 rows at head_dim 512, else 4; the split partials follow its layout
+// bf16 rows at head_dim 512 with one split per token (attn_d512.hip);
+// launch_attn dispatches to it
+hipError_t launch_attn_d512(const AttnParams &p, int out_dtype, hipStream_t s);
+// waves per workgroup of the split-K attention kernel, whose layout the split
+// partials follow: 8 (two head groups, two waves per SIMD) at head_dim 512,
+// else 4
 constexpr int attn_waves(int D, int kv) { return D == 512 ? 8 : 4; }
 
 struct IndexerParams {
