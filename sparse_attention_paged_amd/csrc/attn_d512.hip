@@ -87,6 +87,23 @@ __device__ __forceinline__ void mfma_s(f32x4 &c, const uint4 &a, const bf16x8 &b
 {
     asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(as_bf16x8(a)), "a"(b));
 }
+// a 4-byte global load the compiler does not track (it issues no wait for
+// it): the value is only read through vm_wait4 below
+__device__ __forceinline__ int gload_untracked(const int32_t *src)
+{
+    int v;
+    asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(src) : "memory");
+    return v;
+}
+// at most N vector memory operations in flight, then the four values loaded
+// by gload_untracked are ready (they pass through this statement, so no use
+// can be scheduled above it)
+template <int N>
+__device__ __forceinline__ void vm_wait4(int (&v)[4])
+{
+    asm volatile("s_waitcnt vmcnt(%4)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]) : "n"(N) : "memory");
+}
+
 // 16 bytes from LDS straight into AGPRs (Q); the caller waits with
 // s_waitcnt lgkmcnt(0) before the first use
 __device__ __forceinline__ bf16x8 lds_b128_agpr(uint32_t addr)
@@ -116,14 +133,18 @@ void attn_d512_kernel(AttnParams p)
     __shared__ float xm[kNW][32];     // tile maxima of each wave's 32 heads (slow path)
     __shared__ float xl[kNW][32];     // softmax sums at the end
 
-    // XCD-aware order: consecutive tokens (which share window rows) stay on
-    // one XCD
-    int lb = blockIdx.x;
-    {
-        const int per = (int)gridDim.x >> 3;
-        if (lb < (per << 3)) lb = (lb & 7) * per + (lb >> 3);
+    // Tokens of this workgroup (all of a token's columns, one head block).
+    // A grid of fewer workgroups than tokens is persistent and XCD-aware:
+    // XCD x = blockIdx.x % 8 takes the contiguous token range [T x/8,
+    // T (x+1)/8) and its workgroups interleave over it, so consecutive tokens
+    // (which share window rows) run at the same time on one XCD's L2.
+    int t0 = blockIdx.x, tstep = 1, tend = blockIdx.x + 1;
+    if ((int)gridDim.x < p.T) {
+        const int x = blockIdx.x & 7, per = (int)gridDim.x >> 3;
+        t0 = (int)((int64_t)p.T * x / 8) + (blockIdx.x >> 3);
+        tend = (int)((int64_t)p.T * (x + 1) / 8);
+        tstep = per;
     }
-    const int t = lb;   // one workgroup per (token, head block): all of the token's columns
     const int c_begin = 0, c_end = p.n_cols;
 
     const int tid = threadIdx.x;
@@ -137,15 +158,15 @@ void attn_d512_kernel(AttnParams p)
     // (16-byte chunk c of head row h at slot c ^ (h & 15)); tiles 0 and 1 stay
     // free for the first gathers.
     uint8_t *const qstage = &tiles[2][0];
-    if (c_end > c_begin) {
+    auto stage_q = [&](int tq) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < kAttnHeadsPerBlock / kNW; ++k) {
-        const int h = kNW * k + w;
-        const int head = hbase + h < p.H ? hbase + h : hbase;   // rows past H: finite stand-in
-        const uint16_t *src = p.q + (int64_t)t * p.q_st + (int64_t)head * p.q_sh + 8 * (lane ^ (h & 15));
-        dma16(src, lds_offset(qstage + 1024 * h));
-    }
-    }
+        for (int k = 0; k < kAttnHeadsPerBlock / kNW; ++k) {
+            const int h = kNW * k + w;
+            const int head = hbase + h < p.H ? hbase + h : hbase;   // rows past H: finite stand-in
+            const uint16_t *src = p.q + (int64_t)tq * p.q_st + (int64_t)head * p.q_sh + 8 * (lane ^ (h & 15));
+            dma16(src, lds_offset(qstage + 1024 * h));
+        }
+    };
 
     const uint8_t *const win_pool = p.win, *const cmp_pool = p.cmp;
     const int64_t win_rs = p.win_rs, cmp_rs = p.cmp_rs;
@@ -153,8 +174,9 @@ void attn_d512_kernel(AttnParams p)
     const float sl2 = p.sm_scale_log2;
     // finite bytes that padding columns load instead of a pool row (their
     // scores are -inf and their weights 0)
-    const uint64_t safe_src = (uint64_t)(p.q + (int64_t)t * p.q_st);
-    const int32_t *idx_row = p.idx + (int64_t)t * p.idx_st;
+    int t = t0;
+    uint64_t safe_src = 0;
+    const int32_t *idx_row = nullptr;
 
     // Column staging: a chunk's valid columns are packed to the front of sidx
     // in column order; each entry is its pool row, bit 31 set for the
@@ -470,88 +492,146 @@ void attn_d512_kernel(AttnParams p)
         for (; i + 1 < n; ++i) body(i, F_{}, T_{});
         body(i, F_{}, F_{});   // the last tile (n >= 1)
     };
-    auto stage_chunk = [&](int cc) __attribute__((always_inline)) {
+    // stage a chunk's indices; iv0: its first batch, already loaded
+    auto stage_chunk = [&](int cc, const int (&iv0)[4]) __attribute__((always_inline)) {
         const int cn = min(c_end - cc, kIdxChunk);
         nval = 0;
-        for (int i0 = 0; i0 < cn; i0 += 4 * kNT) {
+        stage4(cc, 0, iv0);
+        for (int i0 = 4 * kNT; i0 < cn; i0 += 4 * kNT) {
             int iv[4];
             load4(cc, cn, i0, iv);
             stage4(cc, i0, iv);
         }
         pad();
-        // a wait the compiler sees: the index loads (and q) are complete, so
-        // none of its waits is left for the tile loop
-        __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
     };
 
-    if (c_end > c_begin) {
-        // first chunk: its indices load while q lands; its first two tiles
-        // go out while the q fragments are read
-        stage_chunk(c_begin);
-        const int n0 = n_tiles;
-        if (n0 > 0) gather(0, 0);
-        if (n0 > 1) gather(1, 1);
-        // (rows past H read the finite stand-in row staged for them; their
-        // scores are never used)
+    // The q rows and the first index batch of a token go out together; for
+    // later tokens they go out before the previous token's output stores,
+    // so they land while those drain.  The index loads are untracked: the
+    // compiler would otherwise wait for every store before staging them.
+    // The store count of a full head block (32 per wave) stays in flight.
+    int iv0[4];
+    const int cn0 = min(c_end - c_begin, kIdxChunk);
+    auto first_loads = [&](int tq) __attribute__((always_inline)) {
+        if (c_end <= c_begin) return;
+        stage_q(tq);
+        const int32_t *row = p.idx + (int64_t)tq * p.idx_st + c_begin;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = 4 * tid + u;
+            iv0[u] = gload_untracked(row + (i < cn0 ? i : 0));
+        }
+    };
+    auto first_batch = [&](bool after_stores) __attribute__((always_inline)) {
+        if (after_stores && hbase + kAttnHeadsPerBlock <= p.H) vm_wait4<kPM * 4>(iv0);
+        else vm_wait4<0>(iv0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) iv0[u] = 4 * tid + u < cn0 ? iv0[u] : -1;
+    };
+    if (t < tend) first_loads(t);
+    for (bool later = false; t < tend; t += tstep, later = true) {
+        idx_row = p.idx + (int64_t)t * p.idx_st;
+        safe_src = (uint64_t)(p.q + (int64_t)t * p.q_st);
+#pragma unroll
+        for (int m = 0; m < kPM; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        m_own[0] = m_own[1] = -INFINITY;
+        l_run[0] = l_run[1] = psum[0] = psum[1] = 0.0f;
+        if (c_end > c_begin) {
+            // first chunk: its first two tiles go out while the q fragments
+            // are read
+            first_batch(later);
+            stage_chunk(c_begin, iv0);
+            const int n0 = n_tiles;
+            if (n0 > 0) gather(0, 0);
+            if (n0 > 1) gather(1, 1);
+            // (rows past H read the finite stand-in row staged for them; their
+            // scores are never used)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int hr = 32 * hg + 16 * jj + l16;
+                const uint32_t row = lds_offset(qstage) + (uint32_t)(hr * 2 * kD);
+#pragma unroll
+                for (int s = 0; s < kSK; ++s) qf[jj][s] = lds_b128_agpr(row + 16u * (uint32_t)((4 * s + g) ^ l16));
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __syncthreads();   // tiles 2 and 3 (q) are free
+            if (n0 > 0) run_chunk(true);
+            for (int cc = c_begin + kIdxChunk; cc < c_end; cc += kIdxChunk) {
+                int iv[4];
+                load4(cc, min(c_end - cc, kIdxChunk), 0, iv);
+                stage_chunk(cc, iv);
+                if (n_tiles > 0) run_chunk(false);
+            }
+        }
+        wait_vm<0>();   // no transfer into LDS is left (and none outlives the workgroup)
+        // wait states between the last accumulating MFMA (inline assembly, which
+        // the compiler's hazard tracking does not see) and the reads of O below
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        // every wave is past its last read of the tiles and of sidx: the next
+        // token's q rows and first indices go out now
+        __syncthreads();
+        if (t + tstep < tend) first_loads(t + tstep);
+        // softmax sums: owners reduce over their columns, everyone adds the two
+        // column halves of each head in a fixed order
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-            const int hr = 32 * hg + 16 * jj + l16;
-            const uint32_t row = lds_offset(qstage) + (uint32_t)(hr * 2 * kD);
-#pragma unroll
-            for (int s = 0; s < kSK; ++s) qf[jj][s] = lds_b128_agpr(row + 16u * (uint32_t)((4 * s + g) ^ l16));
+            const float ls = group4_sum(l_run[jj]);
+            if (g == 0) xl[w][16 * jj + l16] = ls;
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __syncthreads();   // tiles 2 and 3 (q) are free
-        if (n0 > 0) run_chunk(true);
-        for (int cc = c_begin + kIdxChunk; cc < c_end; cc += kIdxChunk) {
-            stage_chunk(cc);
-            if (n_tiles > 0) run_chunk(false);
-        }
-    }
-    wait_vm<0>();   // no transfer into LDS outlives the workgroup
-    // wait states between the last accumulating MFMA (inline assembly, which
-    // the compiler's hazard tracking does not see) and the reads of O below
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-
-    // softmax sums: owners reduce over their columns, everyone adds the two
-    // column halves of each head in a fixed order
+        __syncthreads();
+        // (the output strides pass through an empty statement so that the
+        // per-lane row offsets are formed here, not kept live across the
+        // token loop)
+        int64_t out_st = p.out_st, out_sh = p.out_sh;
+        asm volatile("" : "+s"(out_st), "+s"(out_sh));
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        const float ls = group4_sum(l_run[jj]);
-        if (g == 0) xl[w][16 * jj + l16] = ls;
-    }
-    __syncthreads();
+        for (int j = 0; j < 4; ++j) {
+            const int head = hbase + 16 * j + l16;
+            const int o = 16 * (j & 1) + l16;
+            const float l_tot = xl[j >> 1][o] + xl[(j >> 1) + 2][o];
+            if (head >= p.H) continue;
+            const int d0 = (kD / kNW) * w + 4 * g;
+            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+            if constexpr (OUT == 1) {
+                float *dst = (float *)p.out + (int64_t)t * out_st + (int64_t)head * out_sh + d0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int head = hbase + 16 * j + l16;
-        const int o = 16 * (j & 1) + l16;
-        const float l_tot = xl[j >> 1][o] + xl[(j >> 1) + 2][o];
-        if (head >= p.H) continue;
-        const int d0 = (kD / kNW) * w + 4 * g;
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        if constexpr (OUT == 1) {
-            float *dst = (float *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d0;
+                for (int m = 0; m < kPM; ++m) {
+                    const f32x4 v = acc[m][j] * inv;
+                    *(float4 *)(dst + 16 * m) = make_float4(v[0], v[1], v[2], v[3]);
+                }
+            } else {
+                uint16_t *dst = (uint16_t *)p.out + (int64_t)t * out_st + (int64_t)head * out_sh + d0;
 #pragma unroll
-            for (int m = 0; m < kPM; ++m) {
-                const f32x4 v = acc[m][j] * inv;
-                *(float4 *)(dst + 16 * m) = make_float4(v[0], v[1], v[2], v[3]);
-            }
-        } else {
-            uint16_t *dst = (uint16_t *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d0;
-#pragma unroll
-            for (int m = 0; m < kPM; ++m) {
-                const f32x4 v = acc[m][j] * inv;
-                *(uint2 *)(dst + 16 * m) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                for (int m = 0; m < kPM; ++m) {
+                    const f32x4 v = acc[m][j] * inv;
+                    *(uint2 *)(dst + 16 * m) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                }
             }
         }
     }
+}// workgroups per head block: one per CU (a workgroup takes most of a CU's
+// LDS), rounded down to a multiple of the 8 XCDs, at most one per token
+int persistent_blocks(int T)
+{
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return T;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) return T;
+        cus[dev] = n & ~7;
+    }
+    return T < cus[dev] ? T : cus[dev];
 }
 
 template <int OUT>
 hipError_t launch_t(const AttnParams &p, hipStream_t s)
 {
-    const dim3 grid((unsigned)p.T, (unsigned)((p.H + kAttnHeadsPerBlock - 1) / kAttnHeadsPerBlock));
+    const dim3 grid((unsigned)persistent_blocks(p.T), (unsigned)((p.H + kAttnHeadsPerBlock - 1) / kAttnHeadsPerBlock));
     hipLaunchKernelGGL((attn_d512_kernel<OUT>), grid, dim3(kNT), 0, s, p);
     return hipGetLastError();
 }
