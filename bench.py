@@ -104,6 +104,11 @@ class DecodeStep:
         return self.B * (64 * 512 * 2 + self.C * (self.row_bytes() + 4) + 64 * 512 * 4)
 
 
+# untimed launches before a timed loop of long kernels: the GPU clock ramps
+# up over the first tens of milliseconds of sustained load
+LONG_WARMUP = 20
+
+
 def time_loop(fn, iters, warmup):
     for _ in range(warmup):
         fn()
@@ -166,16 +171,28 @@ def code_sha256(src: str) -> str:
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
+ATTN_SOURCES = ("attn.hip", "attn_d512.hip", "attn_common.hpp")
+
+
+def attn_sources_sha256() -> str:
+    """code_sha256 over the attention kernel sources, in a fixed order."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    parts = []
+    for name in ATTN_SOURCES:
+        with open(os.path.join(here, "sparse_attention_paged_amd", "csrc", name)) as f:
+            parts.append(f.read())
+    return code_sha256("\n".join(parts))
+
+
 def counted_traffic(key):
     """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
-    (profiles/attn_traffic_counters.json), or None when attn.hip changed since
-    the counters were taken."""
+    (profiles/attn_traffic_counters.json), or None when the attention sources
+    changed since the counters were taken."""
     here = os.path.dirname(os.path.abspath(__file__))
     try:
         with open(os.path.join(here, "profiles", "attn_traffic_counters.json")) as f:
             doc = json.load(f)
-        with open(os.path.join(here, "sparse_attention_paged_amd", "csrc", "attn.hip")) as f:
-            sha = code_sha256(f.read())
+        sha = attn_sources_sha256()
     except (OSError, ValueError):
         return None
     if doc.get("attn_code_sha256") != sha or key not in doc:
@@ -213,7 +230,7 @@ def prefill_secondary(iters, kv="bf16"):
     valid = (idx >= 0).sum().item()
     flops = valid * 64 * 512 * 4.0
     ms = time_loop(lambda: sap.sparse_attn_paged(q, win, cmp, idx, case.n_win, case.sm_scale, out=out,
-                                                 win_scale=wsc, cmp_scale=csc, num_splits=1), iters, 2)
+                                                 win_scale=wsc, cmp_scale=csc, num_splits=1), iters, LONG_WARMUP)
     tf = flops / (ms * 1e-3) / 1e12
     key = f"prefill_s8192_r4_{kv}"
     # e4m3 rows are widened to bf16 tiles: the MFMAs are bf16 (P as three bf16 terms triples PV)
@@ -252,7 +269,7 @@ def pages_shapes_secondary(iters):
         out = torch.empty((case.T, 64, 512), dtype=torch.float32, device=d)
         valid = (idx >= 0).sum().item()
         ms = time_loop(lambda: sap.sparse_attn_paged(q, win, cmp, idx, case.n_win, case.sm_scale, out=out,
-                                                     num_splits=1), iters, 2)
+                                                     num_splits=1), iters, LONG_WARMUP)
         tf = valid * 64 * 512 * 4.0 / (ms * 1e-3) / 1e12
         res.append({"workload": name, "us": round(ms * 1e3, 2), "tflops": round(tf, 2),
                     "pages_h100_us": PAGES_H100_US[name],
@@ -294,7 +311,7 @@ def indexer_prefill_secondary(length, start, ratio, iters):
                                                   case.n_keys))
     out = torch.empty((case.T, case.N), dtype=torch.float32, device=d)
     ms = time_graph(lambda: sap.indexer_logits_prefill(q, w, pool, pt, case.page, ts, case.max_tokens, case.N,
-                                                       n_keys=nk, out=out), iters, 1, 2)
+                                                       n_keys=nk, out=out), iters, LONG_WARMUP // 2, 2)
     # useful flops: each visible (token, key) pair costs 32 heads x 128 x 2
     tf = float(case.n_keys.to(torch.float64).sum()) * 32 * 128 * 2 / (ms * 1e-3) / 1e12
     return {"workload": f"indexer_prefill_n{length}_start{start}_r{ratio}", "us": round(ms * 1e3, 2),
