@@ -126,6 +126,9 @@ __device__ Sel radix_select(ForEach for_each, int k, Shared &s)
             ++n;
         }
     });
+    // the histogram is cleared once, ahead of the barrier of the reductions;
+    // afterwards each thread clears the bins it reads
+    for (int i = tid; i < kBins; i += kT) s.hist[i] = 0u;
     block_and_or_count(a, o, n, s);
     const int kk = min(k, n);
     if (kk <= 0) return Sel{0u, 0u, 0, 0};
@@ -135,9 +138,6 @@ __device__ Sel radix_select(ForEach for_each, int k, Shared &s)
     uint32_t M = ~((2u << hb) - 1u);          // hb == 31: 2u << 31 == 0, M == 0
     uint32_t P = a & M;
     int rem = kk;
-    // cleared once here; afterwards each thread clears the bins it reads
-    for (int i = tid; i < kBins; i += kT) s.hist[i] = 0u;
-    __syncthreads();
     for (;;) {
         const int lo = hb >= kDigit - 1 ? hb - (kDigit - 1) : 0;
         const uint32_t dm = (2u << (hb - lo)) - 1u;
@@ -199,6 +199,8 @@ struct IndexList {
     };
     __device__ Run run(int p0, int, int) const { return Run{p0}; }
     __device__ int value_in(const Run &, int position) const { return position; }
+    __device__ bool fast_run(const Run &) const { return true; }
+    __device__ int value_fast(const Run &, int position) const { return position; }
     __device__ void put(int slot, int v) const { out[slot] = v; }
     __device__ void pad(int slot) const { out[slot] = -1; }
     __device__ void window() const {}
@@ -242,6 +244,12 @@ struct SparseIdx {
     __device__ int value_in(const Run &r, int L) const
     {
         if (r.n > page) return value(L);   // pages shorter than a run: look each up
+        return value_fast(r, L);
+    }
+    // the run lies in two pages whose entries are loaded: arithmetic only
+    __device__ bool fast_run(const Run &r) const { return r.n <= page; }
+    __device__ int value_fast(const Run &r, int L) const
+    {
         const int off = L - r.base;
         return off < page ? r.e0 * page + off : r.e1 * page + (off - page);
     }
@@ -260,46 +268,58 @@ struct SparseIdx {
     }
 };
 
-// Writes the selected positions of a block of KPT keys per thread in
-// position order: a selected key's slot is the number of greater keys before
-// it plus min(equal keys before it, rem).  One scan of both counts (16 bits
-// each) gives both.  gt_seen / eq_seen carry the counts of earlier blocks.
-template <int KPT, class ValOf, class Out>
-__device__ void emit_block(const uint32_t (&key)[KPT], ValOf val_of, const Sel &q, const Out &out, int &gt_seen,
+// Places the selected positions of a block of KPT keys per thread in LDS by
+// output slot, in position order: a selected key's slot is the number of
+// greater keys before it plus min(equal keys before it, rem).  One scan of
+// both counts (16 bits each) gives both.  gt_seen / eq_seen carry the counts
+// of earlier blocks.  outv: LDS array of k slots; flush_out writes them out.
+// CHEAP: val_of is arithmetic only, so it is evaluated in the write loop;
+// otherwise (it may load) the values of the selected keys are loaded first,
+// together.  The per-key classes are kept as two bitmasks in VGPRs (per-key
+// booleans become wave masks in SGPRs, which ran out and spilled).
+template <int KPT, bool CHEAP = false, class ValOf>
+__device__ void emit_block(const uint32_t (&key)[KPT], ValOf val_of, const Sel &q, int32_t *outv, int &gt_seen,
                            int &eq_seen, Shared &s)
 {
-    int n_gt = 0, n_eq = 0;
+    static_assert(KPT <= 32, "one bit per key");
+    uint32_t gtm = 0u, eqm = 0u;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-        n_gt += sel_gt(key[j], q);
-        n_eq += sel_eq(key[j], q);
+        gtm |= (sel_gt(key[j], q) ? 1u : 0u) << j;
+        eqm |= (sel_eq(key[j], q) ? 1u : 0u) << j;
     }
-    // values of the candidate positions first (any loads they need are in
-    // flight together), then the stores
-    int val[KPT];
+    int val[CHEAP ? 1 : KPT];
+    if constexpr (!CHEAP) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) val[j] = (sel_gt(key[j], q) || sel_eq(key[j], q)) ? val_of(j) : 0;
+        for (int j = 0; j < KPT; ++j) val[j] = ((gtm | eqm) >> j) & 1u ? val_of(j) : 0;
+    }
     int tot;
-    const int before = block_excl_scan(n_gt | (n_eq << 16), s, tot);
+    const int before = block_excl_scan(__builtin_popcount(gtm) | (__builtin_popcount(eqm) << 16), s, tot);
     int g = gt_seen + (before & 0xFFFF), e = eq_seen + (before >> 16);
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-        if (sel_gt(key[j], q)) {
-            out.put(g + min(e, q.rem), val[j]);
-            ++g;
-        } else if (sel_eq(key[j], q)) {
-            if (e < q.rem) out.put(g + e, val[j]);
-            ++e;
+        const int gt = (int)((gtm >> j) & 1u), eq = (int)((eqm >> j) & 1u);
+        const int slot = gt ? g + min(e, q.rem) : g + e;
+        if ((gt | (eq & (e < q.rem ? 1 : 0))) != 0) {
+            if constexpr (CHEAP) outv[slot] = val_of(j);
+            else outv[slot] = val[j];
         }
+        g += gt;
+        e += eq;
     }
     gt_seen += tot & 0xFFFF;
     eq_seen += tot >> 16;
 }
 
+// the kk selected slots from LDS, then -1 up to k, in coalesced stores
 template <class Out>
-__device__ void pad_out(const Out &out, int from, int k)
+__device__ void flush_out(const Out &out, int kk, int k, const int32_t *outv)
 {
-    for (int i = from + (int)threadIdx.x; i < k; i += kT) out.pad(i);
+    __syncthreads();
+    for (int i = (int)threadIdx.x; i < k; i += kT) {
+        if (i < kk) out.put(i, outv[i]);
+        else out.pad(i);
+    }
 }
 
 // KPT consecutive keys of positions base + tid*KPT .. from row x (n valid)
@@ -325,7 +345,7 @@ __device__ void load_keys(const float *x, int64_t base, int n, uint32_t (&key)[K
 
 // the whole row streamed from memory: every pass reads it again
 template <class Out>
-__device__ void select_streaming(const float *x, int nv, int k, const Out &out, Shared &s)
+__device__ void select_streaming(const float *x, int nv, int k, const Out &out, Shared &s, int32_t *outv)
 {
     constexpr int KPT = 8;
     constexpr int BLK = kT * KPT;
@@ -346,10 +366,13 @@ __device__ void select_streaming(const float *x, int nv, int k, const Out &out, 
             load_keys<KPT>(x, base, nv, key);
             const int p0 = base + (int)threadIdx.x * KPT;
             const auto run = out.run(p0, KPT, nv);
-            emit_block<KPT>(key, [&](int j) { return out.value_in(run, p0 + j); }, q, out, gt_seen, eq_seen, s);
+            if (out.fast_run(run))
+                emit_block<KPT, true>(key, [&](int j) { return out.value_fast(run, p0 + j); }, q, outv, gt_seen, eq_seen, s);
+            else
+                emit_block<KPT>(key, [&](int j) { return out.value_in(run, p0 + j); }, q, outv, gt_seen, eq_seen, s);
         }
     }
-    pad_out(out, kk, k);
+    flush_out(out, kk, k, outv);
 }
 
 // rows of at most kT * KPT positions, keys in registers
@@ -357,6 +380,7 @@ template <int KPT, class Out>
 __global__ __launch_bounds__(kT) void topk_direct_kernel(TopkParams p)
 {
     __shared__ Shared s;
+    __shared__ int32_t outv[kMaxK];   // the selection by output slot
     const int b = blockIdx.x;
     const float *x = p.x + (int64_t)b * p.x_sb;
     const Out out(p, b);
@@ -373,8 +397,13 @@ __global__ __launch_bounds__(kT) void topk_direct_kernel(TopkParams p)
     };
     const Sel q = radix_select(for_each, p.k, s);
     int gt_seen = 0, eq_seen = 0;
-    if (q.kk > 0) emit_block<KPT>(key, [&](int j) { return out.value_in(run, p0 + j); }, q, out, gt_seen, eq_seen, s);
-    pad_out(out, q.kk, p.k);
+    if (q.kk > 0) {
+        if (out.fast_run(run))
+            emit_block<KPT, true>(key, [&](int j) { return out.value_fast(run, p0 + j); }, q, outv, gt_seen, eq_seen, s);
+        else
+            emit_block<KPT>(key, [&](int j) { return out.value_in(run, p0 + j); }, q, outv, gt_seen, eq_seen, s);
+    }
+    flush_out(out, q.kk, p.k, outv);
 }
 
 // workspace of the two-launch path, per row: chunk counts, the sample
@@ -506,8 +535,11 @@ __global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
     }
     const uint32_t tau = ws.tau[b];
     const bool ok = any_over == 0 && total <= kDirectMax && (total >= p.k || tau == 1u);
+    // the selection by output slot reuses ckey: it is read into registers
+    // before the first barrier of the radix select
+    int32_t *const outv = (int32_t *)ckey;
     if (!ok) {
-        select_streaming(x, nv, p.k, out, s);
+        select_streaming(x, nv, p.k, out, s, outv);
         return;
     }
     __syncthreads();
@@ -535,21 +567,22 @@ __global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
             for (int j = 0; j < KPT; ++j) f(key[j]);
         };
         const Sel q = radix_select(for_each, kk, s);
-        emit_block<KPT>(key, [&](int j) { return out.value(cpos[tid * KPT + j]); }, q, out, gt_seen, eq_seen, s);
+        emit_block<KPT>(key, [&](int j) { return out.value(cpos[tid * KPT + j]); }, q, outv, gt_seen, eq_seen, s);
     }
-    pad_out(out, kk, p.k);
+    flush_out(out, kk, p.k, outv);
 }
 
 template <class Out>
 __global__ __launch_bounds__(kT) void topk_stream_kernel(TopkParams p)
 {
     __shared__ Shared s;
+    __shared__ int32_t outv[kMaxK];   // the selection by output slot
     const int b = blockIdx.x;
     int nv = p.n_valid ? p.n_valid[b] : p.N;
     nv = min(max(nv, 0), p.N);
     const Out out(p, b);
     out.window();
-    select_streaming(p.x + (int64_t)b * p.x_sb, nv, p.k, out, s);
+    select_streaming(p.x + (int64_t)b * p.x_sb, nv, p.k, out, s, outv);
 }
 
 int n_chunks(int N) { return (N + kChunk - 1) / kChunk; }
