@@ -156,6 +156,18 @@ def test_head_counts(H):
     assert_attn_close(gpu_attn(case, num_splits=1), ref, f"H={H} one split")
 
 
+def test_prefill_persistent_chunks_partial_heads():
+    """More tokens than workgroups (the prefill launch at head_dim 512 then
+    gives a workgroup several tokens), a partial head block (H = 20, where the
+    next token's loads wait for every store of the previous one) and more
+    columns than one staged index chunk (3128 > 2048)."""
+    need_gpu()
+    case = W.prefill_case(T=300, start=16000, ratio=4, topk=3000, H=20, seed=W.SEED_BASE + 96)
+    assert oracle.case_idx(case).shape[1] > 2048
+    ref = oracle.case_attn(case)
+    assert_attn_close(gpu_attn(case, num_splits=1), ref, "prefill T=300 H=20 3128 columns")
+
+
 @pytest.mark.parametrize("n_win,topk", [(100, 512), (50, 37), (128, 300), (128, 1), (0, 64), (1, 0)])
 def test_window_and_topk_widths(n_win, topk):
     need_gpu()
