@@ -31,6 +31,8 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <type_traits>
+
 namespace sap {
 namespace {
 
@@ -513,20 +515,20 @@ __global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
     const TopkWs ws = topk_ws(p.workspace, p.B, nch);
     const int *cnt = ws.count + (size_t)b * nch;
 
-    // slot offsets in chunk (= position) order
+    // slot offsets in chunk (= position) order, in one scan: a chunk whose
+    // slot overflowed counts kDirectMax + 1, which sends the row to the
+    // streaming path (total < 2^27: kMaxChunks chunks of at most that)
     constexpr int CPT = kMaxChunks / kT;
-    int cl[CPT], local = 0, over = 0;
+    int cl[CPT], local = 0;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         const int ci = tid * CPT + j;
-        cl[j] = ci < nch ? cnt[ci] : 0;
-        over |= cl[j] > kSlotCap;
+        const int c = ci < nch ? cnt[ci] : 0;
+        cl[j] = c > kSlotCap ? kDirectMax + 1 : c;
         local += cl[j];
     }
     int total;
     int o = block_excl_scan(local, s, total);
-    int any_over;
-    block_excl_scan(over, s, any_over);
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
         const int ci = tid * CPT + j;
@@ -534,7 +536,7 @@ __global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
         o += cl[j];
     }
     const uint32_t tau = ws.tau[b];
-    const bool ok = any_over == 0 && total <= kDirectMax && (total >= p.k || tau == 1u);
+    const bool ok = total <= kDirectMax && (total >= p.k || tau == 1u);
     // the selection by output slot reuses ckey: it is read into registers
     // before the first barrier of the radix select
     int32_t *const outv = (int32_t *)ckey;
@@ -553,22 +555,32 @@ __global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
         }
     }
     __syncthreads();
-    uint32_t key[KPT];
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const int i = tid * KPT + j;
-        key[j] = i < total ? ckey[i] : 0u;
-    }
     const int kk = min(p.k, total);
-    int gt_seen = 0, eq_seen = 0;
-    if (kk > 0) {
-        auto for_each = [&](auto f) {
+    // candidates in registers: 8 per thread when they fit (the usual case),
+    // else 32
+    auto select_core = [&](auto kpt_tag) __attribute__((always_inline)) {
+        constexpr int K = decltype(kpt_tag)::value;
+        uint32_t key[K];
 #pragma unroll
-            for (int j = 0; j < KPT; ++j) f(key[j]);
-        };
-        const Sel q = radix_select(for_each, kk, s);
-        emit_block<KPT>(key, [&](int j) { return out.value(cpos[tid * KPT + j]); }, q, outv, gt_seen, eq_seen, s);
-    }
+        for (int j = 0; j < K; ++j) {
+            const int i = tid * K + j;
+            key[j] = i < total ? ckey[i] : 0u;
+        }
+        int gt_seen = 0, eq_seen = 0;
+        if (kk > 0) {
+            auto for_each = [&](auto f) {
+#pragma unroll
+                for (int j = 0; j < K; ++j) f(key[j]);
+            };
+            const Sel q = radix_select(for_each, kk, s);
+            // index lists: a value is an LDS read, taken for every key
+            constexpr bool CHEAP = std::is_same<Out, IndexList>::value;
+            emit_block<K, CHEAP>(key, [&](int j) { return out.value(cpos[min(tid * K + j, kDirectMax - 1)]); }, q,
+                                 outv, gt_seen, eq_seen, s);
+        }
+    };
+    if (total <= 8 * kT) select_core(std::integral_constant<int, 8>{});
+    else select_core(std::integral_constant<int, KPT>{});
     flush_out(out, kk, p.k, outv);
 }
 

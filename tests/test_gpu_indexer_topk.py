@@ -98,7 +98,8 @@ def test_indexer_extreme_scales_and_strides():
 
 @pytest.mark.parametrize("B,N,k", [(1, 131072, 512), (4, 131072, 512), (1, 8192, 512), (3, 4096, 512),
                                    (2, 1000, 512), (2, 70000, 2048), (1, 100000, 1), (2, 50000, 300),
-                                   (2, 12000, 4096), (2, 16384, 512), (2, 16385, 512), (1, 5000, 4096)])
+                                   (2, 12000, 4096), (2, 16384, 512), (2, 16385, 512), (1, 5000, 4096),
+                                   (1, 200000, 4096)])
 def test_topk_same_logits_bit_exact(B, N, k):
     need_gpu()
     g = torch.Generator().manual_seed(N + k + B)
