@@ -448,6 +448,13 @@ __global__ __launch_bounds__(kT) void topk_filter_kernel(TopkParams p, int nch)
     nv = min(max(nv, 0), p.N);
     const TopkWs ws = topk_ws(p.workspace, p.B, nch);
 
+    // this chunk's keys load together with the sample below (one memory
+    // round trip for both)
+    constexpr int KPT = kChunk / kT;
+    uint32_t key[KPT];
+    const int64_t base = (int64_t)c * kChunk;
+    load_keys<KPT>(x, base, nv, key);
+
     // threshold from the fixed strided sample (identical in every chunk)
     uint32_t tau = 1u;
     if (nv > kSample) {
@@ -472,10 +479,6 @@ __global__ __launch_bounds__(kT) void topk_filter_kernel(TopkParams p, int nch)
     }
     if (c == 0 && tid == 0) ws.tau[b] = tau;
 
-    constexpr int KPT = kChunk / kT;
-    uint32_t key[KPT];
-    const int64_t base = (int64_t)c * kChunk;
-    load_keys<KPT>(x, base, nv, key);
     int n = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
@@ -515,6 +518,24 @@ __global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
     const TopkWs ws = topk_ws(p.workspace, p.B, nch);
     const int *cnt = ws.count + (size_t)b * nch;
 
+    // The first 64 entries of this wave's first SPC chunks load together
+    // with the counts (a slot holds kSlotCap >= 64 entries, so the reads stay
+    // inside it; entries past a chunk's count are never used).
+    constexpr int SPC = 4;
+    uint32_t sk[SPC];
+    int32_t sp[SPC];
+#pragma unroll
+    for (int r = 0; r < SPC; ++r) {
+        const int ci = w + r * kW;
+        sk[r] = 0u;
+        sp[r] = 0;
+        if (ci < nch) {
+            const size_t slot = ((size_t)b * nch + ci) * kSlotCap + lane;
+            sk[r] = ws.key[slot];
+            sp[r] = ws.pos[slot];
+        }
+    }
+
     // slot offsets in chunk (= position) order, in one scan: a chunk whose
     // slot overflowed counts kDirectMax + 1, which sends the row to the
     // streaming path (total < 2^27: kMaxChunks chunks of at most that)
@@ -545,15 +566,29 @@ __global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
         return;
     }
     __syncthreads();
-    // gather the slots into LDS, one wave per chunk
-    for (int ci = w; ci < nch; ci += kW) {
-        const int n = cnt[ci], at = offs[ci];
+    // gather the slots into LDS, one wave per chunk; a chunk's count is the
+    // difference of its offsets
+    auto gather_chunk = [&](int ci, int from) __attribute__((always_inline)) {
+        const int at = offs[ci], n = (ci + 1 < nch ? offs[ci + 1] : total) - at;
         const size_t slot = ((size_t)b * nch + ci) * kSlotCap;
-        for (int i = lane; i < n; i += kWave) {
+        for (int i = from + lane; i < n; i += kWave) {
             ckey[at + i] = ws.key[slot + i];
             cpos[at + i] = ws.pos[slot + i];
         }
+        return n;
+    };
+#pragma unroll
+    for (int r = 0; r < SPC; ++r) {
+        const int ci = w + r * kW;
+        if (ci < nch) {
+            const int n = gather_chunk(ci, kWave);   // entries past the first 64
+            if (lane < n) {
+                ckey[offs[ci] + lane] = sk[r];
+                cpos[offs[ci] + lane] = sp[r];
+            }
+        }
     }
+    for (int ci = w + SPC * kW; ci < nch; ci += kW) gather_chunk(ci, 0);
     __syncthreads();
     const int kk = min(p.k, total);
     // candidates in registers: 8 per thread when they fit (the usual case),
