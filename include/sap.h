@@ -184,7 +184,10 @@ int sap_indexer_logits_packed(const void *q, int64_t q_stride_b,
  * cand [T, NC] int32 (row stride cand_stride_t), n_keys [T] or NULL (no
  * bound), logits [T, NC] fp32.  1 <= Hi <= 32, D = 128, T <= 65535.
  * Candidate values below n_keys[t] must address rows inside the pool and
- * pages inside the page table (not checked on the device).
+ * pages inside the page table (not checked on the device).  With a page
+ * table and n_keys, the page-table row of token t must hold
+ * ceil(n_keys[t] / page) entries (the pages of its visible keys): up to 4096
+ * of them are staged on chip in one read.
  * Errors: SAP_ERR_NULL, SAP_ERR_ALIGN, SAP_ERR_SHAPE, SAP_ERR_LAUNCH.
  * ------------------------------------------------------------------------- */
 int sap_indexer_logits_candidates(const void *q, int64_t q_stride_t,

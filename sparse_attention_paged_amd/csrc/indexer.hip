@@ -248,9 +248,13 @@ __device__ __forceinline__ void lane_weights(const float *wr, int Hi, int hh, fl
 // the current one is scored.
 constexpr int kCandChunk = 8;
 
+// page-table entries of one sequence staged in LDS by the candidate kernel
+constexpr int kCandPtLds = 4096;
+
 __global__ __launch_bounds__(256) void indexer_cand_kernel(IndexerParams p)
 {
     __shared__ int rowtab[4][kCandChunk * kKeyTile];
+    __shared__ int ptab[kCandPtLds];
     const int t = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -273,21 +277,61 @@ __global__ __launch_bounds__(256) void indexer_cand_kernel(IndexerParams p)
     float *out = p.logits + (int64_t)t * p.logits_sb;
     int *rt = rowtab[wave];
 
-    for (int c0 = tile0; c0 < tile_end; c0 += kCandChunk) {
+    // candidate positions of chunk c0: (c0 + j) * 64 + lane, -1 = none
+    int cv[kCandChunk];
+    auto load_cand = [&](int c0) __attribute__((always_inline)) {
         const int nc = min(kCandChunk, tile_end - c0);
-        // pool row of candidate (c0 + j) * 64 + lane, -1 = none
-        int cv[kCandChunk];
 #pragma unroll
         for (int j = 0; j < kCandChunk; ++j) {
             const int c = (c0 + j) * kKeyTile + lane;
             cv[j] = (j < nc && c < p.N) ? cr[c] : -1;
         }
+    };
+    // The first chunk's candidates and, when the sequence's pages are known
+    // (n_keys), few enough and fewer than the workgroup's candidates, its
+    // page-table entries go out in the same memory round trip; rows are then
+    // found from LDS.
+    if (tile0 < tile_end) load_cand(tile0);
+    const int *pt_row = p.pt ? p.pt + (int64_t)t * p.pt_sb : nullptr;
+    const int64_t npg = p.pt && p.n_keys ? ((int64_t)max(nk, 0) + p.page - 1) / p.page : 0;
+    // (only when the workgroup's candidates outnumber the pages: a workgroup
+    // of a few tiles reads fewer entries looking each one up)
+    const bool pt_lds = p.pt && p.n_keys && npg <= kCandPtLds &&
+                        (int64_t)p.tiles_per_wave * kKeyTile * 4 >= npg;   // uniform over the workgroup
+    if (pt_lds) {
+        // every load goes out before any is written (a loop that waited for
+        // each load in turn made one round trip per entry group)
+        constexpr int PPT = kCandPtLds / 256;
+        int pv[PPT];
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int i = (int)threadIdx.x + 256 * k;
+            pv[k] = i < (int)npg ? pt_row[i] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int i = (int)threadIdx.x + 256 * k;
+            if (i < (int)npg) ptab[i] = pv[k];
+        }
+        __syncthreads();
+    }
+    const int psh = (p.page & (p.page - 1)) == 0 ? 31 - __builtin_clz((uint32_t)p.page) : -1;
+
+    for (int c0 = tile0; c0 < tile_end; c0 += kCandChunk) {
+        const int nc = min(kCandChunk, tile_end - c0);
+        if (c0 != tile0) load_cand(c0);
 #pragma unroll
         for (int j = 0; j < kCandChunk; ++j) {
             const int n = cv[j];
             int r = -1;
-            if (n >= 0 && n < nk)
-                r = p.pt ? p.pt[(int64_t)t * p.pt_sb + n / p.page] * p.page + n % p.page : n;
+            if (n >= 0 && n < nk) {
+                if (!p.pt) r = n;
+                else {
+                    const int pg = psh >= 0 ? n >> psh : n / p.page;
+                    const int off = psh >= 0 ? n & (p.page - 1) : n - pg * p.page;
+                    r = (pt_lds ? ptab[pg] : pt_row[pg]) * p.page + off;
+                }
+            }
             rt[j * kKeyTile + lane] = r;
         }
         wave_lds_sync();
