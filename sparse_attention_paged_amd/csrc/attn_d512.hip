@@ -25,9 +25,12 @@
 //    64 heads (128 accumulators); the V^T operand is read from the row-major
 //    tile with ds_read_b64_tr_b16.
 //  - pipeline: iteration i issues the gathers of tile i+3, computes S of tile
-//    i+1, then PV of tile i with the softmax of tile i+1 placed between its
-//    MFMAs, and ends with the one barrier that publishes tile i+1's weights
-//    and tile i+2's rows.
+//    i+1, then PV of tile i with the softmax of tile i+1 cut into pieces of a
+//    few VALU cycles, one after each PV MFMA (one wave per SIMD issues in
+//    order: a piece issues while the MFMA before it runs), and ends with the one barrier that publishes tile i+1's weights
+//    and tile i+2's rows.  Tile i's slow path, when taken, runs at the start
+//    of iteration i (after the first K reads of S are issued), so PV's
+//    weights and first V^T fragments can be read under the last S steps.
 //  - gathers: each wave moves 8 rows of a tile straight into LDS
 //    (global_load_lds_dwordx4 with a scalar row base and a per-lane 32-bit
 //    offset; one instruction = one 1 KiB row); the 8 row bases come from one
@@ -37,6 +40,7 @@
 #include "attn_common.hpp"
 
 #include <type_traits>
+#include <utility>
 
 namespace sap {
 namespace {
@@ -104,13 +108,29 @@ __device__ __forceinline__ void vm_wait4(int (&v)[4])
     asm volatile("s_waitcnt vmcnt(%4)" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]) : "n"(N) : "memory");
 }
 
-// 16 bytes from LDS straight into AGPRs (Q); the caller waits with
-// s_waitcnt lgkmcnt(0) before the first use
+// 16 bytes from LDS at addr + OFF straight into AGPRs (Q); the caller waits
+// with s_waitcnt lgkmcnt(0) before the first use
+template <int OFF>
 __device__ __forceinline__ bf16x8 lds_b128_agpr(uint32_t addr)
 {
     bf16x8 v;
-    asm volatile("ds_read_b128 %0, %1" : "=a"(v) : "v"(addr) : "memory");
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=a"(v) : "v"(addr), "n"(OFF) : "memory");
     return v;
+}
+// x, opaque to the compiler: values derived from it inside a loop are formed
+// there instead of being hoisted out and kept live across the loop
+__device__ __forceinline__ int opaque(int x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+// Q fragments s of head rows 32hg + 16jj + l16 (jj = 0, 1): qa[s % 4] + the
+// immediate offset of head tile jj and of chunk group s / 4
+template <size_t... S>
+__device__ __forceinline__ void load_q_frags(bf16x8 (&qf)[2][kSK], const uint32_t (&qa)[4], std::index_sequence<S...>)
+{
+    ((qf[0][S] = lds_b128_agpr<256 * (S / 4)>(qa[S % 4])), ...);
+    ((qf[1][S] = lds_b128_agpr<16 * 2 * kD + 256 * (S / 4)>(qa[S % 4])), ...);
 }
 // wait states between an MFMA's last write of a VGPR and a VALU read of it
 __device__ __forceinline__ void s_wait_mfma() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory"); }
@@ -158,13 +178,19 @@ void attn_d512_kernel(AttnParams p)
     // (16-byte chunk c of head row h at slot c ^ (h & 15)); tiles 0 and 1 stay
     // free for the first gathers.
     uint8_t *const qstage = &tiles[2][0];
+    // (h & 15 takes four values per wave, so four per-lane offsets serve
+    // all 16 heads of a wave)
     auto stage_q = [&](int tq) __attribute__((always_inline)) {
+        const int ln = opaque(lane);
+        uint32_t voff[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) voff[k] = 16u * (uint32_t)(ln ^ (kNW * k + w));
 #pragma unroll
         for (int k = 0; k < kAttnHeadsPerBlock / kNW; ++k) {
             const int h = kNW * k + w;
             const int head = hbase + h < p.H ? hbase + h : hbase;   // rows past H: finite stand-in
-            const uint16_t *src = p.q + (int64_t)tq * p.q_st + (int64_t)head * p.q_sh + 8 * (lane ^ (h & 15));
-            dma16(src, lds_offset(qstage + 1024 * h));
+            const uint64_t src = (uint64_t)(p.q + (int64_t)tq * p.q_st + (int64_t)head * p.q_sh);
+            dma_row(src, voff[k & 3], lds_offset(qstage + 1024 * h));
         }
     };
 
@@ -290,16 +316,6 @@ void attn_d512_kernel(AttnParams p)
 #pragma unroll
             for (int i = 0; i < 4; ++i) x[jj][i] = i < vmax ? (sa[jj][0][i] + sa[jj][1][i]) * sl2 : -INFINITY;
     };
-    // whether a head's tile max exceeds its running max by more than the slack
-    auto beyond = [&]() __attribute__((always_inline)) {
-        int fl = 0;
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const float tm = group4_max(fmaxf(fmaxf(x[jj][0], x[jj][1]), fmaxf(x[jj][2], x[jj][3])));
-            fl |= tm > m_own[jj] + kRescaleSlack ? 1 : 0;
-        }
-        return fl;
-    };
     // weights of head tile jj against its owned max, packed as bf16
     auto weights_of = [&](int jj) __attribute__((always_inline)) {
         const float msub = m_own[jj] == -INFINITY ? 0.0f : m_own[jj];
@@ -356,13 +372,14 @@ void attn_d512_kernel(AttnParams p)
     // S^T of the tile in LDS tile `buf`: sa[jj][e] = partial S^T[column 16cs +
     // 4g + i][head 32hg + 16jj + l16] over the k-steps s with s % 2 == e
     // (K fragments are read KD steps ahead; hook(s) runs between the MFMAs)
-    auto s_tile = [&](int buf, f32x4 (&sa)[2][2], auto hook) __attribute__((always_inline)) {
+    auto s_tile = [&](int buf, f32x4 (&sa)[2][2], auto before, auto hook) __attribute__((always_inline)) {
         const uint8_t *bf = &tiles[buf][0];
         auto kfrag = [&](int s) __attribute__((always_inline)) { return lds_b128(bf + kb[s & 1] + 128 * (s >> 1)); };
-        constexpr int KD = 3;
+        constexpr int KD = 6;
         uint4 f[KD];
 #pragma unroll
         for (int s = 0; s + 1 < KD; ++s) f[s] = kfrag(s);
+        before();
 #pragma unroll
         for (int s = 0; s < kSK; ++s) {
             if (s + KD - 1 < kSK) f[(s + KD - 1) % KD] = kfrag(s + KD - 1);
@@ -378,33 +395,47 @@ void attn_d512_kernel(AttnParams p)
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // O^T += V^T P^T for the tile in LDS tile `buf` with the weights in xp[par]
-    // (V^T fragments are read VD steps ahead; hook(m) runs between the MFMAs)
-    auto pv = [&](int buf, int par, auto hook) __attribute__((always_inline)) {
-        const uint8_t *bf = &tiles[buf][0];
-        auto vfrag = [&](int m) __attribute__((always_inline)) {
-            const uint2 v0 = lds_tr16(bf + vb[m & 3] + 128 * (m >> 2));
-            const uint2 v1 = lds_tr16(bf + vb[m & 3] + 16 * 2 * kD + 128 * (m >> 2));
-            return make_uint4(v0.x, v0.y, v1.x, v1.y);
-        };
+    // O^T += V^T P^T for the tile in LDS tile `buf` with the weights in xp[par].
+    // The weights and the first VD - 1 V^T fragments are read ahead (pv_pre,
+    // under the MFMAs of the S before it); later V^T fragments are read VD - 1
+    // steps ahead; hook(m) runs between the MFMAs.
+    constexpr int VD = 3;
+    struct PvPre {
         uint4 pb[4];
+        uint4 vr[VD - 1];
+    };
+    auto vfrag = [&](int buf, int m) __attribute__((always_inline)) {
+        const uint8_t *bf = &tiles[buf][0];
+        const uint2 v0 = lds_tr16(bf + vb[m & 3] + 128 * (m >> 2));
+        const uint2 v1 = lds_tr16(bf + vb[m & 3] + 16 * 2 * kD + 128 * (m >> 2));
+        return make_uint4(v0.x, v0.y, v1.x, v1.y);
+    };
+    auto load_pb = [&](int par, uint4 (&pb)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint2 a = xp[par][j][0][lane], b = xp[par][j][1][lane];
             pb[j] = make_uint4(a.x, a.y, b.x, b.y);
         }
-        constexpr int VD = 3;
+    };
+    auto pv_pre = [&](int buf, int par, PvPre &pre) __attribute__((always_inline)) {
+        load_pb(par, pre.pb);
+#pragma unroll
+        for (int m = 0; m + 1 < VD; ++m) pre.vr[m] = vfrag(buf, m);
+    };
+    auto pv = [&](int buf, const PvPre &pre, auto hook) __attribute__((always_inline)) {
         uint4 vr[VD];
 #pragma unroll
-        for (int m = 0; m + 1 < VD; ++m) vr[m] = vfrag(m);
+        for (int m = 0; m + 1 < VD; ++m) vr[m] = pre.vr[m];
 #pragma unroll
         for (int m = 0; m < kPM; ++m) {
-            if (m + VD - 1 < kPM) vr[(m + VD - 1) % VD] = vfrag(m + VD - 1);
+            if (m + VD - 1 < kPM) vr[(m + VD - 1) % VD] = vfrag(buf, m + VD - 1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) mfma_acc(acc[m][j], vr[m % VD], pb[j]);
-            hook(m);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int j = 0; j < 4; ++j) {
+                mfma_acc(acc[m][j], vr[m % VD], pre.pb[j]);
+                hook(4 * m + j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
@@ -425,7 +456,7 @@ void attn_d512_kernel(AttnParams p)
         __syncthreads();
         {
             f32x4 sa[2][2];
-            s_tile(0, sa, [](int) {});
+            s_tile(0, sa, [] {}, [](int) {});
             s_wait_mfma();
             scores(sa, 0);   // its maxima are agreed on in the slow path below
         }
@@ -440,38 +471,81 @@ void attn_d512_kernel(AttnParams p)
             constexpr bool G3 = decltype(g3_tag)::value, MORE = decltype(more_tag)::value;
             const int fw = xf[f0];
             if (tid == 0) xf[f2] = 0;   // tile i-1's word: tile i+2 sets it next iteration
+            // tile i: the first of the chunk, or a max beyond the slack (the
+            // slow path rewrites its weights before PV reads them)
+            auto check = [&]() __attribute__((always_inline)) {
+                const int any = i == 0 ? 1 : __builtin_amdgcn_readfirstlane(fw);
+                if (any) slow(i & 1);
+            };
             int e3 = -1;
             if constexpr (G3) e3 = row_entry(i + 3);
             f32x4 sa[2][2];
+            PvPre pre;
+            RowBases rb3{0, 0};
             if constexpr (MORE) {
                 // S of tile i+1; the row bases of tile i+3 are resolved after
-                // the first k-step and its rows go out one per step
-                RowBases rb3{0, 0};
-                s_tile((i + 1) & 3, sa, [&](int s) __attribute__((always_inline)) {
+                // the first k-step and its 8 rows go out spread over S and PV
+                // (one every 4 k-steps, then one every 8 PV MFMAs); PV's
+                // first operands are read during the last steps
+                s_tile((i + 1) & 3, sa, check, [&](int s) __attribute__((always_inline)) {
                     if constexpr (G3) {
                         if (s == 1) rb3 = row_bases(e3);
-                        if (s >= 2 && s < 2 + kRW) gather_row(rb3, (i + 3) & 3, s - 2);
+                        if ((s & 3) == 2) gather_row(rb3, (i + 3) & 3, s >> 2);
                     }
+                    if (s == kSK - 3) pv_pre(i & 3, i & 1, pre);
                 });
+            } else {
+                check();
+                pv_pre(i & 3, i & 1, pre);
             }
-            // tile i: the first of the chunk, or a max beyond the slack
-            const int any = i == 0 ? 1 : __builtin_amdgcn_readfirstlane(fw);
-            if (any) slow(i & 1);
             l_run[0] += psum[0];
             l_run[1] += psum[1];
-            // PV of tile i with the softmax of tile i+1 between its MFMAs
+            // PV of tile i with the softmax of tile i+1 cut into pieces of a
+            // few VALU cycles, one after each MFMA (the pieces issue while
+            // the MFMA runs)
             uint2 pk[2];
-            int fl = 0;
-            pv(i & 3, i & 1, [&](int m) __attribute__((always_inline)) {
+            int fl = 0, vmax = 0;
+            float tm[2], msub[2], pr[2][4];
+            pv(i & 3, pre, [&](int k) __attribute__((always_inline)) {
+                if constexpr (G3) {
+                    if ((k & 7) == 2) gather_row(rb3, (i + 3) & 3, 4 + (k >> 3));
+                }
                 if constexpr (MORE) {
-                    if (m == 1) {
+                    if (k == 1) {
                         s_wait_mfma();
-                        scores(sa, i + 1);
+                        vmax = nval - (i + 1) * kAttnTile - 16 * cs - 4 * g;
                     }
-                    if (m == 2) fl = beyond();
-                    if (m == 3) pk[0] = weights_of(0);
-                    if (m == 4) pk[1] = weights_of(1);
-                    if (m == 5) {
+                    if (k >= 1 && k <= 8) {   // scores (log2 domain)
+                        const int jj = (k - 1) >> 2, e = (k - 1) & 3;
+                        x[jj][e] = e < vmax ? (sa[jj][0][e] + sa[jj][1][e]) * sl2 : -INFINITY;
+                    }
+                    if (k == 9 || k == 12) {   // tile maxima and the slack check
+                        const int jj = (k - 9) / 3;
+                        tm[jj] = fmaxf(fmaxf(x[jj][0], x[jj][1]), fmaxf(x[jj][2], x[jj][3]));
+                    }
+                    if (k == 10 || k == 13) {
+                        const int jj = (k - 10) / 3;
+                        const uint32_t u = __float_as_uint(tm[jj]);
+                        const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+                        tm[jj] = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+                    }
+                    if (k == 11 || k == 14) {
+                        const int jj = (k - 11) / 3;
+                        const uint32_t u = __float_as_uint(tm[jj]);
+                        const auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+                        tm[jj] = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+                        fl |= tm[jj] > m_own[jj] + kRescaleSlack ? 1 : 0;
+                    }
+                    if (k >= 15 && k <= 22) {   // weights against the owned max
+                        const int jj = (k - 15) >> 2, e = (k - 15) & 3;
+                        if (e == 0) msub[jj] = m_own[jj] == -INFINITY ? 0.0f : m_own[jj];
+                        pr[jj][e] = fast_exp2(x[jj][e] - msub[jj]);
+                        if (e == 3) {
+                            psum[jj] = (pr[jj][0] + pr[jj][1]) + (pr[jj][2] + pr[jj][3]);
+                            pk[jj] = make_uint2(pack_bf16x2(pr[jj][0], pr[jj][1]), pack_bf16x2(pr[jj][2], pr[jj][3]));
+                        }
+                    }
+                    if (k == 23) {
                         put_weights((i + 1) & 1, pk);
                         if (lane == 0 && __builtin_amdgcn_ballot_w64(fl != 0) != 0) atomicOr(&xf[f1], 1);
                     }
@@ -550,12 +624,16 @@ void attn_d512_kernel(AttnParams p)
             if (n0 > 1) gather(1, 1);
             // (rows past H read the finite stand-in row staged for them; their
             // scores are never used)
+            // fragment s of head row 32hg + 16jj + l16 sits at chunk
+            // (4s + g) ^ l16 = 16(s / 4) + ((4(s % 4) + g) ^ l16): four
+            // per-lane bases and immediate offsets
+            {
+                const int ln = opaque(lane), q16 = ln & 15, qg = ln >> 4;
+                uint32_t qa[4];
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int hr = 32 * hg + 16 * jj + l16;
-                const uint32_t row = lds_offset(qstage) + (uint32_t)(hr * 2 * kD);
-#pragma unroll
-                for (int s = 0; s < kSK; ++s) qf[jj][s] = lds_b128_agpr(row + 16u * (uint32_t)((4 * s + g) ^ l16));
+                for (int u = 0; u < 4; ++u)
+                    qa[u] = lds_offset(qstage) + (uint32_t)((32 * hg + q16) * 2 * kD + 16 * ((4 * u + qg) ^ q16));
+                load_q_frags(qf, qa, std::make_index_sequence<kSK>{});
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __syncthreads();   // tiles 2 and 3 (q) are free
