@@ -352,7 +352,8 @@ void attn_d512_kernel(AttnParams p)
             const float mn = up ? mt : mr;
             alpha[J] = up ? fast_exp2(mr - mn) : 1.0f;   // 0 from -inf: O and the sums are still zero
             m_run[J] = mn;
-            if (__builtin_amdgcn_ballot_w64(alpha[J] != 1.0f) != 0) {
+            // (from -inf O is zero: nothing to rescale)
+            if (__builtin_amdgcn_ballot_w64(alpha[J] != 1.0f && mr != -INFINITY) != 0) {
 #pragma unroll
                 for (int m = 0; m < kPM; ++m) agpr_scale(acc[m][J], alpha[J]);
             }
@@ -611,6 +612,12 @@ void attn_d512_kernel(AttnParams p)
         for (int m = 0; m < kPM; ++m)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // the zeros are written here: the MFMAs that accumulate onto them
+        // are inline assembly, so the compiler would not keep the wait states
+        // a vector write needs before an MFMA reads it if it moved (or
+        // rematerialised) these writes next to the first PV
+#pragma unroll
+        for (int m = 0; m < kPM; ++m) asm volatile("" : "+a"(acc[m][0]), "+a"(acc[m][1]), "+a"(acc[m][2]), "+a"(acc[m][3]));
         m_run = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         m_own[0] = m_own[1] = -INFINITY;
         l_run[0] = l_run[1] = psum[0] = psum[1] = 0.0f;
