@@ -1,0 +1,108 @@
+"""The bf16 prefill kernel issues its MFMAs from inline assembly (to pin O and
+Q to AGPRs), so the compiler's hazard tracking does not see them: a vector
+write that the compiler places just before such an MFMA, into a register the
+MFMA reads, would get none of the wait states the hardware needs between the
+two, and the MFMA could read the register's old value.  This test compiles
+the kernel to gfx950 assembly (on the CPU) and checks that no register
+written by a VALU or AGPR-write instruction is read by an MFMA within a few
+instructions after the write.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "sparse_attention_paged_amd", "csrc")
+
+# Wait states (issued instructions, s_nop N counting N + 1) that must lie
+# between a write and an MFMA reading the written register.  The hardware
+# needs a few; the kernel keeps far more between every write it makes and
+# the MFMAs, so any compiler-placed write shows up here.
+AGPR_MIN = 8
+VGPR_MIN = 4
+
+
+def _regs(op: str, kind: str) -> set:
+    op = op.strip()
+    m = re.match(kind + r"\[(\d+):(\d+)\]$", op)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(kind + r"(\d+)$", op)
+    return {int(m.group(1))} if m else set()
+
+
+def _hazards(lines):
+    """(write line, mfma line, distance) for each write read too soon by an MFMA."""
+    code = [l.split(";")[0].strip() for l in lines]
+    found = []
+    for i, t in enumerate(code):
+        if not t.startswith("v_") or t.startswith(("v_mfma", "v_cmp", "v_readlane", "v_readfirstlane")):
+            continue
+        parts = t.split(None, 1)
+        if len(parts) < 2:
+            continue
+        dst = parts[1].split(",")[0]
+        agpr = _regs(dst, "a")
+        vgpr = _regs(dst, "v")
+        if not agpr and not vgpr:
+            continue
+        n = 0
+        for j in range(i + 1, min(len(code), i + 40)):
+            u = code[j]
+            if not u or u.startswith("."):
+                continue
+            if u.startswith("s_nop"):
+                n += int(u.split()[1]) + 1
+                continue
+            n += 1
+            if n >= max(AGPR_MIN, VGPR_MIN):
+                break
+            if u.startswith("v_mfma"):
+                ops = [o.strip() for o in u.split(None, 1)[1].split(",")]
+                srcs = set()
+                if agpr:
+                    srcs = set().union(*(_regs(o, "a") for o in ops[1:])) & agpr
+                    if srcs and n < AGPR_MIN:
+                        found.append((t, u, n))
+                if vgpr:
+                    srcs = set().union(*(_regs(o, "v") for o in ops[1:])) & vgpr
+                    if srcs and n < VGPR_MIN:
+                        found.append((t, u, n))
+    return found
+
+
+def test_hazard_scan_catches_a_planted_case():
+    """The scan itself: an AGPR write right before an MFMA that accumulates
+    into it, and a VGPR write right before an MFMA that reads it, are found;
+    the same pairs with enough wait states between them are not."""
+    bad = ["v_accvgpr_write_b32 a5, v7",
+           "v_mfma_f32_16x16x32_bf16 a[4:7], v[0:3], v[8:11], a[4:7]",
+           "v_add_f32_e32 v9, v1, v2",
+           "v_mfma_f32_16x16x32_bf16 a[12:15], v[0:3], v[8:11], a[12:15]"]
+    assert len(_hazards(bad)) == 2
+    good = ["v_accvgpr_write_b32 a5, v7", "s_nop 7",
+            "v_mfma_f32_16x16x32_bf16 a[4:7], v[0:3], v[8:11], a[4:7]",
+            "v_add_f32_e32 v9, v1, v2", "s_nop 3",
+            "v_mfma_f32_16x16x32_bf16 a[12:15], v[0:3], v[8:11], a[12:15]"]
+    assert _hazards(good) == []
+
+
+def test_prefill_kernel_has_no_write_next_to_an_asm_mfma(tmp_path):
+    hipcc = next((c for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc"))
+                  if c and os.path.exists(c)), None)
+    if hipcc is None:
+        pytest.skip("hipcc not available")
+    out = tmp_path / "attn_d512.s"
+    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "--cuda-device-only", "-S",
+           os.path.join(CSRC, "attn_d512.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = out.read_text().splitlines()
+    n_mfma = sum(1 for l in lines if l.strip().startswith("v_mfma"))
+    assert n_mfma > 100, "the kernel's MFMAs were not found in the assembly"
+    found = _hazards(lines)
+    assert not found, f"{len(found)} writes too close to an MFMA, e.g. {found[:3]}"
