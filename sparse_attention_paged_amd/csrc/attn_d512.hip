@@ -581,16 +581,16 @@ void attn_d512_kernel(AttnParams p)
         __syncthreads();
     };
 
-    // The q rows and the first index batch of a token go out together; for
-    // later tokens they go out before the previous token's output stores,
-    // so they land while those drain.  The index loads are untracked: the
-    // compiler would otherwise wait for every store before staging them.
-    // The store count of a full head block (32 per wave) stays in flight.
+    // A token's first index batch is loaded while the token before it runs
+    // its tiles (untracked loads: the compiler would otherwise wait for them
+    // at once; the tile loop's waits are stronger than theirs).  After that
+    // token's last tile, the token's q rows go out, its indices are staged
+    // and its first two tiles go out, and only then does the previous token
+    // write its output, so those loads land while the stores drain.
     int iv0[4];
     const int cn0 = min(c_end - c_begin, kIdxChunk);
-    auto first_loads = [&](int tq) __attribute__((always_inline)) {
-        if (c_end <= c_begin) return;
-        stage_q(tq);
+    const bool cols = c_end > c_begin;
+    auto load_idx0 = [&](int tq) __attribute__((always_inline)) {
         const int32_t *row = p.idx + (int64_t)tq * p.idx_st + c_begin;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -598,16 +598,30 @@ void attn_d512_kernel(AttnParams p)
             iv0[u] = gload_untracked(row + (i < cn0 ? i : 0));
         }
     };
-    auto first_batch = [&](bool after_stores) __attribute__((always_inline)) {
-        if (after_stores && hbase + kAttnHeadsPerBlock <= p.H) vm_wait4<kPM * 4>(iv0);
-        else vm_wait4<0>(iv0);
+    // token tq's indices are in iv0: stage them and send its first two tiles
+    auto begin_token = [&](int tq) __attribute__((always_inline)) {
+        idx_row = p.idx + (int64_t)tq * p.idx_st;
+        safe_src = (uint64_t)(p.q + (int64_t)tq * p.q_st);
 #pragma unroll
         for (int u = 0; u < 4; ++u) iv0[u] = 4 * tid + u < cn0 ? iv0[u] : -1;
+        stage_chunk(c_begin, iv0);
+        if (n_tiles > 0) gather(0, 0);
+        if (n_tiles > 1) gather(1, 1);
     };
-    if (t < tend) first_loads(t);
-    for (bool later = false; t < tend; t += tstep, later = true) {
-        idx_row = p.idx + (int64_t)t * p.idx_st;
-        safe_src = (uint64_t)(p.q + (int64_t)t * p.q_st);
+    if (t < tend && cols) {
+        stage_q(t);
+        load_idx0(t);
+        vm_wait4<0>(iv0);
+        begin_token(t);
+    }
+    for (; t < tend; t += tstep) {
+        const int tn = t + tstep;
+        const bool next = tn < tend && cols;
+        // the loads issued since this token's q rows: its first two tiles
+        // (and no further index batch), the previous token's 32 output
+        // stores and the next token's 4 index loads; otherwise wait for all
+        const bool full = n_tiles > 1 && cn0 <= 4 * kNT && hbase + kAttnHeadsPerBlock <= p.H && next;
+        if (next) load_idx0(tn);
 #pragma unroll
         for (int m = 0; m < kPM; ++m)
 #pragma unroll
@@ -621,14 +635,13 @@ void attn_d512_kernel(AttnParams p)
         m_run = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         m_own[0] = m_own[1] = -INFINITY;
         l_run[0] = l_run[1] = psum[0] = psum[1] = 0.0f;
-        if (c_end > c_begin) {
-            // first chunk: its first two tiles go out while the q fragments
-            // are read
-            first_batch(later);
-            stage_chunk(c_begin, iv0);
+        if (cols) {
+            // the first chunk is staged and its first two tiles are in
+            // flight; the q rows must have landed before their fragments are
+            // read
             const int n0 = n_tiles;
-            if (n0 > 0) gather(0, 0);
-            if (n0 > 1) gather(1, 1);
+            if (full) wait_vm<2 * kRW + kPM * 4 + 4>();
+            else wait_vm<0>();
             // (rows past H read the finite stand-in row staged for them; their
             // scores are never used)
             // fragment s of head row 32hg + 16jj + l16 sits at chunk
@@ -652,14 +665,19 @@ void attn_d512_kernel(AttnParams p)
                 if (n_tiles > 0) run_chunk(false);
             }
         }
-        wait_vm<0>();   // no transfer into LDS is left (and none outlives the workgroup)
+        // no transfer into LDS is left (and none outlives the workgroup); the
+        // next token's first indices have landed
+        vm_wait4<0>(iv0);
         // wait states between the last accumulating MFMA (inline assembly, which
         // the compiler's hazard tracking does not see) and the reads of O below
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
         // every wave is past its last read of the tiles and of sidx: the next
-        // token's q rows and first indices go out now
+        // token's q rows and first two tiles go out now
         __syncthreads();
-        if (t + tstep < tend) first_loads(t + tstep);
+        if (next) {
+            stage_q(tn);
+            begin_token(tn);
+        }
         // softmax sums: owners reduce over their columns, everyone adds the two
         // column halves of each head in a fixed order
 #pragma unroll

@@ -106,3 +106,49 @@ def test_prefill_kernel_has_no_write_next_to_an_asm_mfma(tmp_path):
     assert n_mfma > 100, "the kernel's MFMAs were not found in the assembly"
     found = _hazards(lines)
     assert not found, f"{len(found)} writes too close to an MFMA, e.g. {found[:3]}"
+
+
+def _early_reads(lines):
+    """Loads issued from inline assembly with no compiler tracking
+    ("global_load_dword vN, vaddr, off"): their destination must not be read or
+    written before an s_waitcnt vmcnt(0) (the kernel ties the values to such a
+    wait); a compiler copy of the register before that would copy the old
+    value."""
+    code = [l.split(";")[0].strip() for l in lines]
+    found = []
+    for i, t in enumerate(code):
+        if not (t.startswith("global_load_dword ") and t.endswith(", off")):
+            continue
+        dst = _regs(t.split(None, 1)[1].split(",")[0], "v")
+        for j in range(i + 1, len(code)):
+            u = code[j]
+            if not u or u.startswith("."):
+                continue
+            if u.startswith("s_waitcnt") and "vmcnt(0)" in u:
+                break
+            parts = u.split(None, 1)
+            if len(parts) == 2 and set().union(*(_regs(o, "v") for o in parts[1].split(","))) & dst:
+                found.append((t, u))
+                break
+    return found
+
+
+def test_untracked_loads_untouched_until_waited(tmp_path):
+    hipcc = next((c for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc"))
+                  if c and os.path.exists(c)), None)
+    if hipcc is None:
+        pytest.skip("hipcc not available")
+    assert len(_early_reads(["global_load_dword v4, v[2:3], off", "v_mov_b32_e32 v9, v4",
+                             "s_waitcnt vmcnt(0)"])) == 1
+    assert _early_reads(["global_load_dword v4, v[2:3], off", "s_waitcnt vmcnt(0)",
+                         "v_mov_b32_e32 v9, v4"]) == []
+    out = tmp_path / "attn_d512.s"
+    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "--cuda-device-only", "-S",
+           os.path.join(CSRC, "attn_d512.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = out.read_text().splitlines()
+    assert sum(1 for l in lines if l.strip().startswith("global_load_dword ") and l.strip().endswith(", off")) >= 4
+    found = _early_reads(lines)
+    assert not found, f"{len(found)} untracked load results used before their wait, e.g. {found[:3]}"
