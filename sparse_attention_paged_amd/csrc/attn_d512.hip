@@ -443,7 +443,10 @@ void attn_d512_kernel(AttnParams p)
     // one chunk of columns whose indices are staged in sidx: prologue (tiles
     // 0 .. 2 in flight, S of tile 0), then the tile loop.  Tiles 0 and 1 may
     // have been issued already.
-    auto run_chunk = [&](bool issued01) __attribute__((always_inline)) {
+    // full: tiles 0 and 1 were issued before the previous token's 32 output
+    // stores and the next token's 4 index loads (the waits for tiles 0 and 1
+    // then leave those in flight)
+    auto run_chunk = [&](bool issued01, bool full) __attribute__((always_inline)) {
         const int n = n_tiles;
         if (!issued01) {
             gather(0, 0);
@@ -451,7 +454,10 @@ void attn_d512_kernel(AttnParams p)
         }
         if (n > 2) gather(2, 2);
         if (tid < 3) xf[tid] = 0;
-        if (n > 2) wait_vm<2 * kRW>();
+        constexpr int kAfter = kPM * 4 + 4;   // stores and index loads after tile 1
+        if (full && n > 2) wait_vm<2 * kRW + kAfter>();
+        else if (full) wait_vm<kRW + kAfter>();
+        else if (n > 2) wait_vm<2 * kRW>();
         else if (n > 1) wait_vm<kRW>();
         else wait_vm<0>();
         __syncthreads();
@@ -461,7 +467,9 @@ void attn_d512_kernel(AttnParams p)
             s_wait_mfma();
             scores(sa, 0);   // its maxima are agreed on in the slow path below
         }
-        if (n > 2) wait_vm<kRW>();
+        if (full && n > 2) wait_vm<kRW + kAfter>();
+        else if (full) wait_vm<kAfter>();
+        else if (n > 2) wait_vm<kRW>();
         else wait_vm<0>();
         __syncthreads();
         int f0 = 0, f1 = 1, f2 = 2;   // flag slots of tiles i, i+1, i+2
@@ -614,13 +622,14 @@ void attn_d512_kernel(AttnParams p)
         vm_wait4<0>(iv0);
         begin_token(t);
     }
-    for (; t < tend; t += tstep) {
+    for (bool later = false; t < tend; t += tstep, later = true) {
         const int tn = t + tstep;
         const bool next = tn < tend && cols;
         // the loads issued since this token's q rows: its first two tiles
         // (and no further index batch), the previous token's 32 output
-        // stores and the next token's 4 index loads; otherwise wait for all
-        const bool full = n_tiles > 1 && cn0 <= 4 * kNT && hbase + kAttnHeadsPerBlock <= p.H && next;
+        // stores (the first token has none) and the next token's 4 index
+        // loads; otherwise wait for all
+        const bool full = later && n_tiles > 1 && cn0 <= 4 * kNT && hbase + kAttnHeadsPerBlock <= p.H && next;
         if (next) load_idx0(tn);
 #pragma unroll
         for (int m = 0; m < kPM; ++m)
@@ -657,12 +666,12 @@ void attn_d512_kernel(AttnParams p)
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __syncthreads();   // tiles 2 and 3 (q) are free
-            if (n0 > 0) run_chunk(true);
+            if (n0 > 0) run_chunk(true, full);
             for (int cc = c_begin + kIdxChunk; cc < c_end; cc += kIdxChunk) {
                 int iv[4];
                 load4(cc, min(c_end - cc, kIdxChunk), 0, iv);
                 stage_chunk(cc, iv);
-                if (n_tiles > 0) run_chunk(false);
+                if (n_tiles > 0) run_chunk(false, false);
             }
         }
         // no transfer into LDS is left (and none outlives the workgroup); the
