@@ -789,7 +789,7 @@ void attn_kernel(AttnParams p)
 template <int D, int OUT, int NW>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p)
 {
-    constexpr int U = 16;
+    constexpr int U = kMergeSplits;
     constexpr int PM = D / (16 * NW);   // the split kernel's m-steps per wave
     const int t = blockIdx.x;
     const int grp = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;

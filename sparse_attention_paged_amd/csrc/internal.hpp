@@ -30,6 +30,10 @@ struct AttnParams {
     float *part_ml;                  // [T, S, H, 2] running max (log2 domain), sum
 };
 
+// splits whose partial outputs the merge reads in one memory round trip
+// (more take further passes)
+constexpr int kMergeSplits = 16;
+
 // kv: 0 = bf16, 2 = e4m3.  out: 0 = bf16, 1 = f32.
 hipError_t launch_attn(const AttnParams &p, int D, int kv, int out_dtype, hipStream_t s);
 hipError_t launch_attn_merge(const AttnParams &p, int D, int kv, int out_dtype, hipStream_t s);

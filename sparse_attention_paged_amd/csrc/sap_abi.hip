@@ -33,9 +33,12 @@ SplitPlan plan_splits(int T, int H, int n_cols, int requested)
         const int hb = (H + sap::kAttnHeadsPerBlock - 1) / sap::kAttnHeadsPerBlock;
         const int64_t wgs = (int64_t)T * hb;
         s = wgs >= 128 ? 1 : (int)((160 + wgs - 1) / wgs);
-        // a split's fixed cost (its q, index and first-gather round trips,
-        // its partial output) is worth about two tiles of columns
-        if (s > (tiles + 1) / 2) s = (tiles + 1) / 2;
+        // one 32-column tile per split is fastest as long as the merge reads
+        // every split in one round trip; past that, the fewest tiles per
+        // split that keep the splits within it (measured at decode B1 and B8:
+        // r0 with 4 splits, r128 with 12 and r4 with 10, against 2, 6 and 10
+        // with two tiles per split, 12 % / 10 % / 0 % faster)
+        if (s > sap::kMergeSplits) s = sap::kMergeSplits;
     }
     if (s > tiles) s = tiles;
     if (s < 1) s = 1;

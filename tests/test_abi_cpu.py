@@ -85,10 +85,12 @@ def test_attention_argument_checks(L):
 def test_split_planning(L):
     ns = L.sap_sparse_attn_num_splits
     assert ns(8192, 64, 512, 640, 0) == 1            # prefill: one pass per token
-    assert ns(1, 64, 512, 640, 0) == 10              # decode B1: two 32-column tiles per split
+    assert ns(1, 64, 512, 640, 0) == 10              # decode B1: 20 tiles, at most 16 splits: two tiles each
     assert ns(8, 64, 512, 640, 0) == 10
-    assert ns(1, 64, 512, 128, 0) == 2
-    assert ns(1, 64, 512, 40, 0) == 1                # two tiles: one split
+    assert ns(1, 64, 512, 384, 0) == 12              # 12 tiles: one per split
+    assert ns(1, 64, 512, 128, 0) == 4
+    assert ns(1, 64, 512, 40, 0) == 2                # two tiles (the second partial): two splits
+    assert ns(64, 64, 512, 640, 0) == 3              # 64 workgroups per split: 3 splits of 7 tiles
     assert ns(1, 64, 512, 640, 7) == 7
     assert ns(1, 64, 512, 640, 100) == 20            # never more splits than tiles
     assert ns(1, 64, 512, 0, 0) == 1
