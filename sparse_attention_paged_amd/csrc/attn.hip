@@ -783,13 +783,12 @@ void attn_kernel(AttnParams p)
 // x 4 floats (NW split-kernel waves): one wave of this kernel takes one
 // (head block, w, m, j) group, lane l owning head 16j + l%16 and head_dim
 // 16m + 4(l/16) .. +3 of the split wave's range w,
-// so its partial loads are 1 KiB contiguous per split.  The loads of up to 16
-// splits are issued before any is used (one memory round trip at the usual
-// split counts).
-template <int D, int OUT, int NW>
+// so its partial loads are 1 KiB contiguous per split.  The loads of U splits
+// are issued before any is used: one memory round trip when the launch picks
+// a U of at least the split count (up to kMergeSplits).
+template <int D, int OUT, int NW, int U>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p)
 {
-    constexpr int U = kMergeSplits;
     constexpr int PM = D / (16 * NW);   // the split kernel's m-steps per wave
     const int t = blockIdx.x;
     const int grp = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -870,8 +869,20 @@ hipError_t launch_merge_t(const AttnParams &p, int out, hipStream_t s)
     const int HB = (p.H + kAttnHeadsPerBlock - 1) / kAttnHeadsPerBlock;
     // (HB * NW * PMW * 4 groups, 4 per workgroup; NW * PMW = D / 16)
     const dim3 grid((unsigned)p.T, (unsigned)(HB * (D / 16)));
-    if (out == 1) hipLaunchKernelGGL((attn_merge_kernel<D, 1, NW>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((attn_merge_kernel<D, 0, NW>), grid, dim3(256), 0, s, p);
+    // the smallest batch of the split count (unused slots of a batch repeat
+    // the last split's loads)
+    auto go = [&](auto u_tag) {
+        constexpr int U = decltype(u_tag)::value;
+        if (out == 1) hipLaunchKernelGGL((attn_merge_kernel<D, 1, NW, U>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((attn_merge_kernel<D, 0, NW, U>), grid, dim3(256), 0, s, p);
+    };
+    const int S = p.num_splits;
+    if (S <= 4) go(std::integral_constant<int, 4>{});
+    else if (S <= 8) go(std::integral_constant<int, 8>{});
+    else if (S <= 12) go(std::integral_constant<int, 12>{});
+    else if (S <= 16) go(std::integral_constant<int, 16>{});
+    else if (S <= 20) go(std::integral_constant<int, 20>{});
+    else go(std::integral_constant<int, kMergeSplits>{});
     return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ struct AttnParams {
 
 // splits whose partial outputs the merge reads in one memory round trip
 // (more take further passes)
-constexpr int kMergeSplits = 16;
+constexpr int kMergeSplits = 24;
 
 // kv: 0 = bf16, 2 = e4m3.  out: 0 = bf16, 1 = f32.
 hipError_t launch_attn(const AttnParams &p, int D, int kv, int out_dtype, hipStream_t s);

@@ -32,12 +32,13 @@ SplitPlan plan_splits(int T, int H, int n_cols, int requested)
     } else {
         const int hb = (H + sap::kAttnHeadsPerBlock - 1) / sap::kAttnHeadsPerBlock;
         const int64_t wgs = (int64_t)T * hb;
-        s = wgs >= 128 ? 1 : (int)((160 + wgs - 1) / wgs);
-        // one 32-column tile per split is fastest as long as the merge reads
-        // every split in one round trip; past that, the fewest tiles per
-        // split that keep the splits within it (measured at decode B1 and B8:
-        // r0 with 4 splits, r128 with 12 and r4 with 10, against 2, 6 and 10
-        // with two tiles per split, 12 % / 10 % / 0 % faster)
+        // one 32-column tile per split is fastest while the launch stays
+        // within about 128 workgroups and the merge reads every split in one
+        // round trip; past that, the fewest tiles per split that keep within
+        // both (measured at decode B1 and B8: one sequence takes 4, 12 and 20
+        // splits at r0, r128 and r4 where two tiles per split gave 2, 6 and
+        // 10; eight take 10 at r4)
+        s = wgs >= 128 ? 1 : (int)(128 / wgs);
         if (s > sap::kMergeSplits) s = sap::kMergeSplits;
     }
     if (s > tiles) s = tiles;

@@ -85,12 +85,13 @@ def test_attention_argument_checks(L):
 def test_split_planning(L):
     ns = L.sap_sparse_attn_num_splits
     assert ns(8192, 64, 512, 640, 0) == 1            # prefill: one pass per token
-    assert ns(1, 64, 512, 640, 0) == 10              # decode B1: 20 tiles, at most 16 splits: two tiles each
-    assert ns(8, 64, 512, 640, 0) == 10
-    assert ns(1, 64, 512, 384, 0) == 12              # 12 tiles: one per split
+    assert ns(1, 64, 512, 640, 0) == 20              # decode B1: one 32-column tile per split
+    assert ns(8, 64, 512, 640, 0) == 10              # B8: at most 16 splits (128 workgroups): two tiles each
+    assert ns(1, 64, 512, 384, 0) == 12
     assert ns(1, 64, 512, 128, 0) == 4
     assert ns(1, 64, 512, 40, 0) == 2                # two tiles (the second partial): two splits
-    assert ns(64, 64, 512, 640, 0) == 3              # 64 workgroups per split: 3 splits of 7 tiles
+    assert ns(64, 64, 512, 640, 0) == 2              # 64 workgroups per split: 2 splits of 10 tiles
+    assert ns(1, 64, 512, 32 * 40, 0) == 20          # 40 tiles: at most 24 splits (one merge pass): two each
     assert ns(1, 64, 512, 640, 7) == 7
     assert ns(1, 64, 512, 640, 100) == 20            # never more splits than tiles
     assert ns(1, 64, 512, 0, 0) == 1
