@@ -34,9 +34,11 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__global__ __launch_bounds__(256) void indexer_kernel(IndexerParams p)
+// NWI waves per workgroup (1 or 4)
+template <int NWI>
+__global__ __launch_bounds__(64 * NWI) void indexer_kernel(IndexerParams p)
 {
-    __shared__ __attribute__((aligned(16))) uint32_t stage[4][kTileWords];
+    __shared__ __attribute__((aligned(16))) uint32_t stage[NWI][kTileWords];
     const int b = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerParams p)
     }
 
     const int n_tiles = (p.N + kKeyTile - 1) / kKeyTile;
-    const int tile0 = (blockIdx.x * 4 + wave) * p.tiles_per_wave;
+    const int tile0 = (blockIdx.x * NWI + wave) * p.tiles_per_wave;
     uint32_t *st = stage[wave];
     uint32_t regs[kWordsPerLane];
 
@@ -533,9 +535,16 @@ hipError_t launch_indexer(const IndexerParams &p, hipStream_t s)
 {
     const int n_tiles = (p.N + kKeyTile - 1) / kKeyTile;
     const int waves = (n_tiles + p.tiles_per_wave - 1) / p.tiles_per_wave;
-    const unsigned gx = (unsigned)((waves + 3) / 4);
-    if (gx == 0 || p.B == 0) return hipSuccess;
-    hipLaunchKernelGGL(indexer_kernel, dim3(gx, (unsigned)p.B), dim3(256), 0, s, p);
+    if (waves == 0 || p.B == 0) return hipSuccess;
+    // a launch of at most one wave per CU spreads its waves over as many CUs
+    // (decode B1 over 8192 keys: 4.35 us against 4.7 with four-wave
+    // workgroups); larger launches keep four waves per workgroup
+    if ((int64_t)waves * p.B <= 256) {
+        hipLaunchKernelGGL(indexer_kernel<1>, dim3((unsigned)waves, (unsigned)p.B), dim3(64), 0, s, p);
+    } else {
+        const unsigned gx = (unsigned)((waves + 3) / 4);
+        hipLaunchKernelGGL(indexer_kernel<4>, dim3(gx, (unsigned)p.B), dim3(256), 0, s, p);
+    }
     return hipGetLastError();
 }
 
