@@ -786,12 +786,12 @@ void attn_kernel(AttnParams p)
 // so its partial loads are 1 KiB contiguous per split.  The loads of U splits
 // are issued before any is used: one memory round trip when the launch picks
 // a U of at least the split count (up to kMergeSplits).
-template <int D, int OUT, int NW, int U>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p)
+template <int D, int OUT, int NW, int U, int WPB>   // WPB waves per workgroup
+__global__ __launch_bounds__(64 * WPB) void attn_merge_kernel(AttnParams p)
 {
     constexpr int PM = D / (16 * NW);   // the split kernel's m-steps per wave
     const int t = blockIdx.x;
-    const int grp = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int grp = blockIdx.y * WPB + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int HB = (p.H + kAttnHeadsPerBlock - 1) / kAttnHeadsPerBlock;
     if (grp >= HB * NW * PM * 4) return;
     const int j = grp % 4, m = (grp / 4) % PM, w = (grp / (4 * PM)) % NW, hb = grp / (4 * NW * PM);
@@ -868,13 +868,21 @@ hipError_t launch_merge_t(const AttnParams &p, int out, hipStream_t s)
     // one wave per (head block, w, m, j) group of the partial layout
     const int HB = (p.H + kAttnHeadsPerBlock - 1) / kAttnHeadsPerBlock;
     // (HB * NW * PMW * 4 groups, 4 per workgroup; NW * PMW = D / 16)
-    const dim3 grid((unsigned)p.T, (unsigned)(HB * (D / 16)));
+    // a launch of at most one wave per CU takes one-wave workgroups (its
+    // waves land on as many CUs), larger ones four waves per workgroup
+    const bool one = (int64_t)p.T * HB * (D / 16) * 4 <= 256;
+    const dim3 grid((unsigned)p.T, (unsigned)(HB * (D / 16) * (one ? 4 : 1)));
     // the smallest batch of the split count (unused slots of a batch repeat
     // the last split's loads)
     auto go = [&](auto u_tag) {
         constexpr int U = decltype(u_tag)::value;
-        if (out == 1) hipLaunchKernelGGL((attn_merge_kernel<D, 1, NW, U>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((attn_merge_kernel<D, 0, NW, U>), grid, dim3(256), 0, s, p);
+        if (one) {
+            if (out == 1) hipLaunchKernelGGL((attn_merge_kernel<D, 1, NW, U, 1>), grid, dim3(64), 0, s, p);
+            else hipLaunchKernelGGL((attn_merge_kernel<D, 0, NW, U, 1>), grid, dim3(64), 0, s, p);
+        } else {
+            if (out == 1) hipLaunchKernelGGL((attn_merge_kernel<D, 1, NW, U, 4>), grid, dim3(256), 0, s, p);
+            else hipLaunchKernelGGL((attn_merge_kernel<D, 0, NW, U, 4>), grid, dim3(256), 0, s, p);
+        }
     };
     const int S = p.num_splits;
     if (S <= 4) go(std::integral_constant<int, 4>{});
