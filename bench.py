@@ -378,7 +378,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(each GPU would run its own sequences with no exchange)", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
