@@ -260,3 +260,22 @@ def test_determinism_sha256():
             out = gpu_attn(case, idx=gidx, num_splits=splits)
             h.add(hashlib.sha256(out.cpu().numpy().tobytes()).hexdigest())
         assert len(h) == 1, case.name
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_decode_merge_batches(B):
+    """Split counts that take the merge batches of 16 and 24 splits (the
+    launch picks the smallest batch that holds the split count), with
+    one-wave merge workgroups (B1) and four-wave ones (B8): 1472 columns
+    (46 tiles) in 16 splits of 3 tiles and 23 of 2, and the automatic count
+    (23 splits at B1, 16 at B8)."""
+    need_gpu()
+    case = W.decode_case(B=B, topk=1344, seed=W.SEED_BASE + 130 + B)
+    idx = oracle.case_idx(case)
+    ref = oracle.case_attn(case, idx=idx)
+    gidx = gpu_idx(case)
+    for splits in (16, 23, 0):
+        runs = sap.sparse_attn_num_splits(case.T, 64, 512, idx.shape[1], splits)
+        say(f"  B{B} {idx.shape[1]} columns: {splits} splits requested, {runs} run")
+        out = gpu_attn(case, idx=gidx, num_splits=splits)
+        assert_attn_close(out, ref, f"B{B} splits={splits} (runs {runs})")
