@@ -155,15 +155,19 @@ void attn_d512_kernel(AttnParams p)
 
     // Tokens of this workgroup (all of a token's columns, one head block).
     // A grid of fewer workgroups than tokens is persistent and XCD-aware:
-    // XCD x = blockIdx.x % 8 takes the contiguous token range [T x/8,
-    // T (x+1)/8) and its workgroups interleave over it, so consecutive tokens
-    // (which share window rows) run at the same time on one XCD's L2.
+    // the grid takes the tokens in rounds of gridDim.x, and in each round
+    // XCD x = blockIdx.x % 8 takes the 1/8 block of consecutive tokens
+    // x per .. x per + per - 1 (per = its workgroup count), so consecutive
+    // tokens (which share window rows) run at the same time on one XCD's
+    // L2, and every XCD gets tokens from the whole range (early tokens have
+    // fewer columns: contiguous eighths of the range left the XCD with the
+    // last eighth working longest).
     int t0 = blockIdx.x, tstep = 1, tend = blockIdx.x + 1;
     if ((int)gridDim.x < p.T) {
         const int x = blockIdx.x & 7, per = (int)gridDim.x >> 3;
-        t0 = (int)((int64_t)p.T * x / 8) + (blockIdx.x >> 3);
-        tend = (int)((int64_t)p.T * (x + 1) / 8);
-        tstep = per;
+        t0 = x * per + (blockIdx.x >> 3);
+        tend = p.T;
+        tstep = (int)gridDim.x;
     }
     const int c_begin = 0, c_end = p.n_cols;
 
