@@ -261,9 +261,16 @@ int sap_gated_pool(const void *x, sap_dtype x_dtype, int64_t x_stride_b, int64_t
  * indices are written in ascending order, padded with -1.
  *
  * logits: [B, N] fp32 (row stride stride_b).  out_idx: [B, k] int32 (row
- * stride out_stride_b).  workspace: sap_topk_workspace_bytes(B, N, k) bytes
- * (currently 0: one workgroup selects one row entirely in LDS; the argument
- * is kept so a larger scheme can be adopted without an ABI change).
+ * stride out_stride_b).
+ * workspace: device memory of sap_topk_workspace_bytes(B, N, k) bytes,
+ *   256-byte aligned.  Rows of up to 16384 entries are selected by one
+ *   workgroup entirely on chip and need none (size 0, NULL allowed).  Longer
+ *   rows take two launches: a filter launch in which each 4096-entry chunk of
+ *   a row compacts its keys above a sampled threshold into a slot of the
+ *   workspace, then a select launch over the slots.  With nch =
+ *   ceil(N / 4096) the size is then a(4 B nch) + a(4 B) + 2 a(8192 B nch)
+ *   bytes, a() rounding up to a multiple of 256 (about 512 KiB per row at
+ *   N = 131072).
  * Limits: 1 <= k <= 4096, 0 <= N < 2^31.
  * Errors: SAP_ERR_NULL, SAP_ERR_SHAPE, SAP_ERR_WORKSPACE, SAP_ERR_LAUNCH.
  * ------------------------------------------------------------------------- */
@@ -287,7 +294,9 @@ int sap_topk_select(const float *logits, int64_t stride_b, const int32_t *n_vali
  * sap_topk_select (n_valid may be NULL); pos, seq: [T] int32; page tables as
  * for sap_build_sparse_idx (cmp_pt required, win_pt when n_win > 0);
  * idx: [T, >= n_win + k] int32.  workspace: sap_topk_workspace_bytes(T, N, k)
- * bytes.  Limits as sap_topk_select.
+ * bytes, 256-byte aligned: zero for N <= 16384 (the decode step's 8192
+ * compressed entries), else the two-launch filter/select slots described
+ * for sap_topk_select.  Limits as sap_topk_select.
  * Errors: SAP_ERR_NULL, SAP_ERR_ALIGN, SAP_ERR_SHAPE, SAP_ERR_WORKSPACE,
  * SAP_ERR_LAUNCH.
  * ------------------------------------------------------------------------- */

@@ -29,6 +29,16 @@ def _p(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _ws(workspace: Optional[torch.Tensor]):
+    """(pointer, size in bytes) of a caller's workspace; the ABI wants it
+    256-byte aligned."""
+    if workspace is None:
+        return None, 0
+    if workspace.data_ptr() % 256:
+        raise ValueError("workspace must be 256-byte aligned")
+    return _p(workspace), workspace.numel() * workspace.element_size()
+
+
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -101,8 +111,7 @@ def sparse_attn_paged(q, win_pool, cmp_pool, idx, n_win: int, sm_scale: float, *
         _p(win_scale), _p(cmp_scale),
         _p(out), _out_dtype(out.dtype), out.stride(0), out.stride(1),
         T, H, D, float(sm_scale), int(num_splits),
-        _p(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
-        _stream(q))
+        *_ws(workspace), _stream(q))
     check(rc, "sap_sparse_attn_paged")
     return out
 
@@ -197,8 +206,8 @@ def topk_select(logits, k: int, n_valid=None, out=None, workspace=None) -> torch
     if need > 0 and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
     rc = lib().sap_topk_select(
-        _p(logits), logits.stride(0), _p(n_valid), B, N, k, _p(out), out.stride(0), _p(workspace),
-        0 if workspace is None else workspace.numel(), _stream(logits))
+        _p(logits), logits.stride(0), _p(n_valid), B, N, k, _p(out), out.stride(0), *_ws(workspace),
+        _stream(logits))
     check(rc, "sap_topk_select")
     return out
 
@@ -217,7 +226,7 @@ def topk_sparse_idx(logits, k: int, pos, seq, n_win: int, win_pt, cmp_pt, page: 
     rc = lib().sap_topk_sparse_idx(
         _p(logits), logits.stride(0), _p(n_valid), T, N, k, _p(pos), _p(seq), n_win,
         _p(win_pt), win_pt.stride(0) if win_pt is not None else 0, _p(cmp_pt), cmp_pt.stride(0), page,
-        _p(out), out.stride(0), _p(workspace), 0 if workspace is None else workspace.numel(), _stream(logits))
+        _p(out), out.stride(0), *_ws(workspace), _stream(logits))
     check(rc, "sap_topk_sparse_idx")
     return out
 
