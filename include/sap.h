@@ -36,7 +36,8 @@ typedef enum {
     SAP_ERR_SHAPE = -3,      /* a size, stride or count is out of range */
     SAP_ERR_DTYPE = -4,      /* an unsupported element type */
     SAP_ERR_WORKSPACE = -5,  /* workspace missing or smaller than required */
-    SAP_ERR_LAUNCH = -6      /* the HIP runtime refused a launch */
+    SAP_ERR_LAUNCH = -6,     /* the HIP runtime refused a launch */
+    SAP_ERR_SCRATCH = -7     /* the allocation-free entry point's fixed scratch is too small */
 } sap_status;
 
 typedef enum {
@@ -135,6 +136,37 @@ int sap_sparse_attn_paged(const void *q, sap_dtype q_dtype, int64_t q_stride_t, 
                           void *out, sap_dtype out_dtype, int64_t out_stride_t, int64_t out_stride_h,
                           int T, int H, int D, float sm_scale, int num_splits,
                           void *workspace, size_t workspace_bytes, sap_stream_t stream);
+
+/* -------------------------------------------------------------------------
+ * Allocation-free sparse attention, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops and harnesses
+ * that forbid hipMalloc.  Same arguments and result as sap_sparse_attn_paged
+ * without the workspace: the split partials of a call live in a fixed
+ * device array of sap_sparse_attn_noalloc_max_bytes() bytes (32 MiB) that
+ * the library holds on every GPU it runs on until the process ends.  The
+ * call itself allocates nothing (no hipMalloc, no allocating library call).
+ *
+ * A call whose split plan needs more than that (sap_sparse_attn_workspace_bytes
+ * of the same arguments) returns SAP_ERR_SCRATCH and launches nothing.  The
+ * automatic plan (num_splits = 0) always fits for D <= 512; an explicit
+ * split count may not.  All calls on one
+ * GPU share its array and the array keeps the last call's contents: calls
+ * that overlap on one GPU (different streams, or graphs replayed
+ * concurrently) race and must be ordered by the caller.  Calls on one stream
+ * are ordered.  The array needs no clearing: every split writes its whole
+ * partial before the merge reads it.
+ * Errors: those of sap_sparse_attn_paged except SAP_ERR_WORKSPACE, plus
+ * SAP_ERR_SCRATCH.
+ * ------------------------------------------------------------------------- */
+size_t sap_sparse_attn_noalloc_max_bytes(void);
+int sap_sparse_attn_paged_noalloc(const void *q, sap_dtype q_dtype, int64_t q_stride_t, int64_t q_stride_h,
+                                  const void *win_pool, int64_t win_row_stride_bytes,
+                                  const void *cmp_pool, int64_t cmp_row_stride_bytes,
+                                  sap_dtype kv_dtype,
+                                  const int32_t *idx, int64_t idx_stride, int n_win, int n_cmp,
+                                  const float *win_scale, const float *cmp_scale,
+                                  void *out, sap_dtype out_dtype, int64_t out_stride_t, int64_t out_stride_h,
+                                  int T, int H, int D, float sm_scale, int num_splits, sap_stream_t stream);
 
 /* -------------------------------------------------------------------------
  * Indexer logits over fp4_e8m0_b32 packed key rows ("perf(kernel): read dsv41

@@ -21,6 +21,9 @@ SIGNATURES = {
     "sap_sparse_attn_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "sap_sparse_attn_paged": (_I, [_P, _I, _I64, _I64, _P, _I64, _P, _I64, _I, _P, _I64, _I, _I,
                                    _P, _P, _P, _I, _I64, _I64, _I, _I, _I, _F, _I, _P, _SZ, _P]),
+    "sap_sparse_attn_noalloc_max_bytes": (_SZ, []),
+    "sap_sparse_attn_paged_noalloc": (_I, [_P, _I, _I64, _I64, _P, _I64, _P, _I64, _I, _P, _I64, _I, _I,
+                                           _P, _P, _P, _I, _I64, _I64, _I, _I, _I, _F, _I, _P]),
     "sap_indexer_logits_packed": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _I, _P, _P, _I64,
                                        _I, _I, _I, _I, _P]),
     "sap_indexer_logits_candidates": (_I, [_P, _I64, _P, _I64, _P, _I64, _P, _I64, _I, _P, _I64, _P,

@@ -116,6 +116,36 @@ def sparse_attn_paged(q, win_pool, cmp_pool, idx, n_win: int, sm_scale: float, *
     return out
 
 
+def sparse_attn_noalloc_max_bytes() -> int:
+    return int(lib().sap_sparse_attn_noalloc_max_bytes())
+
+
+def sparse_attn_paged_noalloc(q, win_pool, cmp_pool, idx, n_win: int, sm_scale: float, *, out,
+                              win_scale=None, cmp_scale=None, num_splits: int = 0) -> torch.Tensor:
+    """sparse_attn_paged without a workspace: the split partials live in the
+    library's fixed device array, and the call allocates nothing (`out` is
+    required for the same reason)."""
+    _dev(q, win_pool, cmp_pool, idx, win_scale, cmp_scale, out)
+    T, H, D = q.shape
+    C = int(idx.shape[1])
+    if q.stride(2) != 1 or out.stride(2) != 1 or idx.stride(1) != 1:
+        raise ValueError("the innermost dimension must be contiguous")
+    kv = _kv_dtype(win_pool)
+    cmp = cmp_pool if cmp_pool is not None else win_pool
+    if cmp_pool is not None and _kv_dtype(cmp_pool) != kv:
+        raise ValueError("both pools must share one dtype")
+    rc = lib().sap_sparse_attn_paged_noalloc(
+        _p(q), SAP_BF16 if q.dtype == torch.bfloat16 else -1, q.stride(0), q.stride(1),
+        _p(win_pool), win_pool.stride(0) * win_pool.element_size(),
+        _p(cmp), cmp.stride(0) * cmp.element_size(), kv,
+        _p(idx), idx.stride(0), n_win, C - n_win,
+        _p(win_scale), _p(cmp_scale),
+        _p(out), _out_dtype(out.dtype), out.stride(0), out.stride(1),
+        T, H, D, float(sm_scale), int(num_splits), _stream(q))
+    check(rc, "sap_sparse_attn_paged_noalloc")
+    return out
+
+
 def indexer_logits_packed(q, w, key_pool, page_table, page: int, N: int, n_keys=None,
                           out=None) -> torch.Tensor:
     """q [B, Hi, 128] bf16, w [B, Hi] fp32, key_pool [rows, >=17] int32 -> logits [B, N] fp32."""

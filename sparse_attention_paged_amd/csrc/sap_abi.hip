@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "internal.hpp"
 
 namespace {
@@ -63,6 +65,37 @@ size_t attn_ws_bytes(int T, int H, int D, const SplitPlan &sp)
 
 inline int launched(hipError_t e) { return e == hipSuccess ? SAP_OK : SAP_ERR_LAUNCH; }
 
+// The allocation-free entry point keeps its split partials in this array
+// (each GPU the library runs on holds its own copy until the process ends).
+// Host code must not use the array's name as a device address: its device
+// address comes from hipGetSymbolAddress, taken once per device.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];
+
+// this device's address of `scratch`, looked up on its first use (with the
+// device current); NULL if the runtime refuses
+void *device_scratch()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        scratch_ptr[dev] = ptr;
+    }
+    return scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -79,6 +112,7 @@ const char *sap_status_string(int status)
     case SAP_ERR_DTYPE: return "unsupported element type";
     case SAP_ERR_WORKSPACE: return "workspace missing or too small";
     case SAP_ERR_LAUNCH: return "kernel launch failed";
+    case SAP_ERR_SCRATCH: return "the call needs more scratch memory than the allocation-free entry point holds";
     default: return "unknown status";
     }
 }
@@ -128,15 +162,23 @@ size_t sap_sparse_attn_workspace_bytes(int T, int H, int D, int n_cols, int num_
     return attn_ws_bytes(T, H, D, plan_splits(T, H, n_cols, num_splits));
 }
 
-int sap_sparse_attn_paged(const void *q, sap_dtype q_dtype, int64_t q_stride_t, int64_t q_stride_h,
-                          const void *win_pool, int64_t win_row_stride_bytes,
-                          const void *cmp_pool, int64_t cmp_row_stride_bytes,
-                          sap_dtype kv_dtype,
-                          const int32_t *idx, int64_t idx_stride, int n_win, int n_cmp,
-                          const float *win_scale, const float *cmp_scale,
-                          void *out, sap_dtype out_dtype, int64_t out_stride_t, int64_t out_stride_h,
-                          int T, int H, int D, float sm_scale, int num_splits,
-                          void *workspace, size_t workspace_bytes, sap_stream_t stream)
+}  // extern "C"
+
+namespace {
+
+// Argument checks, split plan and launch of the sparse attention.  With
+// `scratch_dev` the workspace is the library's own device array (the
+// allocation-free entry point): `workspace` is then ignored and a call whose
+// plan needs more than kScratchBytes is refused.
+int attn_call(const void *q, sap_dtype q_dtype, int64_t q_stride_t, int64_t q_stride_h,
+              const void *win_pool, int64_t win_row_stride_bytes,
+              const void *cmp_pool, int64_t cmp_row_stride_bytes,
+              sap_dtype kv_dtype,
+              const int32_t *idx, int64_t idx_stride, int n_win, int n_cmp,
+              const float *win_scale, const float *cmp_scale,
+              void *out, sap_dtype out_dtype, int64_t out_stride_t, int64_t out_stride_h,
+              int T, int H, int D, float sm_scale, int num_splits,
+              void *workspace, size_t workspace_bytes, bool scratch_dev, sap_stream_t stream)
 {
     if (T < 0 || H < 1 || n_win < 0 || n_cmp < 0 || num_splits < 0) return SAP_ERR_SHAPE;
     if (D != 64 && D != 128 && D != 256 && D != 512) return SAP_ERR_SHAPE;
@@ -168,6 +210,12 @@ int sap_sparse_attn_paged(const void *q, sap_dtype q_dtype, int64_t q_stride_t, 
     const SplitPlan sp = plan_splits(T, H, C, num_splits);
     if ((int64_t)T * sp.splits >= (int64_t)1 << 31) return SAP_ERR_SHAPE;
     const size_t need = attn_ws_bytes(T, H, D, sp);
+    if (scratch_dev && need > 0) {
+        if (need > kScratchBytes) return SAP_ERR_SCRATCH;
+        workspace = device_scratch();
+        if (!workspace) return SAP_ERR_LAUNCH;
+        workspace_bytes = kScratchBytes;
+    }
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return SAP_ERR_WORKSPACE;
 
     sap::AttnParams p{};
@@ -203,6 +251,43 @@ int sap_sparse_attn_paged(const void *q, sap_dtype q_dtype, int64_t q_stride_t, 
     hipError_t e = sap::launch_attn(p, D, kv, od, (hipStream_t)stream);
     if (e == hipSuccess && sp.splits > 1) e = sap::launch_attn_merge(p, D, kv, od, (hipStream_t)stream);
     return launched(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int sap_sparse_attn_paged(const void *q, sap_dtype q_dtype, int64_t q_stride_t, int64_t q_stride_h,
+                          const void *win_pool, int64_t win_row_stride_bytes,
+                          const void *cmp_pool, int64_t cmp_row_stride_bytes,
+                          sap_dtype kv_dtype,
+                          const int32_t *idx, int64_t idx_stride, int n_win, int n_cmp,
+                          const float *win_scale, const float *cmp_scale,
+                          void *out, sap_dtype out_dtype, int64_t out_stride_t, int64_t out_stride_h,
+                          int T, int H, int D, float sm_scale, int num_splits,
+                          void *workspace, size_t workspace_bytes, sap_stream_t stream)
+{
+    return attn_call(q, q_dtype, q_stride_t, q_stride_h, win_pool, win_row_stride_bytes, cmp_pool,
+                     cmp_row_stride_bytes, kv_dtype, idx, idx_stride, n_win, n_cmp, win_scale, cmp_scale, out,
+                     out_dtype, out_stride_t, out_stride_h, T, H, D, sm_scale, num_splits, workspace,
+                     workspace_bytes, false, stream);
+}
+
+size_t sap_sparse_attn_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int sap_sparse_attn_paged_noalloc(const void *q, sap_dtype q_dtype, int64_t q_stride_t, int64_t q_stride_h,
+                                  const void *win_pool, int64_t win_row_stride_bytes,
+                                  const void *cmp_pool, int64_t cmp_row_stride_bytes,
+                                  sap_dtype kv_dtype,
+                                  const int32_t *idx, int64_t idx_stride, int n_win, int n_cmp,
+                                  const float *win_scale, const float *cmp_scale,
+                                  void *out, sap_dtype out_dtype, int64_t out_stride_t, int64_t out_stride_h,
+                                  int T, int H, int D, float sm_scale, int num_splits, sap_stream_t stream)
+{
+    return attn_call(q, q_dtype, q_stride_t, q_stride_h, win_pool, win_row_stride_bytes, cmp_pool,
+                     cmp_row_stride_bytes, kv_dtype, idx, idx_stride, n_win, n_cmp, win_scale, cmp_scale, out,
+                     out_dtype, out_stride_t, out_stride_h, T, H, D, sm_scale, num_splits, nullptr, 0, true,
+                     stream);
 }
 
 int sap_indexer_logits_packed(const void *q, int64_t q_stride_b,

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "sap.h")
 
 sap_lib = pytest.importorskip("sparse_attention_paged_amd._lib")
 
-OK, ENULL, EALIGN, ESHAPE, EDTYPE, EWS = 0, -1, -2, -3, -4, -5
+OK, ENULL, EALIGN, ESHAPE, EDTYPE, EWS, ESCRATCH = 0, -1, -2, -3, -4, -5, -7
 BF16, F32, FP8 = 0, 1, 2
 A = 0x10000          # a fake, 16-byte aligned "device" address; never dereferenced
 
@@ -80,6 +80,36 @@ def test_attention_argument_checks(L):
     assert need == 4 * 64 * 512 * 4 + 4 * 64 * 2 * 4 + 0  # partial O + (max, sum), 256-aligned
     assert _attn(L, splits=4, ws=A, wsb=need - 1) == EWS
     assert _attn(L, splits=4, ws=A + 16, wsb=need) == EWS     # workspace must be 256-byte aligned
+
+
+def test_noalloc_argument_checks(L):
+    """The allocation-free entry point validates like sap_sparse_attn_paged
+    and refuses a plan larger than its fixed scratch before any HIP call."""
+    def call(**kw):
+        a = dict(q=A, q_dtype=BF16, q_st=64 * 512, q_sh=512, win=A, win_rs=1024, cmp=A, cmp_rs=1024,
+                 kv=BF16, idx=A, idx_st=640, n_win=128, n_cmp=512, ws_=None, cs_=None, out=A, od=F32,
+                 out_st=64 * 512, out_sh=512, T=1, H=64, D=512, sm=0.04, splits=1)
+        a.update(kw)
+        return L.sap_sparse_attn_paged_noalloc(a["q"], a["q_dtype"], a["q_st"], a["q_sh"], a["win"], a["win_rs"],
+                                               a["cmp"], a["cmp_rs"], a["kv"], a["idx"], a["idx_st"], a["n_win"],
+                                               a["n_cmp"], a["ws_"], a["cs_"], a["out"], a["od"], a["out_st"],
+                                               a["out_sh"], a["T"], a["H"], a["D"], a["sm"], a["splits"], None)
+    mx = L.sap_sparse_attn_noalloc_max_bytes()
+    assert mx == 32 << 20
+    assert call(T=0) == OK
+    assert call(win=A + 8) == EALIGN
+    assert call(idx=None) == ENULL
+    assert call(kv=F32) == EDTYPE
+    assert call(D=100) == ESHAPE
+    # an explicit split count whose partials exceed the fixed array
+    assert L.sap_sparse_attn_workspace_bytes(128, 64, 512, 640, 20) > mx
+    assert call(T=128, splits=20) == ESCRATCH
+    assert "allocation-free" in sap_lib.status_string(ESCRATCH)
+    # the automatic plan fits at every batch size and column count for D <= 512
+    for H in (1, 20, 64, 128):
+        for C in (1, 128, 384, 640, 1472, 4096):
+            for T in list(range(1, 140)) + [256, 8192]:
+                assert L.sap_sparse_attn_workspace_bytes(T, H, 512, C, 0) <= mx, (H, C, T)
 
 
 def test_split_planning(L):
