@@ -1,0 +1,418 @@
+// attn_dec.hip -- split-K sparse attention for decode batches at head_dim 512.
+//
+// What is computed is the same as in attn.hip ("perf(kernel): keep 16-byte kv
+// loads in dsv4 sparse attention and unroll gated pool", Call paths / Kernel
+// time): query token t's H heads share one KV head and attend to the columns
+// of idx[t, :]; column c reads one row of the window pool (c < n_win) or of
+// the compressed pool, and that row is both key and value.  For e4m3 pools
+// the per-row scale multiplies the dot outputs and is folded into the
+// softmax weights for PV; the denominator sums the unscaled weights ("Perf/kv
+// fp8 read path", What this changes).
+//
+// Decode has few tokens, so the work of one token is spread over many
+// workgroups, and what they write for the merge should not outweigh the rows
+// they read.  One workgroup = 4 waves = 16 heads of one token over a range of
+// its columns taken in rounds of 128 (32 per wave); a split's partial output
+// is then 16 heads x 512 fp32 = 32 KiB, the size of 32 rows, for the 128
+// rows (and more) it summarises:
+//  - gather: wave w moves its 32 rows from HBM straight into its own LDS tile
+//    (global_load_lds_dwordx4: one 1 KiB row per wave instruction, 16-byte
+//    loads; e4m3 rows pass through registers and are widened to bf16);
+//  - S^T = K Q^T for the wave's 32 columns and the 16 heads over all 512
+//    dims on MFMA 16x16x32 bf16 (M = columns, N = heads): the wave's own rows
+//    and its own copy of Q, so no partial score crosses waves;
+//  - online softmax (log2 domain): the waves exchange their 16 tile maxima
+//    through LDS (one barrier), so every wave rescales against the same
+//    running max; the weights stay in the MFMA output layout, which is the
+//    PV B-operand layout under the column order kk = 8g + 4c + i <-> column
+//    16c + 4g + i;
+//  - O^T += V^T P^T: wave w owns head_dim 128w .. 128w+127 for the 16 heads
+//    over all 128 columns of the round (the other waves' weights come through
+//    LDS, one barrier); V^T fragments are read from the four row-major tiles
+//    with ds_read_b64_tr_b16.
+// One split per token stores the normalised output; several splits store
+// (unnormalised O, running max, sum) and attn_dec_merge_kernel combines them
+// in split order.  The workgroups of one (token, split) -- its head groups --
+// are placed on one XCD, so a gathered row comes from HBM once and the other
+// head groups find it in that XCD's L2.
+#include "common.hpp"
+#include "formats.hpp"
+#include "internal.hpp"
+#include "attn_common.hpp"
+
+#include <type_traits>
+
+namespace sap {
+namespace {
+
+using namespace attn;
+
+constexpr int kD = 512;                 // head_dim
+constexpr int kWv = 4;                  // waves per workgroup
+constexpr int kCW = 32;                 // columns per wave per round
+constexpr int kRows = kDecRound;        // columns per round (kWv * kCW)
+constexpr int kTileB = kCW * kD * 2;    // one wave's bf16 tile
+constexpr int kPM = kD / (16 * kWv);    // PV m-steps over a wave's head_dim quarter
+
+static_assert(kRows == kWv * kCW, "a round is one tile per wave");
+
+// workgroup -> (unit u = token * splits + split, head group g); blocks whose
+// unit is past the end exit at once.  Block b runs on XCD b % 8 (workgroups
+// are dealt to the eight XCDs in turn), so all head groups of a unit share
+// an XCD.
+struct DecSlot {
+    int u, g;
+};
+__device__ __forceinline__ DecSlot dec_slot(int b, int G)
+{
+    const int x = b & 7, r = b >> 3;
+    return DecSlot{x + 8 * (r / G), r % G};
+}
+
+template <int KV, int OUT>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kWv, 64 * kWv), amdgpu_waves_per_eu(1, 1)))
+void attn_dec_kernel(AttnParams p)
+{
+    // bf16 terms per PV weight: e4m3 weights carry the row scale and must be
+    // held to fp32-like precision (outputs reach ~1e3 against an absolute
+    // bar), so they enter as hi + mid + lo
+    constexpr int NP = KV == 2 ? 3 : 1;
+    using Raw = typename std::conditional<KV == 2, uint2, uint4>::type;
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles[kWv][kTileB];
+    __shared__ __attribute__((aligned(1024))) uint8_t qs[kDecHeads * kD * 2];
+    __shared__ __attribute__((aligned(16))) uint4 xp[NP][kWv][64];   // weights of each wave's columns
+    __shared__ __attribute__((aligned(16))) float meta[kWv][2][kCW]; // per column: bias (0 / -inf), scale
+    __shared__ float xm[kWv][kDecHeads];                            // tile maxima
+    __shared__ float xl[kWv][kDecHeads];                            // softmax sums
+
+    const int G = p.hgroups;
+    const DecSlot sl = dec_slot((int)blockIdx.x, G);
+    if (sl.u >= p.T * p.num_splits) return;
+    const int t = sl.u / p.num_splits, split = sl.u - t * p.num_splits;
+    const int hbase = sl.g * kDecHeads;
+    const int c_begin = split * p.cols_per_split;
+    const int c_end = min(p.n_cols, c_begin + p.cols_per_split);
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+
+    // q rows of the 16 heads -> qs, 16-byte chunk c of head h at slot c ^ h
+    // (the fragment reads below are then free of bank conflicts); rows past
+    // H load head hbase as a finite stand-in
+#pragma unroll
+    for (int k = 0; k < kDecHeads / kWv; ++k) {
+        const int h = (kDecHeads / kWv) * w + k;
+        const int head = hbase + h < p.H ? hbase + h : hbase;
+        dma16(p.q + (int64_t)t * p.q_st + (int64_t)head * p.q_sh + 8 * (lane ^ h), lds_offset(qs + h * kD * 2));
+    }
+    // finite data that invalid columns load instead of a pool row
+    const uint8_t *safe_src = (const uint8_t *)(p.q + (int64_t)t * p.q_st);
+    const int32_t *idx_row = p.idx + (int64_t)t * p.idx_st;
+    const float sl2 = p.sm_scale_log2;
+
+    // LDS byte offsets: S reads chunk 4s + g of row 16c + l16 (swizzled by
+    // rswz(row), the same for both column halves); PV reads rows 4g + l16/4
+    // (+16) at head_dim 128w + 16m + 4(l16 % 4)
+    const int ksw = rswz(l16);
+    const int kb0 = l16 * kD * 2 + 16 * ((0 + g) ^ ksw), kb1 = l16 * kD * 2 + 16 * ((4 + g) ^ ksw);
+    int vb[4];
+    {
+        const int r = 4 * g + (l16 >> 2), vs = rswz(r);
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+            const int d = 128 * w + 16 * mm + 4 * (l16 & 3);
+            vb[mm] = r * kD * 2 + 16 * ((d >> 3) ^ vs) + 2 * (d & 7);
+        }
+    }
+
+    f32x4 acc[kPM];
+#pragma unroll
+    for (int m = 0; m < kPM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;   // running max of head l16 (the same in every wave)
+    float l_run = 0.0f;        // sum of this lane's weights of head l16
+    uint4 qf[kD / 32];         // Q as the B operand of S: head l16, dims 32s + 8g .. +7
+
+    uint8_t *const mytile = tiles[w];
+    bool first = true;
+    for (int c0 = c_begin; c0 < c_end; c0 += kRows) {
+        // the row indices of this wave's 32 columns (lane < 32 owns column cw + lane)
+        const int cw = c0 + kCW * w;
+        int e = -1;
+        if (lane < kCW && cw + lane < c_end) e = idx_row[cw + lane];
+        const bool win = cw + lane < p.n_win;
+        if (!first) __syncthreads();   // every wave has finished PV of the previous round
+        float scl = 0.0f;
+        if (lane < kCW) {
+            if constexpr (KV == 2) {
+                if (e >= 0) scl = (win ? p.win_scale : p.cmp_scale)[e];
+            }
+            meta[w][0][lane] = e >= 0 ? 0.0f : -INFINITY;
+        }
+        // gathers: row r of the tile is column cw + r; chunk j of the row goes
+        // to slot j ^ rswz(r)
+        Raw raw[kCW];
+#pragma unroll
+        for (int r = 0; r < kCW; ++r) {
+            const int er = __builtin_amdgcn_readlane(e, r);
+            const bool wr = __builtin_amdgcn_readlane((int)win, r) != 0;
+            const uint8_t *base = wr ? p.win : p.cmp;
+            const int64_t rs = wr ? p.win_rs : p.cmp_rs;
+            const int j = lane ^ rswz(r);
+            if constexpr (KV == 0) {
+                const uint8_t *src = er >= 0 ? base + (int64_t)er * rs + 16 * j : safe_src + 16 * j;
+                dma16(src, lds_offset(mytile + r * kD * 2));
+            } else {
+                // unused columns keep zero codes (arbitrary bytes may be NaN encodings)
+                const uint8_t *src = er >= 0 ? base + (int64_t)er * rs + 8 * lane : safe_src + 8 * lane;
+                const uint2 v = *(const uint2 *)src;
+                raw[r] = er >= 0 ? v : make_uint2(0u, 0u);
+            }
+        }
+        if (lane < kCW) meta[w][1][lane] = scl;
+        if (first) {
+            // q has landed in every wave (each waits for its own DMAs, the
+            // barrier publishes them); read the fragments while the rows fly
+            if constexpr (KV == 0) wait_vm<kCW>();
+            else wait_vm<0>();
+            __syncthreads();
+            const uint8_t *qrow = qs + l16 * kD * 2;
+#pragma unroll
+            for (int s = 0; s < kD / 32; ++s) qf[s] = lds_b128(qrow + 16 * ((4 * s + g) ^ l16));
+            first = false;
+        }
+        if constexpr (KV == 0) {
+            wait_vm<0>();
+        } else {
+            wait_vm<0>();
+#pragma unroll
+            for (int r = 0; r < kCW; ++r)
+                *(uint4 *)(mytile + r * kD * 2 + 16 * (lane ^ rswz(r))) = e4m3x8_to_bf16x8(raw[r]);
+        }
+
+        // S^T of the wave's columns 16c + 4g + i, heads hbase + l16
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int s = 0; s < kD / 32; ++s) {
+            const int off = 128 * (s >> 1) + ((s & 1) ? kb1 : kb0);
+            const uint4 k0 = lds_b128(mytile + off), k1 = lds_b128(mytile + 16 * kD * 2 + off);
+            sacc[0] = mfma16x16x32(k0, qf[s], sacc[0]);
+            sacc[1] = mfma16x16x32(k1, qf[s], sacc[1]);
+        }
+        float x[2][4], csc[2][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const float4 b4 = *(const float4 *)&meta[w][0][16 * c + 4 * g];
+            const float4 s4 = *(const float4 *)&meta[w][1][16 * c + 4 * g];
+            const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, ss[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = sacc[c][i] * sl2;
+                if constexpr (KV == 2) v *= ss[i];
+                csc[c][i] = ss[i];
+                x[c][i] = v + bb[i];
+                mx = fmaxf(mx, x[c][i]);
+            }
+        }
+        mx = group4_max(mx);
+        if (g == 0) xm[w][l16] = mx;
+        __syncthreads();   // maxima and every wave's rows published
+        const float mt = fmaxf(fmaxf(xm[0][l16], xm[1][l16]), fmaxf(xm[2][l16], xm[3][l16]));
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = m_new == m_run ? 1.0f : fast_exp2(m_run - m_new);   // m_run = -inf: 0
+        const float msub = m_new == -INFINITY ? 0.0f : m_new;
+        m_run = m_new;
+        float pr[2][4], psum = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pr[c][i] = fast_exp2(x[c][i] - msub);
+                psum += pr[c][i];
+            }
+        l_run = l_run * alpha + psum;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+            for (int m = 0; m < kPM; ++m) acc[m] *= alpha;
+        }
+        // this wave's weights in the B-operand layout: element 4c + i of lane
+        // (g, l16) is column 16c + 4g + i (e4m3: times the row scale, as NP
+        // bf16 terms, each the rounding of what the previous ones left)
+        {
+            float r8[8];
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) r8[4 * c + i] = KV == 2 ? pr[c][i] * csc[c][i] : pr[c][i];
+#pragma unroll
+            for (int ep = 0; ep < NP; ++ep) {
+                xp[ep][w][lane] = make_uint4(pack_bf16x2(r8[0], r8[1]), pack_bf16x2(r8[2], r8[3]),
+                                             pack_bf16x2(r8[4], r8[5]), pack_bf16x2(r8[6], r8[7]));
+                if (ep + 1 < NP) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) r8[i] -= __uint_as_float(bf16_bits(r8[i]) << 16);
+                }
+            }
+        }
+        __syncthreads();   // every wave's weights published
+        // O^T[128w + 16m + 4g + i][head l16] += sum over the round's 128 columns
+#pragma unroll
+        for (int wb = 0; wb < kWv; ++wb) {
+            uint4 pb[NP];
+#pragma unroll
+            for (int ep = 0; ep < NP; ++ep) pb[ep] = xp[ep][wb][lane];
+            const uint8_t *bt = tiles[wb];
+#pragma unroll
+            for (int m = 0; m < kPM; ++m) {
+                const uint2 v0 = lds_tr16(bt + vb[m & 3] + 128 * (m >> 2));
+                const uint2 v1 = lds_tr16(bt + vb[m & 3] + 16 * kD * 2 + 128 * (m >> 2));
+                const uint4 a = make_uint4(v0.x, v0.y, v1.x, v1.y);
+#pragma unroll
+                for (int ep = 0; ep < NP; ++ep) acc[m] = mfma16x16x32(a, pb[ep], acc[m]);
+            }
+        }
+    }
+
+    // softmax sums: over the lane groups, then over the waves in a fixed order
+    {
+        const float ls = group4_sum(l_run);
+        if (g == 0) xl[w][l16] = ls;
+    }
+    __syncthreads();
+    const float l_tot = (xl[0][l16] + xl[1][l16]) + (xl[2][l16] + xl[3][l16]);
+    const int head = hbase + l16;
+    if (head >= p.H) return;
+    const int d0 = 128 * w + 4 * g;
+    if (p.num_splits == 1) {
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        if constexpr (OUT == 1) {
+            float *o = (float *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d0;
+#pragma unroll
+            for (int m = 0; m < kPM; ++m) {
+                const f32x4 v = acc[m] * inv;
+                *(float4 *)(o + 16 * m) = make_float4(v[0], v[1], v[2], v[3]);
+            }
+        } else {
+            uint16_t *o = (uint16_t *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d0;
+#pragma unroll
+            for (int m = 0; m < kPM; ++m) {
+                const f32x4 v = acc[m] * inv;
+                *(uint2 *)(o + 16 * m) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            }
+        }
+    } else {
+        // partial outputs in the accumulators' own layout
+        // [unit][head group][w][m][lane] x 4 floats: each store instruction
+        // writes 1 KiB of consecutive bytes
+        const int64_t pb = ((int64_t)sl.u * G + sl.g) * kWv + w;
+#pragma unroll
+        for (int m = 0; m < kPM; ++m)
+            *(float4 *)(p.part_o + ((pb * kPM + m) * 64 + lane) * 4) =
+                make_float4(acc[m][0], acc[m][1], acc[m][2], acc[m][3]);
+        if (w == 0 && g == 0) *(float2 *)(p.part_ml + ((int64_t)sl.u * p.H + head) * 2) = make_float2(m_run, l_tot);
+    }
+}
+
+// out[t, h, :] = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j over the splits
+// j in order; zero when every split was empty.  One wave takes one (token,
+// head group, w, m) group of the partial layout: lane l owns head 16g + l%16
+// and head_dim 128w + 16m + 4(l/16) .. +3, so its partial loads are 1 KiB
+// contiguous per split; the loads of U splits go out before any is used.
+template <int OUT, int U, int WPB>   // WPB waves per workgroup
+__global__ __launch_bounds__(64 * WPB) void attn_dec_merge_kernel(AttnParams p)
+{
+    const int t = blockIdx.x;
+    const int grp = blockIdx.y * WPB + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int G = p.hgroups;
+    if (grp >= G * kWv * kPM) return;
+    const int m = grp % kPM, w = (grp / kPM) % kWv, hg = grp / (kPM * kWv);
+    const int head = hg * kDecHeads + (lane & 15);
+    if (head >= p.H) return;
+    const int d = 128 * w + 16 * m + 4 * (lane >> 4);
+    const int S = p.num_splits;
+    const int64_t pstride = (int64_t)G * kWv * kPM * 64;   // float4 slots per unit
+    const float4 *po = (const float4 *)p.part_o + ((int64_t)t * S) * pstride + (int64_t)grp * 64 + lane;
+    const float2 *pml = (const float2 *)p.part_ml + ((int64_t)t * S) * p.H + head;
+    float M = -INFINITY, L = 0.0f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = 0; j0 < S; j0 += U) {
+        float2 ml[U];
+        float4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int js = min(j0 + u, S - 1);
+            ml[u] = pml[(int64_t)js * p.H];
+            v[u] = po[(int64_t)js * pstride];
+        }
+        float Mb = M;
+#pragma unroll
+        for (int u = 0; u < U; ++u) Mb = fmaxf(Mb, ml[u].x);   // repeats of split S-1 change nothing
+        if (Mb == -INFINITY) continue;                         // every split so far empty
+        const float r = M == -INFINITY ? 0.0f : fast_exp2(M - Mb);
+        L *= r;
+        o.x *= r; o.y *= r; o.z *= r; o.w *= r;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (j0 + u < S) {
+                const float wt = fast_exp2(ml[u].x - Mb);
+                L += wt * ml[u].y;
+                o.x += wt * v[u].x; o.y += wt * v[u].y; o.z += wt * v[u].z; o.w += wt * v[u].w;
+            }
+        }
+        M = Mb;
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    if constexpr (OUT == 1) {
+        float *dst = (float *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d;
+        *(float4 *)dst = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    } else {
+        uint16_t *dst = (uint16_t *)p.out + (int64_t)t * p.out_st + (int64_t)head * p.out_sh + d;
+        *(uint2 *)dst = make_uint2(pack_bf16x2(o.x * inv, o.y * inv), pack_bf16x2(o.z * inv, o.w * inv));
+    }
+}
+
+template <int KV, int OUT>
+hipError_t launch_dec_t(const AttnParams &p, hipStream_t s)
+{
+    const int64_t U = (int64_t)p.T * p.num_splits;
+    const int64_t blocks = 8 * p.hgroups * ((U + 7) / 8);
+    hipLaunchKernelGGL((attn_dec_kernel<KV, OUT>), dim3((unsigned)blocks), dim3(64 * kWv), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int OUT>
+hipError_t launch_dec_merge_t(const AttnParams &p, hipStream_t s)
+{
+    const int groups = p.hgroups * kWv * kPM;
+    // a launch of at most one wave per CU takes one-wave workgroups (its
+    // waves land on as many CUs), larger ones four waves per workgroup
+    const bool one = (int64_t)p.T * groups <= 256;
+    const dim3 grid((unsigned)p.T, (unsigned)(one ? groups : (groups + 3) / 4));
+    auto go = [&](auto u_tag) {
+        constexpr int U = decltype(u_tag)::value;
+        if (one) hipLaunchKernelGGL((attn_dec_merge_kernel<OUT, U, 1>), grid, dim3(64), 0, s, p);
+        else hipLaunchKernelGGL((attn_dec_merge_kernel<OUT, U, 4>), grid, dim3(256), 0, s, p);
+    };
+    const int S = p.num_splits;
+    if (S <= 2) go(std::integral_constant<int, 2>{});
+    else if (S <= 4) go(std::integral_constant<int, 4>{});
+    else if (S <= 8) go(std::integral_constant<int, 8>{});
+    else go(std::integral_constant<int, 16>{});
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_dec(const AttnParams &p, int kv, int out, hipStream_t s)
+{
+    if (kv == 0) return out == 1 ? launch_dec_t<0, 1>(p, s) : launch_dec_t<0, 0>(p, s);
+    return out == 1 ? launch_dec_t<2, 1>(p, s) : launch_dec_t<2, 0>(p, s);
+}
+
+hipError_t launch_attn_dec_merge(const AttnParams &p, int out, hipStream_t s)
+{
+    return out == 1 ? launch_dec_merge_t<1>(p, s) : launch_dec_merge_t<0>(p, s);
+}
+
+}  // namespace sap

@@ -25,10 +25,16 @@ struct AttnParams {
     int64_t out_st, out_sh;
     int T, H;
     float sm_scale_log2;             // sm_scale * log2(e)
-    int num_splits, cols_per_split;  // cols_per_split: multiple of kAttnTile
+    int num_splits, cols_per_split;  // cols_per_split: multiple of kAttnTile (decode kernel: of kDecRound)
     float *part_o;                   // [T, S, H, D] unnormalised partial outputs
     float *part_ml;                  // [T, S, H, 2] running max (log2 domain), sum
+    int hgroups;                     // decode kernel: head groups of kDecHeads
 };
+
+// decode kernel (attn_dec.hip, head_dim 512): heads per workgroup and
+// columns per round (32 per wave)
+constexpr int kDecHeads = 16;
+constexpr int kDecRound = 128;
 
 // splits whose partial outputs the merge reads in one memory round trip
 // (more take further passes)
@@ -40,6 +46,9 @@ hipError_t launch_attn_merge(const AttnParams &p, int D, int kv, int out_dtype, 
 // bf16 rows at head_dim 512 with one split per token (attn_d512.hip);
 // launch_attn dispatches to it
 hipError_t launch_attn_d512(const AttnParams &p, int out_dtype, hipStream_t s);
+// split-K decode at head_dim 512 (attn_dec.hip) and its merge
+hipError_t launch_attn_dec(const AttnParams &p, int kv, int out_dtype, hipStream_t s);
+hipError_t launch_attn_dec_merge(const AttnParams &p, int out_dtype, hipStream_t s);
 // waves per workgroup of the split-K attention kernel, whose layout the split
 // partials follow: 8 (two head groups, two waves per SIMD) at head_dim 512,
 // else 4

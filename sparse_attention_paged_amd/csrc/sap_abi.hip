@@ -17,16 +17,58 @@ inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)
 inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 inline int dtype_size(int dt) { return dt == SAP_BF16 ? 2 : dt == SAP_F32 ? 4 : dt == SAP_FP8_E4M3 ? 1 : 0; }
 
+// How a sparse attention call runs:
+//  - ONEPASS: one pass per token (the prefill launch): at head_dim 512 with
+//    bf16 rows the persistent one-barrier kernel, else the tiled kernel;
+//  - DEC: the decode kernel at head_dim 512 (16 heads per workgroup, rounds
+//    of 128 columns), `splits` column ranges per token, merged when > 1;
+//  - SPLITK: other head_dims with several splits: the tiled kernel per
+//    split, then its merge.
+enum PlanKind { PLAN_ONEPASS = 0, PLAN_DEC = 1, PLAN_SPLITK = 2 };
+
 struct SplitPlan {
+    int kind;
     int splits;
     int cols_per_split;
 };
 
+// workgroups a decode launch aims for: the split count keeps T * head groups
+// * splits within it (two workgroups per CU at most; each holds 149 KiB of LDS)
+constexpr int kDecMaxWgs = 512;
+
 // Splitting a token's columns buys parallelism for decode, where a few tokens
 // would otherwise occupy a few CUs; each split costs a partial output of H*D
 // floats, so prefill-sized batches keep one split.
-SplitPlan plan_splits(int T, int H, int n_cols, int requested)
+SplitPlan plan_splits(int T, int H, int D, int n_cols, int requested)
 {
+    SplitPlan p;
+    if (D == 512 && requested != 1) {
+        const int G = (H + sap::kDecHeads - 1) / sap::kDecHeads;
+        const int rounds = n_cols > 0 ? (n_cols + sap::kDecRound - 1) / sap::kDecRound : 1;
+        const int64_t tg = (int64_t)T * G;
+        int s;
+        if (requested >= 2) {
+            s = requested;
+        } else {
+            // a batch that fills the GPU with one split per token runs the
+            // one-pass kernel; smaller ones split the columns so the launch
+            // has up to kDecMaxWgs workgroups, one round each while that fits
+            if (tg >= kDecMaxWgs) {
+                p.kind = PLAN_ONEPASS;
+                p.splits = 1;
+                p.cols_per_split = n_cols;
+                return p;
+            }
+            s = (int)(kDecMaxWgs / tg);
+        }
+        if (s > rounds) s = rounds;
+        if (s < 1) s = 1;
+        const int rps = (rounds + s - 1) / s;
+        p.kind = PLAN_DEC;
+        p.cols_per_split = rps * sap::kDecRound;
+        p.splits = n_cols > 0 ? (n_cols + p.cols_per_split - 1) / p.cols_per_split : 1;
+        return p;
+    }
     const int tiles = n_cols > 0 ? (n_cols + sap::kAttnTile - 1) / sap::kAttnTile : 1;
     int s;
     if (requested >= 1) {
@@ -34,32 +76,33 @@ SplitPlan plan_splits(int T, int H, int n_cols, int requested)
     } else {
         const int hb = (H + sap::kAttnHeadsPerBlock - 1) / sap::kAttnHeadsPerBlock;
         const int64_t wgs = (int64_t)T * hb;
-        // one 32-column tile per split is fastest while the launch stays
-        // within about 128 workgroups and the merge reads every split in one
-        // round trip; past that, the fewest tiles per split that keep within
-        // both (measured at decode B1 and B8: one sequence takes 4, 12 and 20
-        // splits at r0, r128 and r4 where two tiles per split gave 2, 6 and
-        // 10; eight take 10 at r4)
+        // one 32-column tile per split while the launch stays within about
+        // 128 workgroups and the merge reads every split in one round trip;
+        // past that, the fewest tiles per split that keep within both
         s = wgs >= 128 ? 1 : (int)(128 / wgs);
         if (s > sap::kMergeSplits) s = sap::kMergeSplits;
     }
     if (s > tiles) s = tiles;
     if (s < 1) s = 1;
     const int tiles_per = (tiles + s - 1) / s;
-    SplitPlan p;
     p.cols_per_split = tiles_per * sap::kAttnTile;
     p.splits = n_cols > 0 ? (n_cols + p.cols_per_split - 1) / p.cols_per_split : 1;
+    p.kind = p.splits > 1 ? PLAN_SPLITK : PLAN_ONEPASS;
+    if (p.kind == PLAN_ONEPASS) p.cols_per_split = n_cols;
     return p;
 }
 
+// partial-output bytes of a plan, then (max, sum) per head
 size_t attn_ws_bytes(int T, int H, int D, const SplitPlan &sp)
 {
     if (sp.splits <= 1) return 0;
-    // partial outputs for every head slot of the 64-head blocks, then
-    // (max, sum) per head
     const size_t slots = (size_t)T * sp.splits * H;
-    const size_t oslots = (size_t)T * sp.splits * ((H + sap::kAttnHeadsPerBlock - 1) / sap::kAttnHeadsPerBlock) *
-                          sap::kAttnHeadsPerBlock;
+    size_t oslots;
+    if (sp.kind == PLAN_DEC)
+        oslots = (size_t)T * sp.splits * ((H + sap::kDecHeads - 1) / sap::kDecHeads) * sap::kDecHeads;
+    else
+        oslots = (size_t)T * sp.splits * ((H + sap::kAttnHeadsPerBlock - 1) / sap::kAttnHeadsPerBlock) *
+                 sap::kAttnHeadsPerBlock;
     return align256(oslots * D * 4) + align256(slots * 2 * 4);
 }
 
@@ -153,13 +196,13 @@ int sap_sparse_attn_num_splits(int T, int H, int D, int n_cols, int num_splits)
 {
     (void)D;
     if (T < 0 || H < 1 || n_cols < 0 || num_splits < 0) return SAP_ERR_SHAPE;
-    return plan_splits(T, H, n_cols, num_splits).splits;
+    return plan_splits(T, H, D, n_cols, num_splits).splits;
 }
 
 size_t sap_sparse_attn_workspace_bytes(int T, int H, int D, int n_cols, int num_splits)
 {
     if (T <= 0 || H < 1 || D < 1 || n_cols < 0 || num_splits < 0) return 0;
-    return attn_ws_bytes(T, H, D, plan_splits(T, H, n_cols, num_splits));
+    return attn_ws_bytes(T, H, D, plan_splits(T, H, D, n_cols, num_splits));
 }
 
 }  // extern "C"
@@ -207,7 +250,7 @@ int attn_call(const void *q, sap_dtype q_dtype, int64_t q_stride_t, int64_t q_st
         if (!aligned(cmp_pool, 16) || cmp_row_stride_bytes % 16) return SAP_ERR_ALIGN;
         if (cmp_row_stride_bytes < (int64_t)D * kvb) return SAP_ERR_SHAPE;
     }
-    const SplitPlan sp = plan_splits(T, H, C, num_splits);
+    const SplitPlan sp = plan_splits(T, H, D, C, num_splits);
     if ((int64_t)T * sp.splits >= (int64_t)1 << 31) return SAP_ERR_SHAPE;
     const size_t need = attn_ws_bytes(T, H, D, sp);
     if (scratch_dev && need > 0) {
@@ -240,16 +283,22 @@ int attn_call(const void *q, sap_dtype q_dtype, int64_t q_stride_t, int64_t q_st
     p.sm_scale_log2 = sm_scale * 1.4426950408889634f;
     p.num_splits = sp.splits;
     p.cols_per_split = sp.cols_per_split;
+    p.hgroups = (H + sap::kDecHeads - 1) / sap::kDecHeads;
     if (sp.splits > 1) {
-        const size_t oslots = (size_t)T * sp.splits *
-                              ((H + sap::kAttnHeadsPerBlock - 1) / sap::kAttnHeadsPerBlock) * sap::kAttnHeadsPerBlock;
+        const size_t ml_off = attn_ws_bytes(T, H, D, sp) - align256((size_t)T * sp.splits * H * 2 * 4);
         p.part_o = (float *)workspace;
-        p.part_ml = (float *)((uint8_t *)workspace + align256(oslots * D * 4));
+        p.part_ml = (float *)((uint8_t *)workspace + ml_off);
     }
     const int kv = kv_dtype == SAP_FP8_E4M3 ? 2 : 0;
     const int od = out_dtype == SAP_F32 ? 1 : 0;
-    hipError_t e = sap::launch_attn(p, D, kv, od, (hipStream_t)stream);
-    if (e == hipSuccess && sp.splits > 1) e = sap::launch_attn_merge(p, D, kv, od, (hipStream_t)stream);
+    hipError_t e;
+    if (sp.kind == PLAN_DEC) {
+        e = sap::launch_attn_dec(p, kv, od, (hipStream_t)stream);
+        if (e == hipSuccess && sp.splits > 1) e = sap::launch_attn_dec_merge(p, od, (hipStream_t)stream);
+    } else {
+        e = sap::launch_attn(p, D, kv, od, (hipStream_t)stream);
+        if (e == hipSuccess && sp.splits > 1) e = sap::launch_attn_merge(p, D, kv, od, (hipStream_t)stream);
+    }
     return launched(e);
 }
 

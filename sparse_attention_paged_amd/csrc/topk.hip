@@ -36,10 +36,10 @@
 namespace sap {
 namespace {
 
-constexpr int kT = 512;                  // threads per workgroup
+constexpr int kT = 1024;                 // threads per workgroup
 constexpr int kW = kT / kWave;           // waves per workgroup
-constexpr int kDirectMax = 16384;        // rows selected in one launch (32 keys per thread)
-constexpr int kChunk = 4096;             // positions per filter workgroup (8 keys per thread)
+constexpr int kDirectMax = 16384;        // rows selected in one launch (16 keys per thread)
+constexpr int kChunk = 4096;             // positions per filter workgroup (4 keys per thread)
 constexpr int kSlotCap = 2048;           // candidates one filter workgroup may keep
 constexpr int kMaxChunks = 4096;         // two-launch path: N <= kChunk * kMaxChunks
 constexpr int kSample = 4096;            // strided sample that sets the filter threshold
@@ -47,18 +47,23 @@ constexpr int kMaxK = 4096;
 
 __device__ __forceinline__ uint32_t order_key(float v)
 {
-    const uint32_t u = __float_as_uint(v);
+    uint32_t u = __float_as_uint(v);
     if (v != v || u == 0xFF800000u) return 0u;          // NaN, -inf: not candidates
+    u = u == 0x80000000u ? 0u : u;                      // -0.0 ties with +0.0 (equal values)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // >= 0x00800000 otherwise
 }
 
-constexpr int kDigit = 11;               // bits per radix pass
-constexpr int kBins = 1 << kDigit;       // 4 per thread
+// Radix select keeps a 2048-bin LDS histogram per pass plus one extra bin
+// per lane for keys outside the current prefix, so a histogram instruction
+// never has two lanes on one extra bin.
+constexpr int kBins = 2048;
+constexpr int kExtra = kWave;
 
 struct Shared {
-    uint32_t hist[kBins];
-    int red[3 * kW];
-    int misc[4];
+    __attribute__((aligned(16))) uint32_t hist[kBins + kExtra];
+    int red[kW];
+    uint32_t wand[kW], wor[kW];
+    __attribute__((aligned(16))) int misc[4];
 };
 
 // exclusive prefix sum over the workgroup in thread order; total to all
@@ -80,29 +85,34 @@ __device__ int block_excl_scan(int v, Shared &s, int &total)
     return base + x - v;
 }
 
-// AND and OR of the nonzero keys and their count, over the workgroup
-__device__ void block_and_or_count(uint32_t &a, uint32_t &o, int &n, Shared &s)
+// AND and OR of the nonzero keys, per wave, into s.wand / s.wor (read with
+// and_or_read after a barrier): the bits every candidate shares need no
+// radix pass.
+template <class ForEach>
+__device__ void and_or_publish(ForEach for_each, Shared &s)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t a = ~0u, o = 0u;
+    for_each([&](uint32_t key) {
+        a &= key ? key : ~0u;
+        o |= key;
+    });
     a = wave_last(wave_scan_dpp(a, ~0u, [](uint32_t x, uint32_t y) { return x & y; }));
     o = wave_last(wave_scan_dpp(o, 0u, [](uint32_t x, uint32_t y) { return x | y; }));
-    n = (int)wave_last((uint32_t)wave_incl_sum(n));
     if (lane == 0) {
-        s.red[w] = (int)a;
-        s.red[kW + w] = (int)o;
-        s.red[2 * kW + w] = n;
+        s.wand[w] = a;
+        s.wor[w] = o;
     }
-    __syncthreads();
+}
+__device__ __forceinline__ void and_or_read(const Shared &s, uint32_t &a, uint32_t &o)
+{
     a = ~0u;
     o = 0u;
-    n = 0;
 #pragma unroll
     for (int i = 0; i < kW; ++i) {
-        a &= (uint32_t)s.red[i];
-        o |= (uint32_t)s.red[kW + i];
-        n += s.red[2 * kW + i];
+        a &= s.wand[i];
+        o |= s.wor[i];
     }
-    __syncthreads();
 }
 
 // Outcome of a radix select: keys with (key & M) > P are selected; of the
@@ -113,78 +123,104 @@ struct Sel {
     int rem, kk;
 };
 
-// Radix select of the k largest nonzero keys.  for_each(f) calls f(key) for
-// every key of the row.
-template <class ForEach>
-__device__ Sel radix_select(ForEach for_each, int k, Shared &s)
+// Wave 0, after a histogram pass: the bin d holding the rem-th largest key
+// counted (rem = min(k, total) when k > 0: the first pass, which also
+// reports the total), the keys in bins above d and in d.  Lane l sums bins
+// 32l .. 32l+31 and one DPP scan over the lanes finds the lane L holding the
+// bin; then lane j < 32 takes bin 32L + j and a second scan finds the bin,
+// with no loop over bins.  The bins are cleared for the next pass.  Results
+// in s.misc: d, keys above d, keys in d, total.
+__device__ void find_bin(Shared &s, int rem, int k)
 {
-    const int tid = threadIdx.x;
-    uint32_t a = ~0u, o = 0u;
-    int n = 0;
-    for_each([&](uint32_t key) {
-        if (key) {
-            a &= key;
-            o |= key;
-            ++n;
-        }
-    });
-    // the histogram is cleared once, ahead of the barrier of the reductions;
-    // afterwards each thread clears the bins it reads
-    for (int i = tid; i < kBins; i += kT) s.hist[i] = 0u;
-    block_and_or_count(a, o, n, s);
-    const int kk = min(k, n);
-    if (kk <= 0) return Sel{0u, 0u, 0, 0};
-    const uint32_t diff = a ^ o;
-    if (diff == 0u) return Sel{a, ~0u, kk, kk};   // every candidate has the same key
-    int hb = 31 - __builtin_clz(diff);
-    uint32_t M = ~((2u << hb) - 1u);          // hb == 31: 2u << 31 == 0, M == 0
-    uint32_t P = a & M;
-    int rem = kk;
-    for (;;) {
-        const int lo = hb >= kDigit - 1 ? hb - (kDigit - 1) : 0;
-        const uint32_t dm = (2u << (hb - lo)) - 1u;
-        for_each([&](uint32_t key) {
-            if (key && (key & M) == P) atomicAdd(&s.hist[(key >> lo) & dm], 1u);
-        });
-        __syncthreads();
-        // this thread's bins 4 tid .. 4 tid + 3, cleared for the next pass
-        int c[4];
+    const int lane = threadIdx.x & 63;
+    uint32_t c[32];
+    uint4 *h = (uint4 *)&s.hist[32 * lane];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            c[i] = (int)s.hist[4 * tid + i];
-            s.hist[4 * tid + i] = 0u;
-        }
-        const int cs = c[0] + c[1] + c[2] + c[3];
-        int total;
-        const int pre = block_excl_scan(cs, s, total);   // keys in bins < 4 tid
-        const int x = total - pre;                       // keys in bins >= 4 tid
-        if (x >= rem && x - cs < rem) {
-            int above = x - cs, d = 4 * tid;
-#pragma unroll
-            for (int bb = 3; bb >= 0; --bb) {
-                if (above + c[bb] >= rem) {
-                    d = 4 * tid + bb;
-                    break;
-                }
-                above += c[bb];
-            }
-            s.misc[0] = d;
-            s.misc[1] = above;
-            s.misc[2] = c[d - 4 * tid];
-        }
-        __syncthreads();
-        const int d = s.misc[0];
-        rem -= s.misc[1];
-        const int cd = s.misc[2];
-        P |= (uint32_t)d << lo;
-        M |= dm << lo;
-        if (cd == rem || lo == 0) return Sel{P, M, rem, kk};
-        hb = lo - 1;
+    for (int i = 0; i < 8; ++i) {
+        const uint4 v = h[i];
+        c[4 * i] = v.x;
+        c[4 * i + 1] = v.y;
+        c[4 * i + 2] = v.z;
+        c[4 * i + 3] = v.w;
     }
+#pragma unroll
+    for (int st = 1; st < 32; st *= 2)
+#pragma unroll
+        for (int b = 0; b + st < 32; b += 2 * st) c[b] += c[b + st];
+    const int sum = (int)c[0];
+    const int incl = wave_incl_sum(sum);
+    const int total = (int)wave_last((uint32_t)incl);
+    if (k > 0) rem = min(k, total);
+    const int above = total - incl;          // keys in bins past this lane's range
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(rem > 0 && above < rem && above + sum >= rem);
+    int d = 0, A = 0, cd = 0;
+    if (hit) {
+        const int L = (int)__builtin_ctzll(hit);
+        const int aL = __builtin_amdgcn_readlane(above, L);
+        const int v = lane < 32 ? (int)s.hist[32 * L + lane] : 0;
+        const int pre = wave_incl_sum(v);
+        const int suf = __builtin_amdgcn_readlane(pre, 31) - pre + v;   // lane L's bins >= this one
+        const uint64_t h2 = __builtin_amdgcn_ballot_w64(lane < 32 && aL + suf - v < rem && aL + suf >= rem);
+        const int j = (int)__builtin_ctzll(h2);
+        d = 32 * L + j;
+        A = aL + __builtin_amdgcn_readlane(suf - v, j);
+        cd = __builtin_amdgcn_readlane(v, j);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = make_uint4(0u, 0u, 0u, 0u);
+    s.hist[kBins + lane] = 0u;
+    if (lane == 0) *(int4 *)s.misc = make_int4(d, A, cd, total);
 }
 
-__device__ __forceinline__ bool sel_gt(uint32_t key, const Sel &q) { return key && (key & q.M) > q.P; }
-__device__ __forceinline__ bool sel_eq(uint32_t key, const Sel &q) { return key && (key & q.M) == q.P; }
+// Radix select of the k largest nonzero keys.  for_each(f) calls f(key) for
+// every key of the row; (a, o) = AND and OR of the nonzero keys (from
+// and_or_publish).  Passes start below the bits every candidate shares and
+// take 11 bits each, until the bin of the k-th key is taken whole.  The
+// histogram bins are cleared by the caller before the first pass (and by
+// find_bin after each).
+template <class ForEach>
+__device__ Sel radix_select(ForEach for_each, int k, uint32_t a, uint32_t o, Shared &s)
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    const uint32_t diff = a ^ o;
+    int hb = diff ? 31 - __builtin_clz(diff) : 0;
+    uint32_t M = ~((2u << hb) - 1u);          // hb == 31: 2u << 31 == 0, M == 0
+    uint32_t P = a & M;
+    int rem = 0, kk = 0;
+    bool first = true;
+#pragma unroll 1
+    for (;;) {
+        const int lo = hb >= 10 ? hb - 10 : 0;
+        const uint32_t dm = (2u << (hb - lo)) - 1u;
+        // keys outside the prefix (and non-candidates) go to this lane's extra bin
+        for_each([&](uint32_t key) {
+            const bool in = key != 0u && (key & M) == P;
+            atomicAdd(&s.hist[in ? (key >> lo) & dm : (uint32_t)(kBins + lane)], 1u);
+        });
+        __syncthreads();
+        if (tid < kWave) find_bin(s, rem, first ? k : 0);
+        __syncthreads();
+        const int4 m4 = *(const int4 *)s.misc;
+        if (first) {
+            kk = min(k, m4.w);
+            if (kk <= 0) return Sel{0u, 0u, 0, 0};
+            rem = kk;
+            first = false;
+        }
+        rem -= m4.y;
+        P |= (uint32_t)m4.x << lo;
+        M |= dm << lo;
+        if (m4.z == rem || lo == 0) break;
+        hb = lo - 1;
+    }
+    return Sel{P, M, rem, kk};
+}
+
+// every bin zero (before the first radix pass of a workgroup)
+__device__ __forceinline__ void clear_hist(Shared &s)
+{
+    for (int i = (int)threadIdx.x; i < kBins + kExtra; i += kT) s.hist[i] = 0u;
+}
 
 // Where the selected positions go.  IndexList: out[b][slot] = position.
 // SparseIdx (the decode step's fused index build): the selection of token b
@@ -205,7 +241,10 @@ struct IndexList {
     __device__ int value_fast(const Run &, int position) const { return position; }
     __device__ void put(int slot, int v) const { out[slot] = v; }
     __device__ void pad(int slot) const { out[slot] = -1; }
-    __device__ void window() const {}
+    struct Win {
+    };
+    __device__ Win window_begin() const { return Win{}; }
+    __device__ void window_end(const Win &) const {}
 };
 struct SparseIdx {
     int32_t *row;
@@ -257,16 +296,27 @@ struct SparseIdx {
     }
     __device__ void put(int slot, int v) const { row[n_win + slot] = v; }
     __device__ void pad(int slot) const { row[n_win + slot] = -1; }
-    __device__ void window() const
+    // window column j: row of position pos - (n_win - 1) + j, or -1
+    __device__ int32_t window_row(int j) const
     {
-        for (int j = (int)threadIdx.x; j < n_win; j += kT) {
-            const int64_t q = (int64_t)pos - (n_win - 1) + j;
-            int32_t r = -1;
-            if (q >= 0)
-                r = sh >= 0 ? (win_pt[q >> sh] << sh) + (int32_t)(q & (page - 1))
-                            : win_pt[q / page] * page + (int32_t)(q % page);
-            row[j] = r;
-        }
+        const int64_t q = (int64_t)pos - (n_win - 1) + j;
+        if (q < 0) return -1;
+        return sh >= 0 ? (win_pt[q >> sh] << sh) + (int32_t)(q & (page - 1))
+                       : win_pt[q / page] * page + (int32_t)(q % page);
+    }
+    // the window columns: the page-table load of column threadIdx.x goes out
+    // with the logits, its store after the selection
+    struct Win {
+        int32_t r;
+    };
+    __device__ Win window_begin() const
+    {
+        return Win{(int)threadIdx.x < n_win ? window_row((int)threadIdx.x) : -1};
+    }
+    __device__ void window_end(const Win &w) const
+    {
+        if ((int)threadIdx.x < n_win) row[threadIdx.x] = w.r;
+        for (int j = (int)threadIdx.x + kT; j < n_win; j += kT) row[j] = window_row(j);
     }
 };
 
@@ -275,49 +325,52 @@ struct SparseIdx {
 // greater keys before it plus min(equal keys before it, rem).  One scan of
 // both counts (16 bits each) gives both.  gt_seen / eq_seen carry the counts
 // of earlier blocks.  outv: LDS array of k slots; flush_out writes them out.
-// CHEAP: val_of is arithmetic only, so it is evaluated in the write loop;
-// otherwise (it may load) the values of the selected keys are loaded first,
-// together.  The per-key classes are kept as two bitmasks in VGPRs (per-key
-// booleans become wave masks in SGPRs, which ran out and spilled).
-template <int KPT, bool CHEAP = false, class ValOf>
+// Only the selected keys of a thread are visited (about k/N of them), each
+// with its slot from the popcounts of the class masks below it.
+template <int KPT, class ValOf>
 __device__ void emit_block(const uint32_t (&key)[KPT], ValOf val_of, const Sel &q, int32_t *outv, int &gt_seen,
                            int &eq_seen, Shared &s)
 {
     static_assert(KPT <= 32, "one bit per key");
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     uint32_t gtm = 0u, eqm = 0u;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-        gtm |= (sel_gt(key[j], q) ? 1u : 0u) << j;
-        eqm |= (sel_eq(key[j], q) ? 1u : 0u) << j;
+        const uint32_t x = key[j] & q.M;
+        gtm |= (x > q.P ? 1u : 0u) << j;
+        eqm |= (x == q.P ? 1u : 0u) << j;
     }
-    int val[CHEAP ? 1 : KPT];
-    if constexpr (!CHEAP) {
+    const int cnt = __builtin_popcount(gtm) | (__builtin_popcount(eqm) << 16);
+    const int incl = wave_incl_sum(cnt);
+    if (lane == 63) s.red[w] = incl;
+    __syncthreads();
+    int before = incl - cnt, tot = 0;
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) val[j] = ((gtm | eqm) >> j) & 1u ? val_of(j) : 0;
+    for (int i = 0; i < kW; ++i) {
+        const int r = s.red[i];
+        before += i < w ? r : 0;
+        tot += r;
     }
-    int tot;
-    const int before = block_excl_scan(__builtin_popcount(gtm) | (__builtin_popcount(eqm) << 16), s, tot);
-    int g = gt_seen + (before & 0xFFFF), e = eq_seen + (before >> 16);
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const int gt = (int)((gtm >> j) & 1u), eq = (int)((eqm >> j) & 1u);
-        const int slot = gt ? g + min(e, q.rem) : g + e;
-        if ((gt | (eq & (e < q.rem ? 1 : 0))) != 0) {
-            if constexpr (CHEAP) outv[slot] = val_of(j);
-            else outv[slot] = val[j];
-        }
-        g += gt;
-        e += eq;
+    const int g0 = gt_seen + (before & 0xFFFF), e0 = eq_seen + (before >> 16);
+    uint32_t sel = gtm | eqm;
+    while (sel) {
+        const int j = __builtin_ctz(sel);
+        sel &= sel - 1u;
+        const uint32_t below = (1u << j) - 1u;
+        const int g = g0 + __builtin_popcount(gtm & below), e = e0 + __builtin_popcount(eqm & below);
+        if ((gtm >> j) & 1u) outv[g + min(e, q.rem)] = val_of(j);
+        else if (e < q.rem) outv[g + e] = val_of(j);
     }
     gt_seen += tot & 0xFFFF;
     eq_seen += tot >> 16;
+    __syncthreads();   // s.red is rewritten by the next block's scan
 }
 
-// the kk selected slots from LDS, then -1 up to k, in coalesced stores
+// the kk selected slots from LDS (placed by emit_block, which ends with a
+// barrier), then -1 up to k, in coalesced stores
 template <class Out>
 __device__ void flush_out(const Out &out, int kk, int k, const int32_t *outv)
 {
-    __syncthreads();
     for (int i = (int)threadIdx.x; i < k; i += kT) {
         if (i < kk) out.put(i, outv[i]);
         else out.pad(i);
@@ -359,7 +412,12 @@ __device__ void select_streaming(const float *x, int nv, int k, const Out &out, 
             for (int j = 0; j < KPT; ++j) f(key[j]);
         }
     };
-    const Sel q = radix_select(for_each, k, s);
+    clear_hist(s);
+    and_or_publish(for_each, s);
+    __syncthreads();
+    uint32_t a, o;
+    and_or_read(s, a, o);
+    const Sel q = radix_select(for_each, k, a, o, s);
     const int kk = q.kk;
     int gt_seen = 0, eq_seen = 0;
     if (kk > 0) {
@@ -369,7 +427,7 @@ __device__ void select_streaming(const float *x, int nv, int k, const Out &out, 
             const int p0 = base + (int)threadIdx.x * KPT;
             const auto run = out.run(p0, KPT, nv);
             if (out.fast_run(run))
-                emit_block<KPT, true>(key, [&](int j) { return out.value_fast(run, p0 + j); }, q, outv, gt_seen, eq_seen, s);
+                emit_block<KPT>(key, [&](int j) { return out.value_fast(run, p0 + j); }, q, outv, gt_seen, eq_seen, s);
             else
                 emit_block<KPT>(key, [&](int j) { return out.value_in(run, p0 + j); }, q, outv, gt_seen, eq_seen, s);
         }
@@ -386,25 +444,36 @@ __global__ __launch_bounds__(kT) void topk_direct_kernel(TopkParams p)
     const int b = blockIdx.x;
     const float *x = p.x + (int64_t)b * p.x_sb;
     const Out out(p, b);
-    int nv = p.n_valid ? p.n_valid[b] : p.N;
-    nv = min(max(nv, 0), p.N);
-    uint32_t key[KPT];
-    load_keys<KPT>(x, 0, nv, key);
+    // the page-table entries of this thread's run and window column, the
+    // count of valid entries and the row's keys all load in one round trip
+    // (positions past the valid count are loaded up to N and dropped)
     const int p0 = (int)threadIdx.x * KPT;
-    const auto run = out.run(p0, KPT, nv);
-    out.window();
+    const auto run = out.run(p0, KPT, p.N);
+    const auto win = out.window_begin();
+    const int nv_in = p.n_valid ? p.n_valid[b] : p.N;
+    uint32_t key[KPT];
+    load_keys<KPT>(x, 0, p.N, key);
+    clear_hist(s);
+    const int nv = min(max(nv_in, 0), p.N);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = p0 + j < nv ? key[j] : 0u;
     auto for_each = [&](auto f) {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) f(key[j]);
     };
-    const Sel q = radix_select(for_each, p.k, s);
+    and_or_publish(for_each, s);
+    __syncthreads();
+    uint32_t a, o;
+    and_or_read(s, a, o);
+    const Sel q = radix_select(for_each, p.k, a, o, s);
     int gt_seen = 0, eq_seen = 0;
     if (q.kk > 0) {
         if (out.fast_run(run))
-            emit_block<KPT, true>(key, [&](int j) { return out.value_fast(run, p0 + j); }, q, outv, gt_seen, eq_seen, s);
+            emit_block<KPT>(key, [&](int j) { return out.value_fast(run, p0 + j); }, q, outv, gt_seen, eq_seen, s);
         else
             emit_block<KPT>(key, [&](int j) { return out.value_in(run, p0 + j); }, q, outv, gt_seen, eq_seen, s);
     }
+    out.window_end(win);
     flush_out(out, q.kk, p.k, outv);
 }
 
@@ -458,6 +527,7 @@ __global__ __launch_bounds__(kT) void topk_filter_kernel(TopkParams p, int nch)
     // threshold from the fixed strided sample (identical in every chunk)
     uint32_t tau = 1u;
     if (nv > kSample) {
+        clear_hist(s);   // ordered before the first radix pass by the scan's barriers
         constexpr int SPT = kSample / kT;
         uint32_t sk[SPT];
 #pragma unroll
@@ -465,15 +535,18 @@ __global__ __launch_bounds__(kT) void topk_filter_kernel(TopkParams p, int nch)
         int nz = 0;
 #pragma unroll
         for (int j = 0; j < SPT; ++j) nz += sk[j] != 0u;
+        auto for_each = [&](auto f) {
+#pragma unroll
+            for (int j = 0; j < SPT; ++j) f(sk[j]);
+        };
+        and_or_publish(for_each, s);   // read after the scan's barriers
         int ns;
         block_excl_scan(nz, s, ns);
         const int want = min(kSample, (int)(((int64_t)2 * p.k * kSample + nv - 1) / nv) + 16);
         if (ns >= want) {
-            auto for_each = [&](auto f) {
-#pragma unroll
-                for (int j = 0; j < SPT; ++j) f(sk[j]);
-            };
-            tau = radix_select(for_each, want, s).P;   // low bits zero: key >= tau <=> prefix >= P
+            uint32_t a, o;
+            and_or_read(s, a, o);
+            tau = radix_select(for_each, want, a, o, s).P;   // low bits zero: key >= tau <=> prefix >= P
             if (tau == 0u) tau = 1u;
         }
     }
@@ -512,7 +585,7 @@ __global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const float *x = p.x + (int64_t)b * p.x_sb;
     const Out out(p, b);
-    out.window();
+    const auto win = out.window_begin();
     int nv = p.n_valid ? p.n_valid[b] : p.N;
     nv = min(max(nv, 0), p.N);
     const TopkWs ws = topk_ws(p.workspace, p.B, nch);
@@ -557,12 +630,14 @@ __global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
         o += cl[j];
     }
     const uint32_t tau = ws.tau[b];
+    clear_hist(s);   // ordered before the first radix pass by the barriers below
     const bool ok = total <= kDirectMax && (total >= p.k || tau == 1u);
     // the selection by output slot reuses ckey: it is read into registers
     // before the first barrier of the radix select
     int32_t *const outv = (int32_t *)ckey;
     if (!ok) {
         select_streaming(x, nv, p.k, out, s, outv);
+        out.window_end(win);
         return;
     }
     __syncthreads();
@@ -607,15 +682,18 @@ __global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
 #pragma unroll
                 for (int j = 0; j < K; ++j) f(key[j]);
             };
-            const Sel q = radix_select(for_each, kk, s);
-            // index lists: a value is an LDS read, taken for every key
-            constexpr bool CHEAP = std::is_same<Out, IndexList>::value;
-            emit_block<K, CHEAP>(key, [&](int j) { return out.value(cpos[min(tid * K + j, kDirectMax - 1)]); }, q,
-                                 outv, gt_seen, eq_seen, s);
+            and_or_publish(for_each, s);
+            __syncthreads();
+            uint32_t a, o;
+            and_or_read(s, a, o);
+            const Sel q = radix_select(for_each, kk, a, o, s);
+            emit_block<K>(key, [&](int j) { return out.value(cpos[min(tid * K + j, kDirectMax - 1)]); }, q, outv,
+                          gt_seen, eq_seen, s);
         }
     };
     if (total <= 8 * kT) select_core(std::integral_constant<int, 8>{});
     else select_core(std::integral_constant<int, KPT>{});
+    out.window_end(win);
     flush_out(out, kk, p.k, outv);
 }
 
@@ -628,8 +706,9 @@ __global__ __launch_bounds__(kT) void topk_stream_kernel(TopkParams p)
     int nv = p.n_valid ? p.n_valid[b] : p.N;
     nv = min(max(nv, 0), p.N);
     const Out out(p, b);
-    out.window();
+    const auto win = out.window_begin();
     select_streaming(p.x + (int64_t)b * p.x_sb, nv, p.k, out, s, outv);
+    out.window_end(win);
 }
 
 int n_chunks(int N) { return (N + kChunk - 1) / kChunk; }

@@ -77,7 +77,9 @@ def test_attention_argument_checks(L):
     assert _attn(L, win_rs=512) == ESHAPE                     # rows shorter than D elements
     assert _attn(L, splits=4) == EWS                          # split-K needs a workspace
     need = L.sap_sparse_attn_workspace_bytes(1, 64, 512, 640, 4)
-    assert need == 4 * 64 * 512 * 4 + 4 * 64 * 2 * 4 + 0  # partial O + (max, sum), 256-aligned
+    # 4 splits requested over 5 rounds of 128 columns: 3 splits of 2 rounds,
+    # partial O of 64 heads + (max, sum) per head, each 256-aligned
+    assert need == 3 * 64 * 512 * 4 + 3 * 64 * 2 * 4
     assert _attn(L, splits=4, ws=A, wsb=need - 1) == EWS
     assert _attn(L, splits=4, ws=A + 16, wsb=need) == EWS     # workspace must be 256-byte aligned
 
@@ -114,18 +116,26 @@ def test_noalloc_argument_checks(L):
 
 def test_split_planning(L):
     ns = L.sap_sparse_attn_num_splits
+    # head_dim 512: the decode kernel splits a token's columns in rounds of 128
     assert ns(8192, 64, 512, 640, 0) == 1            # prefill: one pass per token
-    assert ns(1, 64, 512, 640, 0) == 20              # decode B1: one 32-column tile per split
-    assert ns(8, 64, 512, 640, 0) == 10              # B8: at most 16 splits (128 workgroups): two tiles each
-    assert ns(1, 64, 512, 384, 0) == 12
-    assert ns(1, 64, 512, 128, 0) == 4
-    assert ns(1, 64, 512, 40, 0) == 2                # two tiles (the second partial): two splits
-    assert ns(64, 64, 512, 640, 0) == 2              # 64 workgroups per split: 2 splits of 10 tiles
-    assert ns(1, 64, 512, 32 * 40, 0) == 20          # 40 tiles: at most 24 splits (one merge pass): two each
-    assert ns(1, 64, 512, 640, 7) == 7
-    assert ns(1, 64, 512, 640, 100) == 20            # never more splits than tiles
+    assert ns(128, 64, 512, 640, 0) == 1             # a batch that fills the GPU: one pass per token
+    assert ns(1, 64, 512, 640, 0) == 5               # decode B1: one round per split
+    assert ns(8, 64, 512, 640, 0) == 5               # B8: 160 workgroups
+    assert ns(1, 64, 512, 384, 0) == 3
+    assert ns(1, 64, 512, 128, 0) == 1               # window only: one split, no merge
+    assert ns(1, 64, 512, 40, 0) == 1
+    assert ns(64, 64, 512, 640, 0) == 2              # 256 workgroups per split: 2 splits of 3 rounds
+    assert ns(1, 64, 512, 32 * 40, 0) == 10
+    assert ns(1, 64, 512, 640, 7) == 5               # never more splits than rounds
+    assert ns(1, 64, 512, 640, 4) == 3               # 4 requested: 2 rounds each
     assert ns(1, 64, 512, 0, 0) == 1
     assert L.sap_sparse_attn_workspace_bytes(8192, 64, 512, 640, 0) == 0
+    assert L.sap_sparse_attn_workspace_bytes(1, 64, 512, 128, 0) == 0
+    # other head_dims: 32-column tiles per split, the launch within about 128 workgroups
+    assert ns(1, 64, 128, 640, 0) == 20
+    assert ns(8, 64, 128, 640, 0) == 10
+    assert ns(1, 64, 128, 640, 100) == 20            # never more splits than tiles
+    assert ns(8192, 64, 256, 640, 0) == 1
 
 
 def test_indexer_argument_checks(L):

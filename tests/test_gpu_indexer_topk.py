@@ -114,6 +114,25 @@ def test_topk_same_logits_bit_exact(B, N, k):
     assert torch.equal(got.cpu(), ref), f"B{B} N{N} k{k}"
 
 
+def test_topk_signed_zero_ties():
+    """-0.0 and +0.0 are equal values: when the k-th largest value is zero,
+    zeros of either sign tie and go to the lower index (as in the oracle's
+    value order), in the one-launch and the two-launch paths."""
+    need_gpu()
+    for N, k in ((8192, 512), (4000, 100), (40000, 512)):
+        g = torch.Generator().manual_seed(N + 3)
+        x = torch.full((2, N), -1.0)
+        pos = torch.randperm(N, generator=g)
+        x[0, pos[:k // 2]] = 1.0
+        zeros = pos[k // 2:k // 2 + 3 * k]
+        x[0, zeros] = torch.where(torch.rand(zeros.numel(), generator=g) < 0.5, -0.0, 0.0)
+        x[1] = torch.where(torch.rand(N, generator=g) < 0.5, -0.0, 0.0)
+        assert (torch.signbit(x[0]) & (x[0] == 0)).any()
+        got = sap.topk_select(dev(x), k)
+        torch.cuda.synchronize()
+        assert torch.equal(got.cpu(), oracle.topk(x, k)), f"N{N} k{k}"
+
+
 def test_topk_fallback_paths():
     """Long rows whose strided sample misleads the filter threshold: keys at
     the sampled positions dominate (too few keys pass), or one chunk holds
