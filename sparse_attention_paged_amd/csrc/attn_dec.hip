@@ -56,6 +56,19 @@ constexpr int kPM = kD / (16 * kWv);    // PV m-steps over a wave's head_dim qua
 
 static_assert(kRows == kWv * kCW, "a round is one tile per wave");
 
+// lane l moves 16 bytes from base + voff into LDS at lds + 16 l, base a
+// wave-uniform 64-bit address in scalar registers (taken with v_readlane,
+// so the wait states a vector memory instruction needs after a VALU write
+// of its scalar operand are inserted here: the compiler does not see into
+// the assembly)
+__device__ __forceinline__ void dma_row(uint64_t base, uint32_t voff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "s_nop 4\n\t"
+                 "global_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
+}
+
 // workgroup -> (unit u = token * splits + split, head group g); blocks whose
 // unit is past the end exit at once.  Block b runs on XCD b % 8 (workgroups
 // are dealt to the eight XCDs in turn), so all head groups of a unit share
@@ -149,24 +162,24 @@ void attn_dec_kernel(AttnParams p)
             }
             meta[w][0][lane] = e >= 0 ? 0.0f : -INFINITY;
         }
-        // gathers: row r of the tile is column cw + r; chunk j of the row goes
-        // to slot j ^ rswz(r)
+        // gathers: row r of the tile is column cw + r.  Lane r forms the row's
+        // address (a stand-in row for an unused column), and each row goes out
+        // with that address as a scalar base; chunk j of the row goes to slot
+        // j ^ rswz(r)
+        const uint8_t *rsrc = safe_src;
+        if (e >= 0) rsrc = (win ? p.win : p.cmp) + (int64_t)e * (win ? p.win_rs : p.cmp_rs);
+        const uint32_t alo = (uint32_t)(uintptr_t)rsrc, ahi = (uint32_t)((uintptr_t)rsrc >> 32);
         Raw raw[kCW];
 #pragma unroll
         for (int r = 0; r < kCW; ++r) {
-            const int er = __builtin_amdgcn_readlane(e, r);
-            const bool wr = __builtin_amdgcn_readlane((int)win, r) != 0;
-            const uint8_t *base = wr ? p.win : p.cmp;
-            const int64_t rs = wr ? p.win_rs : p.cmp_rs;
-            const int j = lane ^ rswz(r);
+            const uint64_t rb = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ahi, r) << 32) |
+                                (uint32_t)__builtin_amdgcn_readlane((int)alo, r);
             if constexpr (KV == 0) {
-                const uint8_t *src = er >= 0 ? base + (int64_t)er * rs + 16 * j : safe_src + 16 * j;
-                dma16(src, lds_offset(mytile + r * kD * 2));
+                dma_row(rb, 16 * (lane ^ rswz(r)), lds_offset(mytile + r * kD * 2));
             } else {
                 // unused columns keep zero codes (arbitrary bytes may be NaN encodings)
-                const uint8_t *src = er >= 0 ? base + (int64_t)er * rs + 8 * lane : safe_src + 8 * lane;
-                const uint2 v = *(const uint2 *)src;
-                raw[r] = er >= 0 ? v : make_uint2(0u, 0u);
+                const uint2 v = *(const uint2 *)((const uint8_t *)(uintptr_t)rb + 8 * lane);
+                raw[r] = __builtin_amdgcn_readlane(e, r) >= 0 ? v : make_uint2(0u, 0u);
             }
         }
         if (lane < kCW) meta[w][1][lane] = scl;

@@ -236,6 +236,7 @@ struct IndexList {
         int p0;
     };
     __device__ Run run(int p0, int, int) const { return Run{p0}; }
+    __device__ void run_rows(Run &) const {}
     __device__ int value_in(const Run &, int position) const { return position; }
     __device__ bool fast_run(const Run &) const { return true; }
     __device__ int value_fast(const Run &, int position) const { return position; }
@@ -269,18 +270,25 @@ struct SparseIdx {
     // a run of n <= page consecutive positions from p0 (below N) lies in the
     // page starting at base and the next one: their two page-table entries
     // are loaded up front, and no position needs a division
+    // (b0, b1: the rows of the two pages' first entries, b1 less one page)
     struct Run {
-        int base, n, e0, e1;
+        int base, n, b0, b1;
     };
     __device__ Run run(int p0, int n, int N) const
     {
         Run r{p0 - (sh >= 0 ? p0 & (page - 1) : p0 % page), n, 0, 0};
         if (p0 < N && n <= page) {
             const int last = min(p0 + n, N) - 1;
-            r.e0 = cmp_pt[sh >= 0 ? p0 >> sh : p0 / page];
-            r.e1 = cmp_pt[sh >= 0 ? last >> sh : last / page];
+            r.b0 = cmp_pt[sh >= 0 ? p0 >> sh : p0 / page];
+            r.b1 = cmp_pt[sh >= 0 ? last >> sh : last / page];
         }
         return r;
+    }
+    // the page-table entries have landed: their rows, once per run
+    __device__ void run_rows(Run &r) const
+    {
+        r.b0 = sh >= 0 ? r.b0 << sh : r.b0 * page;
+        r.b1 = (sh >= 0 ? r.b1 << sh : r.b1 * page) - page;
     }
     __device__ int value_in(const Run &r, int L) const
     {
@@ -292,7 +300,7 @@ struct SparseIdx {
     __device__ int value_fast(const Run &r, int L) const
     {
         const int off = L - r.base;
-        return off < page ? r.e0 * page + off : r.e1 * page + (off - page);
+        return (off < page ? r.b0 : r.b1) + off;
     }
     __device__ void put(int slot, int v) const { row[n_win + slot] = v; }
     __device__ void pad(int slot) const { row[n_win + slot] = -1; }
@@ -324,10 +332,11 @@ struct SparseIdx {
 // output slot, in position order: a selected key's slot is the number of
 // greater keys before it plus min(equal keys before it, rem).  One scan of
 // both counts (16 bits each) gives both.  gt_seen / eq_seen carry the counts
-// of earlier blocks.  outv: LDS array of k slots; flush_out writes them out.
-// Only the selected keys of a thread are visited (about k/N of them), each
-// with its slot from the popcounts of the class masks below it.
-template <int KPT, class ValOf>
+// of earlier blocks.  outv: LDS array of k slots plus kWave spare slots,
+// where keys that are not selected write (so the unrolled loop below has no
+// branches); flush_out writes the k slots out.  CHEAP: val_of is arithmetic,
+// evaluated for every key; otherwise (it may load) only for selected ones.
+template <int KPT, bool CHEAP, class ValOf>
 __device__ void emit_block(const uint32_t (&key)[KPT], ValOf val_of, const Sel &q, int32_t *outv, int &gt_seen,
                            int &eq_seen, Shared &s)
 {
@@ -352,14 +361,18 @@ __device__ void emit_block(const uint32_t (&key)[KPT], ValOf val_of, const Sel &
         tot += r;
     }
     const int g0 = gt_seen + (before & 0xFFFF), e0 = eq_seen + (before >> 16);
-    uint32_t sel = gtm | eqm;
-    while (sel) {
-        const int j = __builtin_ctz(sel);
-        sel &= sel - 1u;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
         const uint32_t below = (1u << j) - 1u;
         const int g = g0 + __builtin_popcount(gtm & below), e = e0 + __builtin_popcount(eqm & below);
-        if ((gtm >> j) & 1u) outv[g + min(e, q.rem)] = val_of(j);
-        else if (e < q.rem) outv[g + e] = val_of(j);
+        const bool gt = (gtm >> j) & 1u, eq = (eqm >> j) & 1u;
+        const bool take = gt || (eq && e < q.rem);
+        const int slot = take ? (gt ? g + min(e, q.rem) : g + e) : kMaxK + lane;
+        if constexpr (CHEAP) {
+            outv[slot] = val_of(j);
+        } else {
+            if (take) outv[slot] = val_of(j);
+        }
     }
     gt_seen += tot & 0xFFFF;
     eq_seen += tot >> 16;
@@ -425,11 +438,14 @@ __device__ void select_streaming(const float *x, int nv, int k, const Out &out, 
             uint32_t key[KPT];
             load_keys<KPT>(x, base, nv, key);
             const int p0 = base + (int)threadIdx.x * KPT;
-            const auto run = out.run(p0, KPT, nv);
+            auto run = out.run(p0, KPT, nv);
+            out.run_rows(run);
             if (out.fast_run(run))
-                emit_block<KPT>(key, [&](int j) { return out.value_fast(run, p0 + j); }, q, outv, gt_seen, eq_seen, s);
+                emit_block<KPT, true>(key, [&](int j) { return out.value_fast(run, p0 + j); }, q, outv, gt_seen,
+                                      eq_seen, s);
             else
-                emit_block<KPT>(key, [&](int j) { return out.value_in(run, p0 + j); }, q, outv, gt_seen, eq_seen, s);
+                emit_block<KPT, false>(key, [&](int j) { return out.value_in(run, p0 + j); }, q, outv, gt_seen,
+                                       eq_seen, s);
         }
     }
     flush_out(out, kk, k, outv);
@@ -440,7 +456,7 @@ template <int KPT, class Out>
 __global__ __launch_bounds__(kT) void topk_direct_kernel(TopkParams p)
 {
     __shared__ Shared s;
-    __shared__ int32_t outv[kMaxK];   // the selection by output slot
+    __shared__ int32_t outv[kMaxK + kWave];   // the selection by output slot, then spare slots
     const int b = blockIdx.x;
     const float *x = p.x + (int64_t)b * p.x_sb;
     const Out out(p, b);
@@ -448,7 +464,7 @@ __global__ __launch_bounds__(kT) void topk_direct_kernel(TopkParams p)
     // count of valid entries and the row's keys all load in one round trip
     // (positions past the valid count are loaded up to N and dropped)
     const int p0 = (int)threadIdx.x * KPT;
-    const auto run = out.run(p0, KPT, p.N);
+    auto run = out.run(p0, KPT, p.N);
     const auto win = out.window_begin();
     const int nv_in = p.n_valid ? p.n_valid[b] : p.N;
     uint32_t key[KPT];
@@ -468,10 +484,13 @@ __global__ __launch_bounds__(kT) void topk_direct_kernel(TopkParams p)
     const Sel q = radix_select(for_each, p.k, a, o, s);
     int gt_seen = 0, eq_seen = 0;
     if (q.kk > 0) {
+        out.run_rows(run);
         if (out.fast_run(run))
-            emit_block<KPT>(key, [&](int j) { return out.value_fast(run, p0 + j); }, q, outv, gt_seen, eq_seen, s);
+            emit_block<KPT, true>(key, [&](int j) { return out.value_fast(run, p0 + j); }, q, outv, gt_seen, eq_seen,
+                                  s);
         else
-            emit_block<KPT>(key, [&](int j) { return out.value_in(run, p0 + j); }, q, outv, gt_seen, eq_seen, s);
+            emit_block<KPT, false>(key, [&](int j) { return out.value_in(run, p0 + j); }, q, outv, gt_seen, eq_seen,
+                                   s);
     }
     out.window_end(win);
     flush_out(out, q.kk, p.k, outv);
@@ -687,7 +706,7 @@ __global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
             uint32_t a, o;
             and_or_read(s, a, o);
             const Sel q = radix_select(for_each, kk, a, o, s);
-            emit_block<K>(key, [&](int j) { return out.value(cpos[min(tid * K + j, kDirectMax - 1)]); }, q, outv,
+            emit_block<K, false>(key, [&](int j) { return out.value(cpos[min(tid * K + j, kDirectMax - 1)]); }, q, outv,
                           gt_seen, eq_seen, s);
         }
     };
@@ -701,7 +720,7 @@ template <class Out>
 __global__ __launch_bounds__(kT) void topk_stream_kernel(TopkParams p)
 {
     __shared__ Shared s;
-    __shared__ int32_t outv[kMaxK];   // the selection by output slot
+    __shared__ int32_t outv[kMaxK + kWave];   // the selection by output slot, then spare slots
     const int b = blockIdx.x;
     int nv = p.n_valid ? p.n_valid[b] : p.N;
     nv = min(max(nv, 0), p.N);

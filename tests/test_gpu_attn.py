@@ -135,6 +135,24 @@ def test_prefill_sampled(variant):
     assert_attn_close(out[toks], ref, f"{len(toks)} sampled tokens")
 
 
+def test_prefill_every_workgroup_slot_two_rounds():
+    """The prefill launch at head_dim 512 runs 256 persistent workgroups over
+    the tokens in rounds of 256 (round r holds tokens 256r .. 256r+255, each
+    XCD a block of 32 consecutive tokens): tokens 0 .. 511 put every
+    (workgroup, round) slot of the first two rounds against the oracle, and
+    the last two rounds (the tokens with the most columns) follow."""
+    need_gpu()
+    case = W.prefill_case(T=8192, ratio=4)
+    gidx = gpu_idx(case)
+    out = gpu_attn(case, idx=gidx, num_splits=1)
+    idx = oracle.case_idx(case)
+    assert torch.equal(gidx.cpu(), idx)
+    for lo, hi in ((0, 512), (8192 - 512, 8192)):
+        toks = list(range(lo, hi))
+        ref = oracle.sparse_attn(case.q[toks], case.win_pool, case.cmp_pool, idx[toks], case.n_win, case.sm_scale)
+        assert_attn_close(out[toks], ref, f"tokens {lo} .. {hi - 1}")
+
+
 def test_prefill_small_full():
     # every token, ragged tail of the last tile, tokens whose window is clipped
     need_gpu()

@@ -7,6 +7,7 @@ Tolerance: fp32 exponentials and sums over R <= 129 terms stay below
 1e-5 of M = sum_r p_r |x_r| (p = the softmax weights); a bf16 output adds
 its rounding, at most 2^-8 of the value.
 """
+import hashlib
 import math
 
 import numpy as np
@@ -70,3 +71,15 @@ def test_gated_pool_masked_and_dominant_gates():
     got = sap.gated_pool(case.x.cuda(), gate.cuda()).cpu()
     assert (got[:, 5] == 0).all()
     assert torch.equal(got[1, 10:20], case.x[1, 7, 10:20].to(torch.float32))
+
+
+def test_determinism_sha256_gated_pool():
+    need_gpu()
+    case = W.gated_pool_case(B=8, R=128, D=512, seed=W.SEED_BASE + 790)
+    x, g = case.x.cuda(), case.gate.cuda()
+    h = set()
+    for _ in range(3):
+        out = sap.gated_pool(x, g)
+        torch.cuda.synchronize()
+        h.add(hashlib.sha256(out.cpu().numpy().tobytes()).hexdigest())
+    assert len(h) == 1

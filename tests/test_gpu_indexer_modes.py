@@ -11,6 +11,7 @@ Logit tolerance as for full mode: below (128 + 32) * 2^-24 < 1e-5 of
 M = sum_h |w_h| sum_d |q_hd k_d| per logit; the -inf pattern (no candidate,
 a candidate or key beyond the token's visible count) must match exactly.
 """
+import hashlib
 import numpy as np
 import pytest
 import torch
@@ -191,3 +192,28 @@ def test_prefill_page_shapes(length, start, ratio, sample):
     say(f"prefill {case.name} N{case.N}")
     got = _pf_gpu(case)
     _pf_check(case, got, sample, case.name)
+
+
+def test_determinism_sha256_indexer_modes():
+    """Three runs of each indexer mode give identical bytes (sha256 of the
+    full logits), as the pages check output hashes across builds."""
+    need_gpu()
+    runs = []
+    case = W.indexer_case(B=4, N=131072, seed=W.SEED_BASE + 560)
+    q, w, pool, pt = (dev(x) for x in (case.q, case.w, case.key_pool, case.page_table))
+    runs.append(("full B4 N131072", lambda: sap.indexer_logits_packed(q, w, pool, pt, case.page, case.N)))
+    cc = W.indexer_cand_case(T=4, n_ctx=131072, NC=16384, seed=W.SEED_BASE + 561)
+    cq, cw, cpool, cpt, cand, cnk = (dev(x) for x in (cc.q, cc.w, cc.key_pool, cc.page_table, cc.cand, cc.n_keys))
+    runs.append(("candidates T4", lambda: sap.indexer_logits_candidates(cq, cw, cpool, cpt, cc.page, cand, n_keys=cnk)))
+    pc = W.indexer_prefill_case(lengths=(300, 200), starts=(1000, 0), ratio=2, seed=W.SEED_BASE + 562)
+    pq, pw, ppool, ppt, pts, pnk = (dev(x) for x in (pc.q, pc.w, pc.key_pool, pc.page_table, pc.tok_start, pc.n_keys))
+    runs.append(("prefill", lambda: sap.indexer_logits_prefill(pq, pw, ppool, ppt, pc.page, pts, pc.max_tokens, pc.N,
+                                                               n_keys=pnk)))
+    for name, fn in runs:
+        h = set()
+        for _ in range(3):
+            out = fn()
+            torch.cuda.synchronize()
+            h.add(hashlib.sha256(out.cpu().numpy().tobytes()).hexdigest())
+        assert len(h) == 1, name
+        say(f"  {name}: identical sha256 over 3 runs")

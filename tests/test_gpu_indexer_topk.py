@@ -11,6 +11,8 @@ is below (128 + 32) * 2^-24 < 1e-5 of M = sum_h |w_h| sum_d |q_hd k_d|.
 Top-k is compared bit for bit when both sides select from the same fp32
 logits.
 """
+import hashlib
+
 import numpy as np
 import pytest
 import torch
@@ -237,3 +239,25 @@ def test_topk_sparse_idx_matches_oracle(T, N, k, n_win, nv):
     torch.cuda.synchronize()
     assert torch.equal(got, two)
     say(f"  topk_sparse_idx T{T} N{N} k{k} n_win{n_win}: identical to oracle and to the two calls")
+
+
+def test_determinism_sha256_topk():
+    """Three runs of the top-k (one-launch and two-launch paths, and the
+    selection fused with the index build) give identical bytes."""
+    need_gpu()
+    g = torch.Generator().manual_seed(991)
+    for N in (8192, 131072):
+        x = dev((torch.randn(4, N, generator=g) * 4).round() / 4)
+        h = set()
+        for _ in range(3):
+            out = sap.topk_select(x, 512)
+            torch.cuda.synchronize()
+            h.add(hashlib.sha256(out.cpu().numpy().tobytes()).hexdigest())
+        assert len(h) == 1, N
+    x, seq, pos, win_pt, cmp_pt, n_valid = _tk_idx_inputs(8, 8192, 128, None, seed=992)
+    h = set()
+    for _ in range(3):
+        got = sap.topk_sparse_idx(dev(x), 512, dev(pos), dev(seq), 128, dev(win_pt), dev(cmp_pt), 64)
+        torch.cuda.synchronize()
+        h.add(hashlib.sha256(got.cpu().numpy().tobytes()).hexdigest())
+    assert len(h) == 1
