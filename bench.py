@@ -19,9 +19,10 @@ top-k, candidates, gated pool), a decode batch sweep, and cold-cache timings.
 Two timing regimes:
   warm  HIP-graph replays of several calls back to back (inputs stay in the
         L2 caches and the 256 MiB Infinity Cache between calls);
-  cold  one call per replay, with a 1 GiB scratch write and a 1 GiB read of
-        another buffer between replays, outside the timed events, so every
-        input comes from HBM.  HBM fractions are quoted on these.
+  cold  each call preceded by a 512 MiB read of another buffer (L2 and the
+        Infinity Cache evicted), inside a graph of such pairs; the graph of
+        the flushes alone is timed too and subtracted, so every input comes
+        from HBM.  HBM fractions are quoted on these.
 
 Profiling mode (for rocprofv3 counter runs, which need a program that launches
 only the kernels being measured): `python bench.py --only WORKLOAD --reps N`
@@ -118,20 +119,15 @@ def time_graph(fn, iters, warmup, per=GRAPH_CALLS):
 
 
 class Flush:
-    """Evicts the L2 caches and the Infinity Cache: a 1 GiB scratch write,
-    then a 1 GiB read of another buffer (the read's clean lines displace the
-    write's dirty ones, so a timed kernel does not pay their write-back)."""
+    """Evicts the L2 caches and the 256 MiB Infinity Cache: a read of 512 MiB
+    of another buffer (clean lines: a scratch write would leave dirty lines
+    whose write-back then lands inside the timed kernel)."""
 
     def __init__(self):
-        n = (1 << 30) // 4
-        self.w = torch.empty(n, dtype=torch.float32, device="cuda")
-        self.r = torch.ones(n, dtype=torch.float32, device="cuda")
+        self.r = torch.ones((512 << 20) // 4, dtype=torch.float32, device="cuda")
         self.acc = torch.empty((), dtype=torch.float32, device="cuda")
-        self.k = 0
 
     def __call__(self):
-        self.k += 1
-        self.w.fill_(float(self.k))
         torch.sum(self.r, dim=0, out=self.acc)
 
 
@@ -145,22 +141,31 @@ def flusher():
     return _FLUSH
 
 
-def time_cold(fn, reps=30):
-    """Median ms of one call of fn (a graph of one call) replayed after a
-    cache flush; the flush is outside the timed events."""
+def time_cold(fn, n=20, reps=9):
+    """ms of one call of fn with cold caches: a graph of n (flush, fn) pairs
+    against a graph of the n flushes alone, replayed alternately, the
+    difference of the medians per call.  (Timing single replays with events
+    instead would add the graph launch to every call.)"""
     fl = flusher()
-    g = capture(fn, 1)
-    for _ in range(3):
-        g.replay()
-    s = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for e0, e1 in ev:
+
+    def pair():
         fl()
-        e0.record(s)
+        fn()
+    graphs = [capture(pair, n), capture(fl, n)]
+    for g in graphs:
         g.replay()
-        e1.record(s)
     torch.cuda.synchronize()
-    return statistics.median(e0.elapsed_time(e1) for e0, e1 in ev)
+    s = torch.cuda.current_stream()
+    v = [[], []]
+    for _ in range(reps):
+        for i, g in enumerate(graphs):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            g.replay()
+            e1.record(s)
+            e1.synchronize()
+            v[i].append(e0.elapsed_time(e1))
+    return max(statistics.median(v[0]) - statistics.median(v[1]), 0.0) / n
 
 
 def roofline(bound, achieved, peak, unit, traffic=None, **extra):
@@ -353,7 +358,7 @@ def decode_sweep(batches):
         log(f"secondary: decode sweep B{B}")
         sw = SweepDecode(B)
         ms = time_graph(sw.attend, 5, 1, per=4)
-        ms_cold = time_cold(sw.attend, 15)
+        ms_cold = time_cold(sw.attend, 10, 5)
         alg = sw.alg_bytes()
         res.append({"workload": f"decode_sweep_b{B}_pos32767_r4_bf16", "attn_us": round(ms * 1e3, 2),
                     "attn_us_cold": round(ms_cold * 1e3, 2), "splits": sw.splits, "alg_MB": round(alg / 1e6, 2),

@@ -42,6 +42,17 @@ __global__ __launch_bounds__(64 * NWI) void indexer_kernel(IndexerParams p)
     const int b = blockIdx.y;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l32 = lane & 31, hh = lane >> 5;
+    const int n_tiles = (p.N + kKeyTile - 1) / kKeyTile;
+    const int tile0 = (blockIdx.x * NWI + wave) * p.tiles_per_wave;
+    // A tile of 64 keys starting at a multiple of 64 lies inside one page
+    // when the page size is a multiple of 64: one (wave-uniform) page-table
+    // read gives the pool row of its first key and the rest follow it.
+    const bool page_tiles = p.pt == nullptr || p.page % kKeyTile == 0;
+    // the first tile's page-table entry loads together with the valid-key
+    // count (the page table holds an entry for every page below N), so the
+    // key rows are one memory round trip after them, not two
+    int pte0 = 0;
+    if (p.pt && page_tiles && tile0 < n_tiles) pte0 = p.pt[(int64_t)b * p.pt_sb + tile0 * kKeyTile / p.page];
     const int nk = p.n_keys ? min(p.n_keys[b], p.N) : p.N;
 
     // q as the A operand: k-step s holds q[b, head l32, 16s + 8hh .. +7]
@@ -67,15 +78,8 @@ __global__ __launch_bounds__(64 * NWI) void indexer_kernel(IndexerParams p)
         }
     }
 
-    const int n_tiles = (p.N + kKeyTile - 1) / kKeyTile;
-    const int tile0 = (blockIdx.x * NWI + wave) * p.tiles_per_wave;
     uint32_t *st = stage[wave];
     uint32_t regs[kWordsPerLane];
-
-    // A tile of 64 keys starting at a multiple of 64 lies inside one page
-    // when the page size is a multiple of 64: one (wave-uniform) page-table
-    // read gives the pool row of its first key and the rest follow it.
-    const bool page_tiles = p.pt == nullptr || p.page % kKeyTile == 0;
     // a full tile of 17-word rows is one contiguous 4352-byte block: 16-byte
     // loads (4 per lane) plus one word per lane instead of 17 word loads
     const bool vec_ok = page_tiles && p.row_words == kRowWords && (reinterpret_cast<uintptr_t>(p.pool) & 15u) == 0;
@@ -85,7 +89,8 @@ __global__ __launch_bounds__(64 * NWI) void indexer_kernel(IndexerParams p)
         int64_t row0 = (int64_t)b * p.N + key0;
         if (p.pt && page_tiles) {
             const int pg = key0 / p.page;
-            row0 = (int64_t)p.pt[(int64_t)b * p.pt_sb + pg] * p.page + (key0 - pg * p.page);
+            const int e = kt == tile0 ? pte0 : p.pt[(int64_t)b * p.pt_sb + pg];
+            row0 = (int64_t)e * p.page + (key0 - pg * p.page);
         }
         vec = vec_ok && key0 + kKeyTile <= nk;
         if (vec) {

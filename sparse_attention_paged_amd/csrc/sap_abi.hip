@@ -108,6 +108,12 @@ size_t attn_ws_bytes(int T, int H, int D, const SplitPlan &sp)
 
 inline int launched(hipError_t e) { return e == hipSuccess ? SAP_OK : SAP_ERR_LAUNCH; }
 
+// waves a full-mode indexer launch is sized to (two per SIMD of 256 CUs)
+#ifndef SAP_INDEXER_WAVES
+#define SAP_INDEXER_WAVES 2048
+#endif
+constexpr int64_t kIndexerWaves = SAP_INDEXER_WAVES;
+
 // The allocation-free entry point keeps its split partials in this array
 // (each GPU the library runs on holds its own copy until the process ends).
 // Host code must not use the array's name as a device address: its device
@@ -372,9 +378,10 @@ int sap_indexer_logits_packed(const void *q, int64_t q_stride_b,
     p.B = B;
     p.Hi = Hi;
     p.N = N;
-    // about two waves per SIMD (256 CUs x 4 SIMDs), each streaming its tiles
+    // at most kIndexerWaves waves, each streaming its tiles with the next
+    // tile's loads in flight
     const int64_t tiles = ((int64_t)N + 63) / 64 * B;
-    p.tiles_per_wave = (int)((tiles + 2047) / 2048);
+    p.tiles_per_wave = (int)((tiles + kIndexerWaves - 1) / kIndexerWaves);
     if (p.tiles_per_wave < 1) p.tiles_per_wave = 1;
     return launched(sap::launch_indexer(p, (hipStream_t)stream));
 }
