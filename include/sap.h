@@ -186,7 +186,9 @@ int sap_sparse_attn_paged_noalloc(const void *q, sap_dtype q_dtype, int64_t q_st
  *   batch row b is pool row page_table[b][n / page] * page + n % page.  NULL
  *   means pool row b * N + n.
  * n_keys: [B] int32 valid key counts (NULL = N everywhere).  Keys at or past
- *   n_keys[b] are never read.
+ *   n_keys[b] score -inf; their rows are read only where they share a
+ *   64-key tile (inside one page) with a valid key, so every page that holds
+ *   a valid key must be whole in the pool.
  * logits: [B, N] fp32, batch stride logits_stride_b.
  * Limits: Hi in [1, 32], D == 128, 0 <= N, page >= 1.
  * Errors: SAP_ERR_NULL, SAP_ERR_ALIGN, SAP_ERR_SHAPE, SAP_ERR_LAUNCH.

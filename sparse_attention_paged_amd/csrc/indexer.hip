@@ -19,6 +19,8 @@
 #include "formats.hpp"
 #include "internal.hpp"
 
+#include <type_traits>
+
 namespace sap {
 namespace {
 
@@ -34,8 +36,12 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// NWI waves per workgroup (1 or 4)
-template <int NWI>
+// NWI waves per workgroup (1 or 4).  VEC: the host has checked that every
+// tile is a whole one inside one page of 17-word rows on a 16-byte aligned
+// pool (N a multiple of 64, pages a multiple of 64 rows or no page table), so
+// every tile below the valid-key count loads as one contiguous block; the
+// per-word path (and its registers) is compiled out.
+template <int NWI, bool VEC>
 __global__ __launch_bounds__(64 * NWI) void indexer_kernel(IndexerParams p)
 {
     __shared__ __attribute__((aligned(16))) uint32_t stage[NWI][kTileWords];
@@ -82,7 +88,7 @@ __global__ __launch_bounds__(64 * NWI) void indexer_kernel(IndexerParams p)
     uint32_t regs[kWordsPerLane];
     // a full tile of 17-word rows is one contiguous 4352-byte block: 16-byte
     // loads (4 per lane) plus one word per lane instead of 17 word loads
-    const bool vec_ok = page_tiles && p.row_words == kRowWords && (reinterpret_cast<uintptr_t>(p.pool) & 15u) == 0;
+    const bool vec_ok = VEC || (page_tiles && p.row_words == kRowWords && (reinterpret_cast<uintptr_t>(p.pool) & 15u) == 0);
     bool vec = false;   // layout of regs for the tile in flight (wave-uniform)
     auto load_tile = [&](int kt) {
         const int key0 = kt * kKeyTile;
@@ -92,7 +98,10 @@ __global__ __launch_bounds__(64 * NWI) void indexer_kernel(IndexerParams p)
             const int e = kt == tile0 ? pte0 : p.pt[(int64_t)b * p.pt_sb + pg];
             row0 = (int64_t)e * p.page + (key0 - pg * p.page);
         }
-        vec = vec_ok && key0 + kKeyTile <= nk;
+        // (VEC: a tile that holds the last valid key loads whole: its page
+        // is a valid one and its rows exist; the keys past the count are
+        // masked when the logits are written)
+        vec = VEC ? key0 < nk : vec_ok && key0 + kKeyTile <= nk;
         if (vec) {
             const uint32_t *tp = (const uint32_t *)p.pool + row0 * kRowWords;
 #pragma unroll
@@ -104,6 +113,12 @@ __global__ __launch_bounds__(64 * NWI) void indexer_kernel(IndexerParams p)
                 regs[4 * k + 3] = v.w;
             }
             regs[16] = tp[4 * 4 * kWave + lane];
+            return;
+        }
+        if constexpr (VEC) {
+            // a tile past the valid keys: nothing is read, its logits are -inf
+#pragma unroll
+            for (int k = 0; k < kWordsPerLane; ++k) regs[k] = 0u;
             return;
         }
 #pragma unroll
@@ -544,12 +559,19 @@ hipError_t launch_indexer(const IndexerParams &p, hipStream_t s)
     // a launch of at most one wave per CU spreads its waves over as many CUs
     // (decode B1 over 8192 keys: 4.35 us against 4.7 with four-wave
     // workgroups); larger launches keep four waves per workgroup
-    if ((int64_t)waves * p.B <= 256) {
-        hipLaunchKernelGGL(indexer_kernel<1>, dim3((unsigned)waves, (unsigned)p.B), dim3(64), 0, s, p);
-    } else {
-        const unsigned gx = (unsigned)((waves + 3) / 4);
-        hipLaunchKernelGGL(indexer_kernel<4>, dim3(gx, (unsigned)p.B), dim3(256), 0, s, p);
-    }
+    const bool vec = p.N % kKeyTile == 0 && p.row_words == kRowWords &&
+                     (reinterpret_cast<uintptr_t>(p.pool) & 15u) == 0 && (p.pt == nullptr || p.page % kKeyTile == 0);
+    auto go = [&](auto vec_tag) {
+        constexpr bool V = decltype(vec_tag)::value;
+        if ((int64_t)waves * p.B <= 256) {
+            hipLaunchKernelGGL((indexer_kernel<1, V>), dim3((unsigned)waves, (unsigned)p.B), dim3(64), 0, s, p);
+        } else {
+            const unsigned gx = (unsigned)((waves + 3) / 4);
+            hipLaunchKernelGGL((indexer_kernel<4, V>), dim3(gx, (unsigned)p.B), dim3(256), 0, s, p);
+        }
+    };
+    if (vec) go(std::true_type{});
+    else go(std::false_type{});
     return hipGetLastError();
 }
 

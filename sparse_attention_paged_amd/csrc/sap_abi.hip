@@ -108,9 +108,9 @@ size_t attn_ws_bytes(int T, int H, int D, const SplitPlan &sp)
 
 inline int launched(hipError_t e) { return e == hipSuccess ? SAP_OK : SAP_ERR_LAUNCH; }
 
-// waves a full-mode indexer launch is sized to (two per SIMD of 256 CUs)
+// waves a full-mode indexer launch is sized to (four per SIMD of 256 CUs)
 #ifndef SAP_INDEXER_WAVES
-#define SAP_INDEXER_WAVES 2048
+#define SAP_INDEXER_WAVES 4096
 #endif
 constexpr int64_t kIndexerWaves = SAP_INDEXER_WAVES;
 

@@ -58,7 +58,8 @@ def _gpu_logits(case):
     return out
 
 
-@pytest.mark.parametrize("B,N,n_keys", [(1, 8192, None), (4, 2000, [2000, 1999, 1000, 1]), (2, 333, [333, 0])])
+@pytest.mark.parametrize("B,N,n_keys", [(1, 8192, None), (4, 2000, [2000, 1999, 1000, 1]), (2, 333, [333, 0]),
+                                        (3, 4096, [4096, 2500, 63]), (2, 128, [0, 65])])
 def test_indexer_logits_small(B, N, n_keys):
     need_gpu()
     case = W.indexer_case(B=B, N=N, seed=W.SEED_BASE + 500 + B + N, n_keys=n_keys)
