@@ -7,18 +7,21 @@
 // sparse attention and unroll gated pool", Kernel time).
 //
 // Values become order-preserving 32-bit keys (0 = not a candidate).  The
-// selection core runs in one 512-thread workgroup on keys held in registers,
-// each thread owning a contiguous run of positions:
+// selection core runs in one 1024-thread workgroup (one CU) on keys held in
+// registers.  One CU issues 64 lane-operations per cycle, so at 8192 keys
+// every instruction per key costs 128 cycles: the core is built to spend few
+// instructions per key, not to save barriers.
 //  - radix select finds the prefix of the k-th largest key.  It starts below
 //    the bits every candidate shares (found by AND/OR reductions, which also
-//    count the candidates), takes 11 bits per pass into one LDS histogram of
-//    2048 bins (wide enough that clustered logits rarely pile onto one bin's
-//    atomics, and two passes usually settle it), finds the bin holding the
-//    k-th key with one block scan over 4 bins per thread, and stops as soon
-//    as that bin is taken whole;
-//  - the selected positions are written through one order-preserving block
-//    scan of (greater, equal) counts, so the output is already in ascending
-//    index order -- no sort.
+//    tell whether any key is a non-candidate; if none is, the first pass
+//    needs no prefix test), takes 11 bits per pass into one LDS histogram of
+//    2048 bins, finds the bin holding the k-th key in one wave with two DPP
+//    scans, and stops as soon as that bin is taken whole;
+//  - keys sit in a strided layout (thread t holds entries j*1024 + t), so a
+//    ballot over one key column lists 64 consecutive entries in order: a
+//    selected key's output slot is the count of selected keys in earlier
+//    (column, wave) pairs, from one exchange of per-pair ballot counts, plus
+//    mbcnt of its ballot.  The output is in ascending index order -- no sort.
 // Wave-level scans and reductions use DPP row shifts and broadcasts.
 // Rows of up to 16384 entries are selected directly.  Longer rows take two
 // launches: a filter launch where each workgroup derives the same threshold
@@ -47,10 +50,12 @@ constexpr int kMaxK = 4096;
 
 __device__ __forceinline__ uint32_t order_key(float v)
 {
-    uint32_t u = __float_as_uint(v);
-    if (v != v || u == 0xFF800000u) return 0u;          // NaN, -inf: not candidates
-    u = u == 0x80000000u ? 0u : u;                      // -0.0 ties with +0.0 (equal values)
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // >= 0x00800000 otherwise
+    // v + 0 turns -0.0 into +0.0 (equal values share one key) and leaves every
+    // other value as it is; negative values have all bits flipped, others only
+    // the sign bit.  Keys of candidates are >= 0x00800000.
+    const uint32_t u = __float_as_uint(v + 0.0f);
+    const uint32_t key = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+    return __builtin_amdgcn_classf(v, 0x7) ? 0u : key;   // signaling or quiet NaN, -inf
 }
 
 // Radix select keeps a 2048-bin LDS histogram per pass plus one extra bin
@@ -59,11 +64,14 @@ __device__ __forceinline__ uint32_t order_key(float v)
 constexpr int kBins = 2048;
 constexpr int kExtra = kWave;
 
+constexpr int kMaxKPT = 16;   // keys per thread of the selection core
+
 struct Shared {
     __attribute__((aligned(16))) uint32_t hist[kBins + kExtra];
     int red[kW];
-    uint32_t wand[kW], wor[kW];
+    uint32_t wand[kW], wor[kW], wzero[kW];
     __attribute__((aligned(16))) int misc[4];
+    __attribute__((aligned(16))) int tab[kMaxKPT * kW];   // per (key column, wave) counts
 };
 
 // exclusive prefix sum over the workgroup in thread order; total to all
@@ -93,26 +101,39 @@ __device__ void and_or_publish(ForEach for_each, Shared &s)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     uint32_t a = ~0u, o = 0u;
+    bool zero = false;
     for_each([&](uint32_t key) {
         a &= key ? key : ~0u;
         o |= key;
+        zero |= key == 0u;
     });
     a = wave_last(wave_scan_dpp(a, ~0u, [](uint32_t x, uint32_t y) { return x & y; }));
     o = wave_last(wave_scan_dpp(o, 0u, [](uint32_t x, uint32_t y) { return x | y; }));
+    const bool wz = __builtin_amdgcn_ballot_w64(zero) != 0u;
     if (lane == 0) {
         s.wand[w] = a;
         s.wor[w] = o;
+        s.wzero[w] = wz;
     }
 }
-__device__ __forceinline__ void and_or_read(const Shared &s, uint32_t &a, uint32_t &o)
+// zero: some key of the workgroup is 0 (not a candidate)
+__device__ __forceinline__ void and_or_read(const Shared &s, uint32_t &a, uint32_t &o, bool &zero)
 {
     a = ~0u;
     o = 0u;
+    uint32_t z = 0u;
 #pragma unroll
     for (int i = 0; i < kW; ++i) {
         a &= s.wand[i];
         o |= s.wor[i];
+        z |= s.wzero[i];
     }
+    zero = z != 0u;
+}
+__device__ __forceinline__ void and_or_read(const Shared &s, uint32_t &a, uint32_t &o)
+{
+    bool zero;
+    and_or_read(s, a, o, zero);
 }
 
 // Outcome of a radix select: keys with (key & M) > P are selected; of the
@@ -121,6 +142,7 @@ __device__ __forceinline__ void and_or_read(const Shared &s, uint32_t &a, uint32
 struct Sel {
     uint32_t P, M;
     int rem, kk;
+    int ceq;   // keys with (key & M) == P
 };
 
 // Wave 0, after a histogram pass: the bin d holding the rem-th largest key
@@ -179,41 +201,49 @@ __device__ void find_bin(Shared &s, int rem, int k)
 // histogram bins are cleared by the caller before the first pass (and by
 // find_bin after each).
 template <class ForEach>
-__device__ Sel radix_select(ForEach for_each, int k, uint32_t a, uint32_t o, Shared &s)
+__device__ Sel radix_select(ForEach for_each, int k, uint32_t a, uint32_t o, Shared &s, bool nozero = false)
 {
     const int tid = threadIdx.x, lane = tid & 63;
     const uint32_t diff = a ^ o;
     int hb = diff ? 31 - __builtin_clz(diff) : 0;
     uint32_t M = ~((2u << hb) - 1u);          // hb == 31: 2u << 31 == 0, M == 0
     uint32_t P = a & M;
-    int rem = 0, kk = 0;
+    int rem = 0, kk = 0, ceq = 0;
     bool first = true;
 #pragma unroll 1
     for (;;) {
         const int lo = hb >= 10 ? hb - 10 : 0;
         const uint32_t dm = (2u << (hb - lo)) - 1u;
-        // keys outside the prefix (and non-candidates) go to this lane's extra bin
-        for_each([&](uint32_t key) {
-            const bool in = key != 0u && (key & M) == P;
-            atomicAdd(&s.hist[in ? (key >> lo) & dm : (uint32_t)(kBins + lane)], 1u);
-        });
+        if (first && nozero) {
+            // every key is a candidate and shares the prefix of the AND/OR
+            for_each([&](uint32_t key) { atomicAdd(&s.hist[(key >> lo) & dm], 1u); });
+        } else {
+            // keys outside the prefix (and non-candidates) go to this lane's extra bin
+            for_each([&](uint32_t key) {
+                const bool in = key != 0u && (key & M) == P;
+                atomicAdd(&s.hist[in ? (key >> lo) & dm : (uint32_t)(kBins + lane)], 1u);
+            });
+        }
         __syncthreads();
         if (tid < kWave) find_bin(s, rem, first ? k : 0);
         __syncthreads();
         const int4 m4 = *(const int4 *)s.misc;
         if (first) {
             kk = min(k, m4.w);
-            if (kk <= 0) return Sel{0u, 0u, 0, 0};
+            if (kk <= 0) return Sel{0u, 0u, 0, 0, 0};
             rem = kk;
             first = false;
         }
         rem -= m4.y;
         P |= (uint32_t)m4.x << lo;
         M |= dm << lo;
-        if (m4.z == rem || lo == 0) break;
+        if (m4.z == rem || lo == 0) {
+            ceq = m4.z;
+            break;
+        }
         hb = lo - 1;
     }
-    return Sel{P, M, rem, kk};
+    return Sel{P, M, rem, kk, ceq};
 }
 
 // every bin zero (before the first radix pass of a workgroup)
@@ -246,6 +276,13 @@ struct IndexList {
     };
     __device__ Win window_begin() const { return Win{}; }
     __device__ void window_end(const Win &) const {}
+    // no page table: the selected position is the output
+    static constexpr int kStage = 1;
+    struct Stage {
+    };
+    __device__ Stage stage_load(int) const { return Stage{}; }
+    __device__ void stage_store(const Stage &, int32_t *, int) const {}
+    __device__ int staged_value(int position, const int32_t *, int) const { return position; }
 };
 struct SparseIdx {
     int32_t *row;
@@ -312,19 +349,71 @@ struct SparseIdx {
         return sh >= 0 ? (win_pt[q >> sh] << sh) + (int32_t)(q & (page - 1))
                        : win_pt[q / page] * page + (int32_t)(q % page);
     }
-    // the window columns: the page-table load of column threadIdx.x goes out
-    // with the logits, its store after the selection
+    // the window columns: the page-table entry of column threadIdx.x loads
+    // with the logits and is used after the selection.  The load is
+    // unconditional (position clamped into 0 .. pos) so no branch around it
+    // makes the wave wait for it before the logits go out.
     struct Win {
-        int32_t r;
+        int32_t e;
     };
     __device__ Win window_begin() const
     {
-        return Win{(int)threadIdx.x < n_win ? window_row((int)threadIdx.x) : -1};
+        if (pos < 0) return Win{0};
+        const int64_t q = (int64_t)pos - (n_win - 1) + (int)threadIdx.x;
+        const int64_t c = q < 0 ? 0 : (q > pos ? (int64_t)pos : q);
+        return Win{win_pt[sh >= 0 ? c >> sh : c / page]};
     }
     __device__ void window_end(const Win &w) const
     {
-        if ((int)threadIdx.x < n_win) row[threadIdx.x] = w.r;
-        for (int j = (int)threadIdx.x + kT; j < n_win; j += kT) row[j] = window_row(j);
+        const int j = (int)threadIdx.x;
+        if (j < n_win) {
+            const int64_t q = (int64_t)pos - (n_win - 1) + j;
+            row[j] = q < 0 ? -1
+                           : (sh >= 0 ? (w.e << sh) + (int32_t)(q & (page - 1))
+                                      : w.e * page + (int32_t)(q % page));
+        }
+        for (int jj = j + kT; jj < n_win; jj += kT) row[jj] = window_row(jj);
+    }
+    // The page-table entries of positions 0 .. N-1 go to LDS when they fit
+    // (loaded with the logits, stored before the first barrier), so the
+    // selected positions become rows without a memory round trip.
+    static constexpr int kStage = 4096;
+    static constexpr int kStagePT = kStage / kT;
+    struct Stage {
+        int32_t e[kStagePT];
+    };
+    __device__ int entries(int N) const
+    {
+        return N <= 0 ? 0 : (sh >= 0 ? ((N - 1) >> sh) + 1 : (N - 1) / page + 1);
+    }
+    __device__ Stage stage_load(int N) const
+    {
+        // branch-free (indices clamped into the row) so the loads go out
+        // together with the logits
+        Stage st{};
+        const int ne = entries(N);
+        if (ne >= 1 && ne <= kStage) {
+#pragma unroll
+            for (int r = 0; r < kStagePT; ++r) st.e[r] = cmp_pt[min(r * kT + (int)threadIdx.x, ne - 1)];
+        }
+        return st;
+    }
+    __device__ void stage_store(const Stage &st, int32_t *ptab, int N) const
+    {
+        const int ne = entries(N);
+        if (ne <= kStage) {
+#pragma unroll
+            for (int r = 0; r < kStagePT; ++r) {
+                const int i = r * kT + (int)threadIdx.x;
+                if (i < ne) ptab[i] = st.e[r];
+            }
+        }
+    }
+    __device__ int staged_value(int L, const int32_t *ptab, int N) const
+    {
+        const bool staged = entries(N) <= kStage;
+        if (sh >= 0) return ((staged ? ptab[L >> sh] : cmp_pt[L >> sh]) << sh) + (L & (page - 1));
+        return (staged ? ptab[L / page] : cmp_pt[L / page]) * page + L % page;
     }
 };
 
@@ -377,6 +466,101 @@ __device__ void emit_block(const uint32_t (&key)[KPT], ValOf val_of, const Sel &
     gt_seen += tot & 0xFFFF;
     eq_seen += tot >> 16;
     __syncthreads();   // s.red is rewritten by the next block's scan
+}
+
+// Selection core in the strided layout: key[j] of thread t is entry j*kT + t
+// of the row, so the 64 lanes of a wave hold consecutive entries and a
+// ballot over one key column lists them in entry order.  A selected key's
+// output slot is the number of selected keys before it: the selected keys of
+// earlier (column, wave) pairs, from one exchange of per-pair counts, plus
+// the lanes below it in its own ballot (mbcnt).
+
+// Exclusive prefix of the per-(column j, wave w) counts in s.tab (entry
+// j*kW + w, in entry order), for this wave's entry of every column.
+template <int KPT>
+__device__ void strided_bases(const int *tab, int (&base)[KPT])
+{
+    constexpr int R = KPT * kW / kWave;   // table entries per lane
+    static_assert(R >= 1 && kW % R == 0, "KPT must be a multiple of 4");
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int v[R], sum = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        v[r] = tab[lane * R + r];
+        sum += v[r];
+    }
+    const int incl = wave_incl_sum(sum);
+    const int rr = w % R;
+    int pre = incl - sum;
+#pragma unroll
+    for (int r = 0; r < R; ++r) pre += r < rr ? v[r] : 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) base[j] = __builtin_amdgcn_readlane(pre, j * (kW / R) + w / R);
+}
+
+__device__ __forceinline__ int rank_in(uint64_t m, int base)
+{
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)base));
+}
+
+// Writes the entry index of every selected key to outv[slot] (q.kk > 0, so
+// P != 0 and keys of 0 are never selected); ends with a barrier.
+template <int KPT>
+__device__ void emit_strided(const uint32_t (&key)[KPT], const Sel &q, int32_t *outv, Shared &s)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
+    int base[KPT];
+    if (q.rem == q.ceq) {
+        // the tie bin is taken whole: the selected keys are the keys >= P
+        // (P has no bits below the mask)
+        uint64_t m[KPT];
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) m[j] = __builtin_amdgcn_ballot_w64(key[j] >= q.P);
+        if (lane == 0) {
+#pragma unroll
+            for (int j = 0; j < KPT; ++j) s.tab[j * kW + w] = __builtin_popcountll(m[j]);
+        }
+        __syncthreads();
+        strided_bases<KPT>(s.tab, base);
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+            if (key[j] >= q.P) outv[rank_in(m[j], base[j])] = j * kT + tid;
+    } else {
+        // keys of the tie bin are taken in entry order while fewer than rem
+        // of them come before: slot = greater keys before + min(ties before, rem)
+        uint64_t gm[KPT], em[KPT];
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const uint32_t x = key[j] & q.M;
+            gm[j] = __builtin_amdgcn_ballot_w64(x > q.P);
+            em[j] = __builtin_amdgcn_ballot_w64(x == q.P);
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int j = 0; j < KPT; ++j)
+                s.tab[j * kW + w] = __builtin_popcountll(gm[j]) | (__builtin_popcountll(em[j]) << 16);
+        }
+        __syncthreads();
+        strided_bases<KPT>(s.tab, base);
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const uint32_t x = key[j] & q.M;
+            const int g = rank_in(gm[j], base[j] & 0xFFFF), e = rank_in(em[j], base[j] >> 16);
+            if (x > q.P || (x == q.P && e < q.rem)) outv[g + min(e, q.rem)] = j * kT + tid;
+        }
+    }
+    __syncthreads();
+}
+
+// the kk selected entry indices from LDS (placed by emit_strided), mapped to
+// their outputs, then -1 up to k
+template <class Out, class Map>
+__device__ void flush_idx(const Out &out, int kk, int k, const int32_t *outv, Map map)
+{
+    for (int i = (int)threadIdx.x; i < k; i += kT) {
+        if (i < kk) out.put(i, map(outv[i]));
+        else out.pad(i);
+    }
 }
 
 // the kk selected slots from LDS (placed by emit_block, which ends with a
@@ -451,28 +635,48 @@ __device__ void select_streaming(const float *x, int nv, int k, const Out &out, 
     flush_out(out, kk, k, outv);
 }
 
-// rows of at most kT * KPT positions, keys in registers
+// rows of at most kT * KPT positions, keys in registers (strided layout)
 template <int KPT, class Out>
 __global__ __launch_bounds__(kT) void topk_direct_kernel(TopkParams p)
 {
     __shared__ Shared s;
-    __shared__ int32_t outv[kMaxK + kWave];   // the selection by output slot, then spare slots
-    const int b = blockIdx.x;
+    __shared__ int32_t outv[kMaxK];             // selected entry indices by output slot
+    __shared__ int32_t ptab[Out::kStage];       // page-table entries (fused index build)
+    const int b = blockIdx.x, tid = threadIdx.x;
     const float *x = p.x + (int64_t)b * p.x_sb;
     const Out out(p, b);
-    // the page-table entries of this thread's run and window column, the
-    // count of valid entries and the row's keys all load in one round trip
-    // (positions past the valid count are loaded up to N and dropped)
-    const int p0 = (int)threadIdx.x * KPT;
-    auto run = out.run(p0, KPT, p.N);
+    // the page-table entries, the window column, the count of valid entries
+    // and the row's logits all load in one round trip
+    const auto st = out.stage_load(p.N);
     const auto win = out.window_begin();
     const int nv_in = p.n_valid ? p.n_valid[b] : p.N;
-    uint32_t key[KPT];
-    load_keys<KPT>(x, 0, p.N, key);
-    clear_hist(s);
-    const int nv = min(max(nv_in, 0), p.N);
+    float v[KPT];
+    if (p.N == KPT * kT) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = p0 + j < nv ? key[j] : 0u;
+        for (int j = 0; j < KPT; ++j) v[j] = x[j * kT + tid];
+    } else if (p.N > 0) {
+        // indices clamped into the row (no branch around the loads); entries
+        // past N become -inf
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int i = j * kT + tid;
+            const float t = x[min(i, p.N - 1)];
+            v[j] = i < p.N ? t : -__builtin_inff();
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) v[j] = -__builtin_inff();
+    }
+    uint32_t key[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = order_key(v[j]);
+    clear_hist(s);
+    out.stage_store(st, ptab, p.N);
+    const int nv = min(max(nv_in, 0), p.N);
+    if (nv < p.N) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) key[j] = j * kT + tid < nv ? key[j] : 0u;
+    }
     auto for_each = [&](auto f) {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) f(key[j]);
@@ -480,20 +684,12 @@ __global__ __launch_bounds__(kT) void topk_direct_kernel(TopkParams p)
     and_or_publish(for_each, s);
     __syncthreads();
     uint32_t a, o;
-    and_or_read(s, a, o);
-    const Sel q = radix_select(for_each, p.k, a, o, s);
-    int gt_seen = 0, eq_seen = 0;
-    if (q.kk > 0) {
-        out.run_rows(run);
-        if (out.fast_run(run))
-            emit_block<KPT, true>(key, [&](int j) { return out.value_fast(run, p0 + j); }, q, outv, gt_seen, eq_seen,
-                                  s);
-        else
-            emit_block<KPT, false>(key, [&](int j) { return out.value_in(run, p0 + j); }, q, outv, gt_seen, eq_seen,
-                                   s);
-    }
+    bool zero;
+    and_or_read(s, a, o, zero);
+    const Sel q = radix_select(for_each, p.k, a, o, s, !zero);
+    if (q.kk > 0) emit_strided<KPT>(key, q, outv, s);
     out.window_end(win);
-    flush_out(out, q.kk, p.k, outv);
+    flush_idx(out, q.kk, p.k, outv, [&](int i) { return out.staged_value(i, ptab, p.N); });
 }
 
 // workspace of the two-launch path, per row: chunk counts, the sample
@@ -685,17 +881,16 @@ __global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
     for (int ci = w + SPC * kW; ci < nch; ci += kW) gather_chunk(ci, 0);
     __syncthreads();
     const int kk = min(p.k, total);
-    // candidates in registers: 8 per thread when they fit (the usual case),
-    // else 32
+    // candidates in registers (strided layout): 8 per thread when they fit
+    // (the usual case), else 16; every candidate is nonzero
     auto select_core = [&](auto kpt_tag) __attribute__((always_inline)) {
         constexpr int K = decltype(kpt_tag)::value;
         uint32_t key[K];
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-            const int i = tid * K + j;
+            const int i = j * kT + tid;
             key[j] = i < total ? ckey[i] : 0u;
         }
-        int gt_seen = 0, eq_seen = 0;
         if (kk > 0) {
             auto for_each = [&](auto f) {
 #pragma unroll
@@ -704,16 +899,16 @@ __global__ __launch_bounds__(kT) void topk_select_kernel(TopkParams p, int nch)
             and_or_publish(for_each, s);
             __syncthreads();
             uint32_t a, o;
-            and_or_read(s, a, o);
-            const Sel q = radix_select(for_each, kk, a, o, s);
-            emit_block<K, false>(key, [&](int j) { return out.value(cpos[min(tid * K + j, kDirectMax - 1)]); }, q, outv,
-                          gt_seen, eq_seen, s);
+            bool zero;
+            and_or_read(s, a, o, zero);
+            const Sel q = radix_select(for_each, kk, a, o, s, !zero);
+            emit_strided<K>(key, q, outv, s);
         }
     };
     if (total <= 8 * kT) select_core(std::integral_constant<int, 8>{});
     else select_core(std::integral_constant<int, KPT>{});
     out.window_end(win);
-    flush_out(out, kk, p.k, outv);
+    flush_idx(out, kk, p.k, outv, [&](int i) { return out.value(cpos[i]); });
 }
 
 template <class Out>
@@ -748,9 +943,9 @@ hipError_t launch_topk_t(const TopkParams &p, hipStream_t st)
 {
     if (p.B == 0) return hipSuccess;
     if (p.N <= kDirectMax) {
+        static_assert(kDirectMax == kMaxKPT * kT, "direct rows fit the largest core");
         if (p.N <= 8 * kT) hipLaunchKernelGGL((topk_direct_kernel<8, Out>), dim3((unsigned)p.B), dim3(kT), 0, st, p);
-        else if (p.N <= 16 * kT) hipLaunchKernelGGL((topk_direct_kernel<16, Out>), dim3((unsigned)p.B), dim3(kT), 0, st, p);
-        else hipLaunchKernelGGL((topk_direct_kernel<32, Out>), dim3((unsigned)p.B), dim3(kT), 0, st, p);
+        else hipLaunchKernelGGL((topk_direct_kernel<kMaxKPT, Out>), dim3((unsigned)p.B), dim3(kT), 0, st, p);
         return hipGetLastError();
     }
     const int nch = n_chunks(p.N);

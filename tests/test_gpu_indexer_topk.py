@@ -242,6 +242,63 @@ def test_topk_sparse_idx_matches_oracle(T, N, k, n_win, nv):
     say(f"  topk_sparse_idx T{T} N{N} k{k} n_win{n_win}: identical to oracle and to the two calls")
 
 
+@pytest.mark.parametrize("T,N,k,page", [
+    (2, 8192, 512, 1),       # 8192 page-table entries: more than the LDS stage holds, looked up in memory
+    (2, 8192, 512, 3),       # pages of 3 entries: 2731 entries, staged, mapped by division
+    (2, 16384, 512, 16),     # 16 keys per thread
+    (3, 12000, 2048, 128),   # rows shorter than 16 keys per thread, k = 2048
+    (1, 4097, 512, 1),       # 4097 entries: one past the LDS stage
+])
+def test_topk_sparse_idx_page_sizes(T, N, k, page):
+    """The fused selection maps positions to rows through the page table,
+    staged in LDS when it fits, read from memory otherwise, for power-of-two
+    and other page sizes."""
+    need_gpu()
+    x, seq, pos, win_pt, cmp_pt, n_valid = _tk_idx_inputs(T, N, 128, None, seed=700 + N + page, page=page)
+    sel_ref = oracle.topk(x, k, n_valid)
+    idx_ref = oracle.build_idx(pos, seq, 128, win_pt, page, sel_ref, k, cmp_pt)
+    got = sap.topk_sparse_idx(dev(x), k, dev(pos), dev(seq), 128, dev(win_pt), dev(cmp_pt), page)
+    torch.cuda.synchronize()
+    assert torch.equal(got.cpu(), idx_ref), f"T{T} N{N} k{k} page{page}"
+
+
+@pytest.mark.parametrize("kind", ["negative", "wide", "mixed_sign", "one_value"])
+def test_topk_value_distributions(kind):
+    """Rows that are all negative, span the whole float range, mix signs
+    around zero, or hold one value: the radix passes start at different bits
+    and the tie bin is taken whole or in part."""
+    need_gpu()
+    g = torch.Generator().manual_seed(800 + len(kind))
+    N = 8192
+    if kind == "negative":
+        x = -torch.rand((4, N), generator=g) * 10 - 0.5
+    elif kind == "wide":
+        x = torch.randn((4, N), generator=g) * torch.pow(2.0, torch.randint(-120, 120, (4, N), generator=g).double()).float()
+    elif kind == "mixed_sign":
+        x = (torch.randn((4, N), generator=g) * 1e-3).to(torch.bfloat16).float()
+    else:
+        x = torch.full((4, N), 0.75)
+        x[:, ::97] = 2.0
+    for k in (1, 512, 4096):
+        got = sap.topk_select(dev(x), k)
+        torch.cuda.synchronize()
+        assert torch.equal(got.cpu(), oracle.topk(x, k)), f"{kind} k{k}"
+
+
+def test_topk_repeated_launches_identical():
+    """The decode step's selection shape (8192 logits, top-512, fused index
+    build) launched 50 times in a row on the same inputs gives the same rows
+    as the oracle every time."""
+    need_gpu()
+    x, seq, pos, win_pt, cmp_pt, n_valid = _tk_idx_inputs(8, 8192, 128, None, seed=993)
+    idx_ref = oracle.build_idx(pos, seq, 128, win_pt, 64, oracle.topk(x, 512), 512, cmp_pt)
+    xd, posd, seqd, wd, cd = dev(x), dev(pos), dev(seq), dev(win_pt), dev(cmp_pt)
+    outs = [sap.topk_sparse_idx(xd, 512, posd, seqd, 128, wd, cd, 64) for _ in range(50)]
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert torch.equal(o.cpu(), idx_ref), f"launch {i}"
+
+
 def test_determinism_sha256_topk():
     """Three runs of the top-k (one-launch and two-launch paths, and the
     selection fused with the index build) give identical bytes."""
