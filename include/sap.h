@@ -326,7 +326,10 @@ int sap_topk_select(const float *logits, int64_t stride_b, const int32_t *n_vali
  *
  * logits: [T, N] fp32 (row stride stride_t), candidates as for
  * sap_topk_select (n_valid may be NULL); pos, seq: [T] int32; page tables as
- * for sap_build_sparse_idx (cmp_pt required, win_pt when n_win > 0);
+ * for sap_build_sparse_idx (cmp_pt required, win_pt when n_win > 0).  Every
+ * cmp_pt row holds ceil(N / page) entries (the pages of entries 0 .. N-1),
+ * and every win_pt row the pages of positions 0 .. pos[t]: the kernel may read
+ * any of them, not only those of selected entries.
  * idx: [T, >= n_win + k] int32.  workspace: sap_topk_workspace_bytes(T, N, k)
  * bytes, 256-byte aligned: zero for N <= 16384 (the decode step's 8192
  * compressed entries), else the two-launch filter/select slots described

@@ -58,16 +58,14 @@ __device__ __forceinline__ uint32_t order_key(float v)
     return __builtin_amdgcn_classf(v, 0x7) ? 0u : key;   // signaling or quiet NaN, -inf
 }
 
-// Radix select keeps a 2048-bin LDS histogram per pass plus one extra bin
-// per lane for keys outside the current prefix, so a histogram instruction
-// never has two lanes on one extra bin.
+// Radix select keeps one 2048-bin LDS histogram, counting the keys inside
+// the current prefix.
 constexpr int kBins = 2048;
-constexpr int kExtra = kWave;
 
 constexpr int kMaxKPT = 16;   // keys per thread of the selection core
 
 struct Shared {
-    __attribute__((aligned(16))) uint32_t hist[kBins + kExtra];
+    __attribute__((aligned(16))) uint32_t hist[kBins];
     int red[kW];
     uint32_t wand[kW], wor[kW], wzero[kW];
     __attribute__((aligned(16))) int misc[4];
@@ -190,7 +188,6 @@ __device__ void find_bin(Shared &s, int rem, int k)
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) h[i] = make_uint4(0u, 0u, 0u, 0u);
-    s.hist[kBins + lane] = 0u;
     if (lane == 0) *(int4 *)s.misc = make_int4(d, A, cd, total);
 }
 
@@ -203,7 +200,7 @@ __device__ void find_bin(Shared &s, int rem, int k)
 template <class ForEach>
 __device__ Sel radix_select(ForEach for_each, int k, uint32_t a, uint32_t o, Shared &s, bool nozero = false)
 {
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
     const uint32_t diff = a ^ o;
     int hb = diff ? 31 - __builtin_clz(diff) : 0;
     uint32_t M = ~((2u << hb) - 1u);          // hb == 31: 2u << 31 == 0, M == 0
@@ -218,10 +215,10 @@ __device__ Sel radix_select(ForEach for_each, int k, uint32_t a, uint32_t o, Sha
             // every key is a candidate and shares the prefix of the AND/OR
             for_each([&](uint32_t key) { atomicAdd(&s.hist[(key >> lo) & dm], 1u); });
         } else {
-            // keys outside the prefix (and non-candidates) go to this lane's extra bin
+            // only keys inside the prefix are counted: an LDS atomic costs per
+            // active lane, and after the first pass few keys are inside
             for_each([&](uint32_t key) {
-                const bool in = key != 0u && (key & M) == P;
-                atomicAdd(&s.hist[in ? (key >> lo) & dm : (uint32_t)(kBins + lane)], 1u);
+                if (key != 0u && (key & M) == P) atomicAdd(&s.hist[(key >> lo) & dm], 1u);
             });
         }
         __syncthreads();
@@ -249,7 +246,7 @@ __device__ Sel radix_select(ForEach for_each, int k, uint32_t a, uint32_t o, Sha
 // every bin zero (before the first radix pass of a workgroup)
 __device__ __forceinline__ void clear_hist(Shared &s)
 {
-    for (int i = (int)threadIdx.x; i < kBins + kExtra; i += kT) s.hist[i] = 0u;
+    for (int i = (int)threadIdx.x; i < kBins; i += kT) s.hist[i] = 0u;
 }
 
 // Where the selected positions go.  IndexList: out[b][slot] = position.
@@ -388,13 +385,14 @@ struct SparseIdx {
     }
     __device__ Stage stage_load(int N) const
     {
-        // branch-free (indices clamped into the row) so the loads go out
-        // together with the logits
+        // no per-lane branch (indices clamped into the row) so the loads go
+        // out together with the logits; rounds past the entries are skipped
         Stage st{};
         const int ne = entries(N);
         if (ne >= 1 && ne <= kStage) {
 #pragma unroll
-            for (int r = 0; r < kStagePT; ++r) st.e[r] = cmp_pt[min(r * kT + (int)threadIdx.x, ne - 1)];
+            for (int r = 0; r < kStagePT; ++r)
+                if (r * kT < ne) st.e[r] = cmp_pt[min(r * kT + (int)threadIdx.x, ne - 1)];
         }
         return st;
     }
