@@ -148,11 +148,13 @@ void attn_dec_kernel(AttnParams p)
 
     uint8_t *const mytile = tiles[w];
     bool first = true;
+    // the row indices of this wave's 32 columns (lane < 32 owns column cw +
+    // lane); each round's indices load during the round before
+    int e_next = -1;
+    if (lane < kCW && c_begin + kCW * w + lane < c_end) e_next = idx_row[c_begin + kCW * w + lane];
     for (int c0 = c_begin; c0 < c_end; c0 += kRows) {
-        // the row indices of this wave's 32 columns (lane < 32 owns column cw + lane)
         const int cw = c0 + kCW * w;
-        int e = -1;
-        if (lane < kCW && cw + lane < c_end) e = idx_row[cw + lane];
+        const int e = e_next;
         const bool win = cw + lane < p.n_win;
         if (!first) __syncthreads();   // every wave has finished PV of the previous round
         float scl = 0.0f;
@@ -183,6 +185,8 @@ void attn_dec_kernel(AttnParams p)
             }
         }
         if (lane < kCW) meta[w][1][lane] = scl;
+        e_next = -1;
+        if (lane < kCW && cw + kRows + lane < c_end) e_next = idx_row[cw + kRows + lane];
         if (first) {
             // q has landed in every wave (each waits for its own DMAs, the
             // barrier publishes them); read the fragments while the rows fly

@@ -32,9 +32,12 @@ struct SplitPlan {
     int cols_per_split;
 };
 
-// workgroups a decode launch aims for: the split count keeps T * head groups
-// * splits within it (two workgroups per CU at most; each holds 149 KiB of LDS)
-constexpr int kDecMaxWgs = 512;
+// Decode workgroups hold 149 KiB of LDS each, so one fits on a CU: a launch
+// of more than 256 runs the rest only as the first ones finish.  The split
+// count keeps T * head groups * splits within kDecResident; a batch with at
+// least kDecOnePass token x head-group pairs runs the one-pass kernel.
+constexpr int kDecResident = 256;
+constexpr int kDecOnePass = 512;
 
 // Splitting a token's columns buys parallelism for decode, where a few tokens
 // would otherwise occupy a few CUs; each split costs a partial output of H*D
@@ -52,14 +55,15 @@ SplitPlan plan_splits(int T, int H, int D, int n_cols, int requested)
         } else {
             // a batch that fills the GPU with one split per token runs the
             // one-pass kernel; smaller ones split the columns so the launch
-            // has up to kDecMaxWgs workgroups, one round each while that fits
-            if (tg >= kDecMaxWgs) {
+            // has up to kDecResident workgroups (all resident at once), one
+            // round each while that fits
+            if (tg >= kDecOnePass) {
                 p.kind = PLAN_ONEPASS;
                 p.splits = 1;
                 p.cols_per_split = n_cols;
                 return p;
             }
-            s = (int)(kDecMaxWgs / tg);
+            s = (int)(kDecResident / tg);
         }
         if (s > rounds) s = rounds;
         if (s < 1) s = 1;

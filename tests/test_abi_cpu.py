@@ -124,7 +124,9 @@ def test_split_planning(L):
     assert ns(1, 64, 512, 384, 0) == 3
     assert ns(1, 64, 512, 128, 0) == 1               # window only: one split, no merge
     assert ns(1, 64, 512, 40, 0) == 1
-    assert ns(64, 64, 512, 640, 0) == 2              # 256 workgroups per split: 2 splits of 3 rounds
+    assert ns(16, 64, 512, 640, 0) == 3              # 192 workgroups of 2 rounds: every one resident
+    assert ns(32, 64, 512, 640, 0) == 2              # 256 workgroups: 2 splits of 3 rounds
+    assert ns(64, 64, 512, 640, 0) == 1              # 256 workgroups of 5 rounds, no merge
     assert ns(1, 64, 512, 32 * 40, 0) == 10
     assert ns(1, 64, 512, 640, 7) == 5               # never more splits than rounds
     assert ns(1, 64, 512, 640, 4) == 3               # 4 requested: 2 rounds each

@@ -84,6 +84,22 @@ def test_decode_bf16(B, ratio):
         assert d.abs().max().item() <= 1e-2 and rel <= 2e-3, (s, rel)
 
 
+@pytest.mark.parametrize("B,kv", [(16, "bf16"), (32, "bf16"), (64, "bf16"), (64, "e4m3")])
+def test_decode_resident_batches(B, kv):
+    """Batches whose automatic plan keeps every decode workgroup resident on
+    its own CU: B16 runs 3 splits of 2 rounds, B32 2 splits of 3, B64 one
+    split of 5 rounds and no merge (each round's row indices load during the
+    round before)."""
+    need_gpu()
+    case = W.decode_case(B=B, ratio=4, kv_dtype=kv, seed=W.SEED_BASE + 140 + B)
+    idx = oracle.case_idx(case)
+    ref = oracle.case_attn(case, idx=idx)
+    runs = sap.sparse_attn_num_splits(case.T, 64, 512, idx.shape[1], 0)
+    say(f"  {case.name}: {runs} splits")
+    out = gpu_attn(case, idx=dev(idx), num_splits=0)
+    assert_attn_close(out, ref, f"B{B} {kv} auto ({runs} splits)")
+
+
 def test_decode_fp8_b8():
     need_gpu()
     case = W.decode_case(B=8, ratio=4, kv_dtype="e4m3", seed=W.SEED_BASE + 4)
