@@ -5,7 +5,9 @@ MFMA reads, would get none of the wait states the hardware needs between the
 two, and the MFMA could read the register's old value.  This test compiles
 the kernel to gfx950 assembly (on the CPU) and checks that no register
 written by a VALU or AGPR-write instruction is read by an MFMA within a few
-instructions after the write.
+instructions after the write.  It also checks the order of vector memory
+instructions that the kernel's hand-counted vmcnt waits rely on, and that m0
+(which the row-gather assembly sets) is used by nothing else.
 """
 import os
 import re
@@ -91,17 +93,7 @@ def test_hazard_scan_catches_a_planted_case():
 
 
 def test_prefill_kernel_has_no_write_next_to_an_asm_mfma(tmp_path):
-    hipcc = next((c for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc"))
-                  if c and os.path.exists(c)), None)
-    if hipcc is None:
-        pytest.skip("hipcc not available")
-    out = tmp_path / "attn_d512.s"
-    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "--cuda-device-only", "-S",
-           os.path.join(CSRC, "attn_d512.hip"), "-o", str(out)]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-2000:]
-    lines = out.read_text().splitlines()
+    lines = _compile(tmp_path, "attn_d512")
     n_mfma = sum(1 for l in lines if l.strip().startswith("v_mfma"))
     assert n_mfma > 100, "the kernel's MFMAs were not found in the assembly"
     found = _hazards(lines)
@@ -134,21 +126,100 @@ def _early_reads(lines):
 
 
 def test_untracked_loads_untouched_until_waited(tmp_path):
-    hipcc = next((c for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc"))
-                  if c and os.path.exists(c)), None)
-    if hipcc is None:
-        pytest.skip("hipcc not available")
     assert len(_early_reads(["global_load_dword v4, v[2:3], off", "v_mov_b32_e32 v9, v4",
                              "s_waitcnt vmcnt(0)"])) == 1
     assert _early_reads(["global_load_dword v4, v[2:3], off", "s_waitcnt vmcnt(0)",
                          "v_mov_b32_e32 v9, v4"]) == []
-    out = tmp_path / "attn_d512.s"
-    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "--cuda-device-only", "-S",
-           os.path.join(CSRC, "attn_d512.hip"), "-o", str(out)]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-2000:]
-    lines = out.read_text().splitlines()
+    lines = _compile(tmp_path, "attn_d512")
     assert sum(1 for l in lines if l.strip().startswith("global_load_dword ") and l.strip().endswith(", off")) >= 4
     found = _early_reads(lines)
     assert not found, f"{len(found)} untracked load results used before their wait, e.g. {found[:3]}"
+
+
+_VM = ("global_", "buffer_", "flat_", "scratch_")
+
+
+_ASM = {}
+
+
+def _compile(tmp_path, name):
+    """gfx950 assembly of csrc/<name>.hip (compiled once per test session)."""
+    if name in _ASM:
+        return _ASM[name]
+    hipcc = next((c for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc"))
+                  if c and os.path.exists(c)), None)
+    if hipcc is None:
+        pytest.skip("hipcc not available")
+    out = tmp_path / f"{name}.s"
+    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "--cuda-device-only", "-S",
+           os.path.join(CSRC, f"{name}.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    _ASM[name] = out.read_text().splitlines()
+    return _ASM[name]
+
+
+def _kernels(lines, stem):
+    """{symbol: [instructions]} of every kernel whose name contains stem."""
+    out, cur = {}, None
+    for l in lines:
+        m = re.match(r"^(_Z\S+):", l)
+        if m:
+            cur = m.group(1) if stem in m.group(1) else None
+            if cur:
+                out[cur] = []
+            continue
+        if cur and l.startswith(".Lfunc_end"):
+            cur = None
+            continue
+        if cur:
+            t = l.split(";")[0].strip()
+            if t and not t.startswith(".") and not t.endswith(":"):
+                out[cur].append(t)
+    return out
+
+
+def test_prefill_token_switch_wait_counts(tmp_path):
+    """The prefill kernel waits for the next token's first tiles with
+    hand-counted vmcnt values that assume exactly this order of vector memory
+    instructions at a token switch: the 16 row DMAs of tiles 0 and 1 (8 rows
+    per wave each), then the previous token's 32 output stores (8 m-steps x 4
+    head blocks), then the next token's index loads.  Fewer or merged stores
+    would let a wait pass before its tile has landed, so the order and the
+    count are checked here."""
+    kern = _kernels(_compile(tmp_path, "attn_d512"), "attn_d512_kernel")
+    assert len(kern) == 2, list(kern)
+    for name, code in kern.items():
+        vm = [t for t in code if t.startswith(_VM)]
+        first_store = next(i for i, t in enumerate(vm) if t.startswith("global_store"))
+        before = vm[first_store - 16:first_store]
+        assert all(t.startswith("global_load_lds_dwordx4") for t in before), (name, before)
+        run = 0
+        for t in vm[first_store:]:
+            if not t.startswith("global_store"):
+                break
+            run += 1
+        assert run == 32, f"{name}: {run} consecutive output stores after the token-switch DMAs, expected 32"
+        assert sum(1 for t in vm if t.startswith("global_store")) == 32, name
+
+
+def test_m0_written_only_by_the_row_gathers(tmp_path):
+    """The row gathers set m0 (the LDS address of global_load_lds) from inline
+    assembly, which the compiler does not preserve around: no compiler-placed
+    instruction may read or write m0 in these kernels (indirect register
+    indexing, s_sendmsg and the like would)."""
+    for name in ("attn_d512", "attn_dec", "attn"):
+        lines = _compile(tmp_path, name)
+        code = [l.split(";")[0].strip() for l in lines]
+        bad = []
+        for i, t in enumerate(code):
+            if not re.search(r"\bm0\b", t):
+                continue
+            if t.startswith("s_mov_b32 m0, s"):
+                nxt = [u for u in code[i + 1:i + 4] if u and not u.startswith("s_nop")]
+                if nxt and nxt[0].startswith("global_load_lds_dwordx4"):
+                    continue
+            bad.append(t)
+        assert not bad, f"{name}: m0 used outside the row-gather assembly: {bad[:3]}"
+        assert not any(t.startswith(("s_set_gpr_idx", "v_movrel", "s_movrel")) for t in code), name
