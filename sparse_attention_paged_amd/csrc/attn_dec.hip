@@ -32,9 +32,9 @@
 //    with ds_read_b64_tr_b16.
 // One split per token stores the normalised output; several splits store
 // (unnormalised O, running max, sum) and attn_dec_merge_kernel combines them
-// in split order.  The workgroups of one (token, split) -- its head groups --
-// are placed on one XCD, so a gathered row comes from HBM once and the other
-// head groups find it in that XCD's L2.
+// in split order.  All workgroups of one token -- its splits and head groups
+// -- are placed on one XCD, so a gathered row and the q rows come from HBM
+// once and the other head groups find them in that XCD's L2.
 #include "common.hpp"
 #include "formats.hpp"
 #include "internal.hpp"
@@ -70,16 +70,20 @@ __device__ __forceinline__ void dma_row(uint64_t base, uint32_t voff, uint32_t l
 }
 
 // workgroup -> (unit u = token * splits + split, head group g); blocks whose
-// unit is past the end exit at once.  Block b runs on XCD b % 8 (workgroups
-// are dealt to the eight XCDs in turn), so all head groups of a unit share
-// an XCD.
+// token is past the end exit at once.  Block b runs on XCD b % 8 (workgroups
+// are dealt to the eight XCDs in turn): token t's splits and head groups all
+// run on XCD t % 8, so its q rows come from memory once, and its merge
+// workgroups (placed the same way) read the partials through the same L2.
 struct DecSlot {
     int u, g;
+    bool valid;
 };
-__device__ __forceinline__ DecSlot dec_slot(int b, int G)
+__device__ __forceinline__ DecSlot dec_slot(int b, int G, int S, int T)
 {
     const int x = b & 7, r = b >> 3;
-    return DecSlot{x + 8 * (r / G), r % G};
+    const int k = r / (S * G), rem = r - k * (S * G);
+    const int t = 8 * k + x;
+    return DecSlot{t * S + rem / G, rem % G, t < T};
 }
 
 template <int KV, int OUT>
@@ -99,8 +103,8 @@ void attn_dec_kernel(AttnParams p)
     __shared__ float xl[kWv][kDecHeads];                            // softmax sums
 
     const int G = p.hgroups;
-    const DecSlot sl = dec_slot((int)blockIdx.x, G);
-    if (sl.u >= p.T * p.num_splits) return;
+    const DecSlot sl = dec_slot((int)blockIdx.x, G, p.num_splits, p.T);
+    if (!sl.valid) return;
     const int t = sl.u / p.num_splits, split = sl.u - t * p.num_splits;
     const int hbase = sl.g * kDecHeads;
     const int c_begin = split * p.cols_per_split;
@@ -337,10 +341,14 @@ void attn_dec_kernel(AttnParams p)
 // and head_dim 128w + 16m + 4(l/16) .. +3, so its partial loads are 1 KiB
 // contiguous per split; the loads of U splits go out before any is used.
 template <int OUT, int U, int WPB>   // WPB waves per workgroup
-__global__ __launch_bounds__(64 * WPB) void attn_dec_merge_kernel(AttnParams p)
+__global__ __launch_bounds__(64 * WPB) void attn_dec_merge_kernel(AttnParams p, int nb)
 {
-    const int t = blockIdx.x;
-    const int grp = blockIdx.y * WPB + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    // block b -> (token t, block y of the token's nb): token t on XCD t % 8,
+    // where its partials were written
+    const int x = (int)blockIdx.x & 7, r = (int)blockIdx.x >> 3;
+    const int t = 8 * (r / nb) + x;
+    if (t >= p.T) return;
+    const int grp = (r % nb) * WPB + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int G = p.hgroups;
     if (grp >= G * kWv * kPM) return;
     const int m = grp % kPM, w = (grp / kPM) % kWv, hg = grp / (kPM * kWv);
@@ -392,8 +400,7 @@ __global__ __launch_bounds__(64 * WPB) void attn_dec_merge_kernel(AttnParams p)
 template <int KV, int OUT>
 hipError_t launch_dec_t(const AttnParams &p, hipStream_t s)
 {
-    const int64_t U = (int64_t)p.T * p.num_splits;
-    const int64_t blocks = 8 * p.hgroups * ((U + 7) / 8);
+    const int64_t blocks = 8 * (int64_t)p.num_splits * p.hgroups * ((p.T + 7) / 8);
     hipLaunchKernelGGL((attn_dec_kernel<KV, OUT>), dim3((unsigned)blocks), dim3(64 * kWv), 0, s, p);
     return hipGetLastError();
 }
@@ -405,11 +412,12 @@ hipError_t launch_dec_merge_t(const AttnParams &p, hipStream_t s)
     // a launch of at most one wave per CU takes one-wave workgroups (its
     // waves land on as many CUs), larger ones four waves per workgroup
     const bool one = (int64_t)p.T * groups <= 256;
-    const dim3 grid((unsigned)p.T, (unsigned)(one ? groups : (groups + 3) / 4));
+    const int nb = one ? groups : (groups + 3) / 4;   // workgroups per token
+    const dim3 grid((unsigned)(8 * (int64_t)nb * ((p.T + 7) / 8)));
     auto go = [&](auto u_tag) {
         constexpr int U = decltype(u_tag)::value;
-        if (one) hipLaunchKernelGGL((attn_dec_merge_kernel<OUT, U, 1>), grid, dim3(64), 0, s, p);
-        else hipLaunchKernelGGL((attn_dec_merge_kernel<OUT, U, 4>), grid, dim3(256), 0, s, p);
+        if (one) hipLaunchKernelGGL((attn_dec_merge_kernel<OUT, U, 1>), grid, dim3(64), 0, s, p, nb);
+        else hipLaunchKernelGGL((attn_dec_merge_kernel<OUT, U, 4>), grid, dim3(256), 0, s, p, nb);
     };
     const int S = p.num_splits;
     if (S <= 2) go(std::integral_constant<int, 2>{});
