@@ -196,7 +196,8 @@ def sources_sha256(names) -> str:
 
 # which kernel sources each counted-traffic entry depends on
 TRAFFIC_SOURCES = {
-    "attn": ("attn.hip", "attn_d512.hip", "attn_dec.hip", "attn_common.hpp"),
+    "attn_dec": ("attn_dec.hip", "attn_common.hpp", "formats.hpp"),
+    "attn_d512": ("attn_d512.hip", "attn_common.hpp"),
     "indexer": ("indexer.hip", "formats.hpp"),
 }
 
