@@ -58,6 +58,18 @@ __device__ __forceinline__ uint32_t fp4_elem_exact(uint32_t nib, uint32_t e) {
     return sign | ((2u + mbit) << (u + 132));
 }
 
+// 8 e2m1 codes of one word times scale = 2^(e - 127) for a scale byte e in
+// 2..252 (the caller has checked it), by the hardware scaled conversion,
+// which is exact there.
+__device__ __forceinline__ uint4 fp4x8_scaled_bf16x8(uint32_t word, float scale) {
+    uint4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 1));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 2));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 3));
+    return r;
+}
+
 // 8 e2m1 codes of one word with one scale byte -> 8 bf16 (element e in half
 // e%2 of dword e/2).  Scale bytes 2..252 keep every result a finite normal
 // bf16; there the hardware scaled conversion is exact and is used.  Other
@@ -65,11 +77,7 @@ __device__ __forceinline__ uint32_t fp4_elem_exact(uint32_t nib, uint32_t e) {
 __device__ __forceinline__ uint4 fp4x8_to_bf16x8(uint32_t word, uint32_t e) {
     uint4 r;
     if (e >= 2u && e <= 252u) {
-        const float scale = __uint_as_float(e << 23);     // 2^(e - 127)
-        r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0));
-        r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 1));
-        r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 2));
-        r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 3));
+        r = fp4x8_scaled_bf16x8(word, __uint_as_float(e << 23));   // 2^(e - 127)
     } else {
         uint32_t h[8];
 #pragma unroll

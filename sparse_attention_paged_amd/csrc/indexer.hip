@@ -57,8 +57,12 @@ __global__ __launch_bounds__(64 * NWI) void indexer_kernel(IndexerParams p)
     // the first tile's page-table entry loads together with the valid-key
     // count (the page table holds an entry for every page below N), so the
     // key rows are one memory round trip after them, not two
-    int pte0 = 0;
+    // (so is the second tile's: its rows then go out without waiting for a
+    // page-table read)
+    int pte0 = 0, pte1 = 0;
     if (p.pt && page_tiles && tile0 < n_tiles) pte0 = p.pt[(int64_t)b * p.pt_sb + tile0 * kKeyTile / p.page];
+    if (p.pt && page_tiles && p.tiles_per_wave > 1 && tile0 + 1 < n_tiles)
+        pte1 = p.pt[(int64_t)b * p.pt_sb + (tile0 + 1) * kKeyTile / p.page];
     const int nk = p.n_keys ? min(p.n_keys[b], p.N) : p.N;
 
     // q as the A operand: k-step s holds q[b, head l32, 16s + 8hh .. +7]
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(64 * NWI) void indexer_kernel(IndexerParams p)
         int64_t row0 = (int64_t)b * p.N + key0;
         if (p.pt && page_tiles) {
             const int pg = key0 / p.page;
-            const int e = kt == tile0 ? pte0 : p.pt[(int64_t)b * p.pt_sb + pg];
+            const int e = kt == tile0 ? pte0 : kt == tile0 + 1 ? pte1 : p.pt[(int64_t)b * p.pt_sb + pg];
             row0 = (int64_t)e * p.page + (key0 - pg * p.page);
         }
         // (VEC: a tile that holds the last valid key loads whole: its page
@@ -158,11 +162,22 @@ __global__ __launch_bounds__(64 * NWI) void indexer_kernel(IndexerParams p)
             const uint32_t *r = st + (nt * 32 + l32) * kRowWords;
             const uint32_t sw = r[16];
             f32x16 acc = {};
+            // the row's four scale bytes: when every lane's lie in 2..252 the
+            // hardware scaled conversion is exact for all of them
+            const uint32_t e0 = sw & 0xFFu, e1 = (sw >> 8) & 0xFFu, e2 = (sw >> 16) & 0xFFu, e3 = sw >> 24;
+            const uint32_t emin = min(min(e0, e1), min(e2, e3)), emax = max(max(e0, e1), max(e2, e3));
+            if (__builtin_amdgcn_ballot_w64(emin < 2u || emax > 252u) == 0) {
+                const float sc[4] = {__uint_as_float(e0 << 23), __uint_as_float(e1 << 23), __uint_as_float(e2 << 23),
+                                     __uint_as_float(e3 << 23)};
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const uint32_t word = r[2 * s + hh];
-                const uint32_t e = (sw >> (8 * (s >> 1))) & 0xFFu;
-                acc = mfma32x32x16(qa[s], fp4x8_to_bf16x8(word, e), acc);
+                for (int s = 0; s < 8; ++s) acc = mfma32x32x16(qa[s], fp4x8_scaled_bf16x8(r[2 * s + hh], sc[s >> 1]), acc);
+            } else {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const uint32_t word = r[2 * s + hh];
+                    const uint32_t e = (sw >> (8 * (s >> 1))) & 0xFFu;
+                    acc = mfma32x32x16(qa[s], fp4x8_to_bf16x8(word, e), acc);
+                }
             }
             float part = 0.0f;
 #pragma unroll
