@@ -39,7 +39,8 @@ def hipcc() -> str:
 
 
 def check_no_scratch(remarks: str) -> None:
-    """The bf16 attention kernels count their own in-flight gathers with
+    """The attention kernels that gather rows with LDS DMA (bf16 rows, and
+    e4m3 rows in the one-pass kernel at head_dim 512) count their own in-flight gathers with
     s_waitcnt vmcnt(N); a compiler-generated scratch access would be one more
     vector memory operation in that count.  Refuse such a build."""
     name = None
@@ -51,7 +52,7 @@ def check_no_scratch(remarks: str) -> None:
         m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
         if m and name and int(m.group(1)) > 0:
             # attn_kernel<D, KV, OUT, NW>: KV == 0 is bf16 (mangled ...ILi<D>ELi0E...);
-            # attn_d512_kernel is bf16 only
+            # attn_d512_kernel counts its gathers for bf16 and e4m3 rows alike
             if re.search(r"attn_kernelILi\d+ELi0E", name) or "attn_d512_kernel" in name:
                 raise RuntimeError(f"{name} uses scratch memory ({m.group(1)} bytes/lane); "
                                    "its gather wait counts would be wrong")

@@ -857,7 +857,7 @@ hipError_t launch_attn_d(const AttnParams &p, int kv, int out, hipStream_t s)
     // bf16 rows at head_dim 512, one split per token (prefill): the
     // one-barrier kernel of attn_d512.hip; split-K (decode) stays here, where
     // eight waves share the q staging and partial stores of the few workgroups
-    if (D == 512 && kv == 0 && p.num_splits == 1) return launch_attn_d512(p, out, s);
+    if (D == 512 && p.num_splits == 1) return launch_attn_d512(p, kv, out, s);
     if (kv == 0) return out == 1 ? launch_attn_t<D, 0, 1>(p, s) : launch_attn_t<D, 0, 0>(p, s);
     return out == 1 ? launch_attn_t<D, 2, 1>(p, s) : launch_attn_t<D, 2, 0>(p, s);
 }

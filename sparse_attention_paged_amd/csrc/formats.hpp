@@ -32,6 +32,17 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 c) {
     return r;
 }
 
+// 8 codes -> 8 f16 (element e in half e%2 of dword e/2).  Every finite e4m3
+// value (|x| in [2^-9, 448], 4 significant bits) is exactly an f16 as well.
+__device__ __forceinline__ uint4 e4m3x8_to_f16x8(uint2 c) {
+    uint4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.x, 1.0f, false));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.x, 1.0f, true));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.y, 1.0f, false));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.y, 1.0f, true));
+    return r;
+}
+
 // ---------------------------------------------------------------------------
 // fp4_e8m0_b32 ("perf(kernel): read dsv41 indexer key rows as int32 words",
 // Changes).  One key row is 17 int32 words: words 0..15 carry 128 e2m1 codes

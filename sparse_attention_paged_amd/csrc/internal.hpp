@@ -43,9 +43,9 @@ constexpr int kMergeSplits = 24;
 // kv: 0 = bf16, 2 = e4m3.  out: 0 = bf16, 1 = f32.
 hipError_t launch_attn(const AttnParams &p, int D, int kv, int out_dtype, hipStream_t s);
 hipError_t launch_attn_merge(const AttnParams &p, int D, int kv, int out_dtype, hipStream_t s);
-// bf16 rows at head_dim 512 with one split per token (attn_d512.hip);
-// launch_attn dispatches to it
-hipError_t launch_attn_d512(const AttnParams &p, int out_dtype, hipStream_t s);
+// bf16 or e4m3 rows (kv 0 or 2) at head_dim 512 with one split per token
+// (attn_d512.hip); launch_attn dispatches to it
+hipError_t launch_attn_d512(const AttnParams &p, int kv, int out_dtype, hipStream_t s);
 // split-K decode at head_dim 512 (attn_dec.hip) and its merge
 hipError_t launch_attn_dec(const AttnParams &p, int kv, int out_dtype, hipStream_t s);
 hipError_t launch_attn_dec_merge(const AttnParams &p, int out_dtype, hipStream_t s);

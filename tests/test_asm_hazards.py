@@ -183,18 +183,25 @@ def _kernels(lines, stem):
 def test_prefill_token_switch_wait_counts(tmp_path):
     """The prefill kernel waits for the next token's first tiles with
     hand-counted vmcnt values that assume exactly this order of vector memory
-    instructions at a token switch: the 16 row DMAs of tiles 0 and 1 (8 rows
-    per wave each), then the previous token's 32 output stores (8 m-steps x 4
-    head blocks), then the next token's index loads.  Fewer or merged stores
-    would let a wait pass before its tile has landed, so the order and the
-    count are checked here."""
+    instructions at a token switch: the gathers of tiles 0 and 1 (bf16 rows:
+    8 row DMAs per wave and tile; e4m3 rows: 4 DMAs of two rows each, then
+    the rows' scales), then the previous token's 32 output stores (8 m-steps
+    x 4 head blocks), then the next token's index loads.  Fewer or merged
+    stores would let a wait pass before its tile has landed, so the order and
+    the count are checked here."""
     kern = _kernels(_compile(tmp_path, "attn_d512"), "attn_d512_kernel")
-    assert len(kern) == 2, list(kern)
+    assert len(kern) == 4, list(kern)
     for name, code in kern.items():
+        e4 = "Lb1E" in name   # attn_d512_kernel<OUT, E4 = true>
         vm = [t for t in code if t.startswith(_VM)]
         first_store = next(i for i, t in enumerate(vm) if t.startswith("global_store"))
-        before = vm[first_store - 16:first_store]
-        assert all(t.startswith("global_load_lds_dwordx4") for t in before), (name, before)
+        if e4:
+            before = vm[first_store - 10:first_store]
+            tile = ["global_load_lds_dwordx4"] * 4 + ["global_load_lds_dword"]
+            assert [t.split()[0] for t in before] == tile * 2, (name, before)
+        else:
+            before = vm[first_store - 16:first_store]
+            assert all(t.startswith("global_load_lds_dwordx4") for t in before), (name, before)
         run = 0
         for t in vm[first_store:]:
             if not t.startswith("global_store"):
@@ -205,7 +212,7 @@ def test_prefill_token_switch_wait_counts(tmp_path):
 
 
 def test_m0_written_only_by_the_row_gathers(tmp_path):
-    """The row gathers set m0 (the LDS address of global_load_lds) from inline
+    """The row (and row-scale) gathers set m0 (the LDS address of global_load_lds) from inline
     assembly, which the compiler does not preserve around: no compiler-placed
     instruction may read or write m0 in these kernels (indirect register
     indexing, s_sendmsg and the like would)."""
@@ -218,7 +225,7 @@ def test_m0_written_only_by_the_row_gathers(tmp_path):
                 continue
             if t.startswith("s_mov_b32 m0, s"):
                 nxt = [u for u in code[i + 1:i + 4] if u and not u.startswith("s_nop")]
-                if nxt and nxt[0].startswith("global_load_lds_dwordx4"):
+                if nxt and nxt[0].startswith(("global_load_lds_dwordx4", "global_load_lds_dword ")):
                     continue
             bad.append(t)
         assert not bad, f"{name}: m0 used outside the row-gather assembly: {bad[:3]}"

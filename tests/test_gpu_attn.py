@@ -202,6 +202,49 @@ def test_prefill_persistent_chunks_partial_heads():
     assert_attn_close(gpu_attn(case, num_splits=1), ref, "prefill T=300 H=20 3128 columns")
 
 
+def _late_jump_case(kv: str, seed: int):
+    """One token over 96 columns (three tiles) whose third tile holds a row
+    aligned with head 5's query: that head's running max jumps by hundreds of
+    log2 units after the first tile, and so do several other heads' (by tens).
+    Without the rescale the weights of such a head overflow."""
+    g = torch.Generator().manual_seed(seed)
+    H, D, N = 64, 512, 96
+    q = torch.randn((1, H, D), generator=g)
+    if kv == "bf16":
+        # rows of the workload's size; head 5's query 8x larger, so that its
+        # score against row 70 passes 2^128 in the weights' exponent
+        q[0, 5] *= 8.0
+        q = q.to(torch.bfloat16)
+        sgn = torch.where(q[0, 5].float() >= 0, 1.0, -1.0)
+        pool = torch.randn((N, D), generator=g).to(torch.bfloat16)
+        pool[70] = (2.0 * sgn).to(torch.bfloat16)
+        scale = None
+    else:
+        q = q.to(torch.bfloat16)
+        sgn = torch.where(q[0, 5].float() >= 0, 1.0, -1.0)
+        vals = torch.tensor([-1.0, -0.5, 0.5, 1.0])[torch.randint(0, 4, (N, D), generator=g)]
+        vals[70] = 16.0 * sgn
+        pool = vals.to(torch.float8_e4m3fn).view(torch.uint8)
+        scale = torch.exp2(torch.rand(N, generator=g) * 2.0 - 1.0).to(torch.float32)
+    idx = torch.arange(N, dtype=torch.int32)[None, :]
+    return q, pool, scale, idx
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+def test_late_max_jump_on_any_head(kv):
+    """The one-pass kernel rescales when a later tile's max passes the
+    running max by more than its slack: every head of the wave must be able
+    to raise that flag, not only the first of each 16-head tile."""
+    need_gpu()
+    q, pool, scale, idx = _late_jump_case(kv, 180 + (kv == "e4m3"))
+    sm = 1.0 / math.sqrt(512)
+    ref = oracle.sparse_attn(q, pool, None, idx, idx.shape[1], sm, scale, None)
+    out = sap.sparse_attn_paged(dev(q), dev(pool), None, dev(idx), idx.shape[1], sm,
+                                win_scale=dev(scale), num_splits=1)
+    torch.cuda.synchronize()
+    assert_attn_close(out, ref, f"late max jump {kv}")
+
+
 @pytest.mark.parametrize("n_win,topk", [(100, 512), (50, 37), (128, 300), (128, 1), (0, 64), (1, 0)])
 def test_window_and_topk_widths(n_win, topk):
     need_gpu()
@@ -270,17 +313,17 @@ def test_ratio0_alias_and_row_offset_views():
 
 
 def test_bf16_output():
-    # A bf16 output adds one rounding (at most half an ulp, <= 2^-9 |x|) on
-    # top of the fp32-output bar: rel-L2 grows by 2^-9 and max-abs by
-    # 2^-9 max|ref| (tokens with one or two columns output a row itself).
+    # A bf16 output adds one rounding on top of the fp32-output bar: half an
+    # ulp of an 8-bit significand, at most 2^-8 |x| (just above a power of
+    # two), so rel-L2 grows by 2^-8 and max-abs by 2^-8 max|ref|.
     need_gpu()
     for case, splits in ((W.decode_case(B=8, ratio=4, seed=W.SEED_BASE + 90), 0),
                          (W.prefill_case(T=300, ratio=4, seed=W.SEED_BASE + 91), 1)):
         ref = oracle.case_attn(case)
         out = gpu_attn(case, out_dtype=torch.bfloat16, num_splits=splits)
         assert out.dtype == torch.bfloat16
-        bound = 1e-2 + 2.0 ** -9 * ref.abs().max().item()
-        assert_attn_close(out.float(), ref, f"bf16 out {case.name}", max_abs=bound, rel_l2=2e-3 + 2.0 ** -9)
+        bound = 1e-2 + 2.0 ** -8 * ref.abs().max().item()
+        assert_attn_close(out.float(), ref, f"bf16 out {case.name}", max_abs=bound, rel_l2=2e-3 + 2.0 ** -8)
 
 
 def test_determinism_sha256():
