@@ -350,6 +350,8 @@ int sap_topk_sparse_idx(const float *logits, int64_t stride_t, const int32_t *n_
  * sap_debug_e4m3_table: out[c] = bf16 bits the attention row loader produces
  *   for e4m3 code c (c = 0..255); *fold_factor = the factor that multiplies
  *   that 16-bit value to give the code's value (folded into the row scale).
+ * sap_debug_e4m3_f16_table: out[c] = f16 bits of e4m3 code c as the one-pass
+ *   kernel at head_dim 512 widens its V^T operand (fold factor 1).
  * sap_debug_fp4_table: out[(c * 256 + s) * 2 + j] = bf16 bits of nibble j
  *   (0 = low, 1 = high) of code byte c times scale byte s, as the indexer's
  *   row loader dequantises them.
@@ -357,6 +359,7 @@ int sap_topk_sparse_idx(const float *logits, int64_t stride_t, const int32_t *n_
  * ------------------------------------------------------------------------- */
 int sap_debug_e4m3_table(uint16_t *out /* [256] */, float *fold_factor /* [1] */,
                          sap_stream_t stream);
+int sap_debug_e4m3_f16_table(uint16_t *out /* [256] */, sap_stream_t stream);
 int sap_debug_fp4_table(uint16_t *out /* [256 * 256 * 2] */, sap_stream_t stream);
 
 #ifdef __cplusplus

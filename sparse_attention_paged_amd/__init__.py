@@ -5,7 +5,7 @@ include/sap.h).  This package only marshals torch device tensors into that
 ABI: pointers, strides, dtypes and the current HIP stream.
 """
 from ._lib import LIB_PATH, SapError, lib, status_string
-from .api import (build_sparse_idx, debug_e4m3_table, debug_fp4_table, gated_pool, indexer_logits_candidates,
+from .api import (build_sparse_idx, debug_e4m3_table, debug_e4m3_f16_table, debug_fp4_table, gated_pool, indexer_logits_candidates,
                   indexer_logits_packed, indexer_logits_prefill,
                   sparse_attn_noalloc_max_bytes, sparse_attn_num_splits, sparse_attn_paged,
                   sparse_attn_paged_noalloc, sparse_attn_workspace_bytes,
@@ -16,5 +16,5 @@ __all__ = [
     "sparse_attn_num_splits", "sparse_attn_workspace_bytes",
     "sparse_attn_paged_noalloc", "sparse_attn_noalloc_max_bytes", "indexer_logits_packed",
     "indexer_logits_candidates", "indexer_logits_prefill", "topk_select",
-    "topk_workspace_bytes", "topk_sparse_idx", "gated_pool", "debug_e4m3_table", "debug_fp4_table",
+    "topk_workspace_bytes", "topk_sparse_idx", "gated_pool", "debug_e4m3_table", "debug_e4m3_f16_table", "debug_fp4_table",
 ]

@@ -36,6 +36,7 @@ SIGNATURES = {
     "sap_topk_sparse_idx": (_I, [_P, _I64, _P, _I, _I, _I, _P, _P, _I, _P, _I64, _P, _I64, _I, _P, _I64, _P,
                                  _SZ, _P]),
     "sap_debug_e4m3_table": (_I, [_P, _P, _P]),
+    "sap_debug_e4m3_f16_table": (_I, [_P, _P]),
     "sap_debug_fp4_table": (_I, [_P, _P]),
 }
 

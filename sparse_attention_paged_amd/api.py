@@ -269,6 +269,13 @@ def debug_e4m3_table(device="cuda"):
     return out, fold
 
 
+def debug_e4m3_f16_table(device="cuda"):
+    """uint16 [256]: f16 bits of each e4m3 code from the one-pass kernel's V^T widening."""
+    out = torch.empty(256, dtype=torch.int16, device=device)
+    check(lib().sap_debug_e4m3_f16_table(_p(out), _stream(out)), "sap_debug_e4m3_f16_table")
+    return out
+
+
 def debug_fp4_table(device="cuda"):
     """int16 [256, 256, 2]: bf16 bits of (code byte, scale byte, nibble) from the indexer's decoder."""
     out = torch.empty((256, 256, 2), dtype=torch.int16, device=device)

@@ -25,6 +25,20 @@ __global__ __launch_bounds__(64) void debug_e4m3_kernel(uint16_t *out, float *fo
     if (lane == 0) *fold = kE4m3FoldFactor;
 }
 
+// the f16 widening of the one-pass kernel at head_dim 512 (its V^T operand)
+__global__ __launch_bounds__(64) void debug_e4m3_f16_kernel(uint16_t *out)
+{
+    const int lane = threadIdx.x;
+    if (lane >= 32) return;
+    const uint32_t c0 = 8u * lane;
+    uint2 codes;
+    codes.x = c0 | ((c0 + 1) << 8) | ((c0 + 2) << 16) | ((c0 + 3) << 24);
+    codes.y = (c0 + 4) | ((c0 + 5) << 8) | ((c0 + 6) << 16) | ((c0 + 7) << 24);
+    const uint4 r = e4m3x8_to_f16x8(codes);
+    const uint32_t dw[4] = {r.x, r.y, r.z, r.w};
+    for (int e = 0; e < 8; ++e) out[c0 + e] = (uint16_t)(dw[e >> 1] >> (16 * (e & 1)));
+}
+
 __global__ __launch_bounds__(256) void debug_fp4_kernel(uint16_t *out)
 {
     // one code byte per block, one scale byte per thread
@@ -39,6 +53,12 @@ __global__ __launch_bounds__(256) void debug_fp4_kernel(uint16_t *out)
 hipError_t launch_debug_e4m3(uint16_t *out, float *fold, hipStream_t s)
 {
     hipLaunchKernelGGL(debug_e4m3_kernel, dim3(1), dim3(64), 0, s, out, fold);
+    return hipGetLastError();
+}
+
+hipError_t launch_debug_e4m3_f16(uint16_t *out, hipStream_t s)
+{
+    hipLaunchKernelGGL(debug_e4m3_f16_kernel, dim3(1), dim3(64), 0, s, out);
     return hipGetLastError();
 }
 

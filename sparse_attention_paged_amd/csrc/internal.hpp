@@ -145,6 +145,7 @@ struct IdxBuildParams {
 hipError_t launch_build_idx(const IdxBuildParams &p, hipStream_t s);
 
 hipError_t launch_debug_e4m3(uint16_t *out, float *fold, hipStream_t s);
+hipError_t launch_debug_e4m3_f16(uint16_t *out, hipStream_t s);
 hipError_t launch_debug_fp4(uint16_t *out, hipStream_t s);
 
 }  // namespace sap

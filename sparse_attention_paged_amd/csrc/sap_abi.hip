@@ -581,6 +581,12 @@ int sap_debug_e4m3_table(uint16_t *out, float *fold_factor, sap_stream_t stream)
     return launched(sap::launch_debug_e4m3(out, fold_factor, (hipStream_t)stream));
 }
 
+int sap_debug_e4m3_f16_table(uint16_t *out, sap_stream_t stream)
+{
+    if (!out) return SAP_ERR_NULL;
+    return launched(sap::launch_debug_e4m3_f16(out, (hipStream_t)stream));
+}
+
 int sap_debug_fp4_table(uint16_t *out, sap_stream_t stream)
 {
     if (!out) return SAP_ERR_NULL;

@@ -32,6 +32,23 @@ def test_e4m3_loader_table_bit_exact():
     say(f"  e4m3: 254 finite codes exact, fold factor {f}")
 
 
+def test_e4m3_f16_loader_table_bit_exact():
+    """The one-pass kernel at head_dim 512 widens V^T to f16: every finite
+    e4m3 value (4 significant bits, |x| in [2^-9, 448]) is exactly an f16."""
+    need_gpu()
+    bits = sap.debug_e4m3_f16_table()
+    torch.cuda.synchronize()
+    vals = bits.cpu().numpy().astype(np.uint16).view(np.float16).astype(np.float64)
+    ref = oracle.e4m3_table()
+    for c in range(256):
+        got = float(vals[c])
+        if math.isnan(ref[c]):
+            assert math.isnan(got), hex(c)
+        else:
+            assert got == ref[c] and math.copysign(1, got) == math.copysign(1, ref[c]), (hex(c), got, ref[c])
+    say("  e4m3 -> f16: 254 finite codes exact")
+
+
 def test_fp4_loader_table_bit_exact():
     need_gpu()
     got = sap.debug_fp4_table().cpu().numpy().astype(np.uint16)      # [code, scale, nibble]
