@@ -1,6 +1,6 @@
 // attn_common.hpp -- device helpers shared by the attention kernels
-// (attn.hip: every head_dim and row format; attn_d512.hip: bf16 rows at
-// head_dim 512).
+// (attn.hip: every head_dim and row format; attn_d512.hip and attn_dec.hip:
+// bf16 and e4m3 rows at head_dim 512).
 #pragma once
 #include "common.hpp"
 #include "internal.hpp"
@@ -26,6 +26,37 @@ __device__ __forceinline__ uint2 lds_tr16(const uint8_t *p)
     v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4i16 __attribute__((address_space(3))) *)p);
     return __builtin_bit_cast(uint2, r);
 }
+
+// An e4m3 tile (raw codes, 512 bytes per row): row rho holds 16-byte chunk j
+// at slot j ^ eswz(rho).  16 consecutive rows take 16 distinct values (the S
+// reads: 16 rows, one chunk), and so do rows {4a .. 4a+3, 16+4a .. 16+4a+3}
+// and the 16 rows that two neighbouring 16-lane blocks of a transposed V^T
+// read cover.
+__device__ __forceinline__ int eswz(int rho) { return (rho & 7) | ((((rho >> 3) ^ (rho >> 4)) & 1) << 3); }
+
+// ds_read_b64_tr_b8: in each 16-lane block, lane 8h + i receives byte i of
+// the 8 bytes addressed by lanes 2k + h, k = 0..7 (byte k of the result)
+__device__ __forceinline__ uint2 lds_tr8(const uint8_t *p)
+{
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i __attribute__((address_space(3))) *)p);
+    return __builtin_bit_cast(uint2, r);
+}
+
+// a, b -> two f16 terms each (round to nearest): hi = f16(a), lo =
+// f16(a - hi); a - hi is exact in fp32 and |a - (hi + lo)| <= 2^-22 |a|
+// above the f16 subnormal range (an absolute 2^-25 below it)
+__device__ __forceinline__ void split_f16x2(float a, float b, uint32_t &hi, uint32_t &lo)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 h = __builtin_convertvector((f32x2{a, b}), f16x2);
+    const f16x2 l = __builtin_convertvector((f32x2{a - (float)h[0], b - (float)h[1]}), f16x2);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
+}
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // max over the four lanes l, l^16, l^32, l^48 with the gfx950 row-swap
 // permutes (VALU, no LDS round trip)

@@ -92,21 +92,6 @@ __device__ __forceinline__ void dma_row(uint64_t base, uint32_t voff, uint32_t l
                  :: "v"(voff), "s"(base), "s"(lds) : "memory", "m0");
 }
 
-// e4m3 tile row rho holds 16-byte chunk j at slot j ^ eswz(rho): 16
-// consecutive rows take 16 distinct values (the S reads: 16 rows, one chunk),
-// and so do rows {4a .. 4a+3, 16+4a .. 16+4a+3} and the 16 rows that two
-// neighbouring 16-lane blocks of a transposed V^T read cover.
-__device__ __forceinline__ int eswz(int rho) { return (rho & 7) | ((((rho >> 3) ^ (rho >> 4)) & 1) << 3); }
-
-// ds_read_b64_tr_b8: in each 16-lane block, lane 8h + i receives byte i of
-// the 8 bytes addressed by lanes 2k + h, k = 0..7 (byte k of the result)
-__device__ __forceinline__ uint2 lds_tr8(const uint8_t *p)
-{
-    typedef int v2i __attribute__((ext_vector_type(2)));
-    const v2i r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((v2i __attribute__((address_space(3))) *)p);
-    return __builtin_bit_cast(uint2, r);
-}
-
 // 4 bytes per lane from global memory into LDS at lds_addr + 4 * lane
 // (global_load_lds_dword), untracked like dma16
 __device__ __forceinline__ void dma4(const void *src, uint32_t lds_addr)
@@ -142,7 +127,6 @@ __device__ __forceinline__ void mfma_s(f32x4 &c, const uint4 &a, const bf16x8 &b
 // the e4m3 PV step: O (AGPRs) += V^T (f16) P^T (one f16 term of the weights).
 // V^T comes from a VALU conversion, made a whole m-step (eight MFMAs) before
 // the MFMAs that read it.
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ void mfma_acc_f16(f32x4 &c, const uint4 &a, const uint4 &b)
 {
     asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
@@ -200,18 +184,6 @@ __device__ __forceinline__ void pin(uint4 &v)
 // wait states between an MFMA's last write of a VGPR and a VALU read of it
 __device__ __forceinline__ void s_wait_mfma() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory"); }
 
-// a, b -> two f16 terms each (round to nearest): hi = f16(a), lo =
-// f16(a - hi); a - hi is exact in fp32 and |a - (hi + lo)| <= 2^-22 |a|
-// above the f16 subnormal range (an absolute 2^-25 below it)
-__device__ __forceinline__ void split_f16x2(float a, float b, uint32_t &hi, uint32_t &lo)
-{
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-    const f16x2 h = __builtin_convertvector((f32x2{a, b}), f16x2);
-    const f16x2 l = __builtin_convertvector((f32x2{a - (float)h[0], b - (float)h[1]}), f16x2);
-    hi = __builtin_bit_cast(uint32_t, h);
-    lo = __builtin_bit_cast(uint32_t, l);
-}
 
 template <int OUT, bool E4>
 __global__ __attribute__((amdgpu_flat_work_group_size(kNT, kNT), amdgpu_waves_per_eu(1, 1)))

@@ -17,7 +17,7 @@
 // rows (and more) it summarises:
 //  - gather: wave w moves its 32 rows from HBM straight into its own LDS tile
 //    (global_load_lds_dwordx4: one 1 KiB row per wave instruction, 16-byte
-//    loads; e4m3 rows pass through registers and are widened to bf16);
+//    loads; e4m3 rows: the raw codes, two 512-byte rows per instruction);
 //  - S^T = K Q^T for the wave's 32 columns and the 16 heads over all 512
 //    dims on MFMA 16x16x32 bf16 (M = columns, N = heads): the wave's own rows
 //    and its own copy of Q, so no partial score crosses waves;
@@ -30,6 +30,11 @@
 //    over all 128 columns of the round (the other waves' weights come through
 //    LDS, one barrier); V^T fragments are read from the four row-major tiles
 //    with ds_read_b64_tr_b16.
+// e4m3 rows: K fragments are widened to bf16 in registers (exact); the row
+// scale s = mu * 2^e multiplies the scores and e joins the log2 score, V^T
+// comes from ds_read_b64_tr_b8 widened to f16 (exact), and the weights
+// p * s = mu * exp2(x + e - m) (below 1: the running max is exact here)
+// enter PV as two f16 terms; the sums take p = 2^-e exp2(x + e - m).
 // One split per token stores the normalised output; several splits store
 // (unnormalised O, running max, sum) and attn_dec_merge_kernel combines them
 // in split order.  All workgroups of one token -- its splits and head groups
@@ -51,8 +56,11 @@ constexpr int kD = 512;                 // head_dim
 constexpr int kWv = 4;                  // waves per workgroup
 constexpr int kCW = 32;                 // columns per wave per round
 constexpr int kRows = kDecRound;        // columns per round (kWv * kCW)
-constexpr int kTileB = kCW * kD * 2;    // one wave's bf16 tile
 constexpr int kPM = kD / (16 * kWv);    // PV m-steps over a wave's head_dim quarter
+
+// what unused columns of an e4m3 tile gather: zeros (any other stand-in's
+// bytes could hold the e4m3 NaN codes, and a zero weight times NaN is NaN)
+__device__ __attribute__((aligned(16))) uint8_t g_dec_pad_row[kD];
 
 static_assert(kRows == kWv * kCW, "a round is one tile per wave");
 
@@ -90,12 +98,13 @@ template <int KV, int OUT>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWv, 64 * kWv), amdgpu_waves_per_eu(1, 1)))
 void attn_dec_kernel(AttnParams p)
 {
-    // bf16 terms per PV weight: e4m3 weights carry the row scale and must be
-    // held to fp32-like precision (outputs reach ~1e3 against an absolute
-    // bar), so they enter as hi + mid + lo
-    constexpr int NP = KV == 2 ? 3 : 1;
-    using Raw = typename std::conditional<KV == 2, uint2, uint4>::type;
-    __shared__ __attribute__((aligned(1024))) uint8_t tiles[kWv][kTileB];
+    constexpr bool E4 = KV == 2;
+    // PV weight terms: e4m3 weights carry the row scale and must be held to
+    // fp32-like precision (outputs reach ~1e3 against an absolute bar), so
+    // they enter as two f16 terms, hi + lo
+    constexpr int NP = E4 ? 2 : 1;
+    constexpr int kRB = E4 ? kD : 2 * kD;   // bytes of one tile row
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles[kWv][kCW * kRB];
     __shared__ __attribute__((aligned(1024))) uint8_t qs[kDecHeads * kD * 2];
     __shared__ __attribute__((aligned(16))) uint4 xp[NP][kWv][64];   // weights of each wave's columns
     __shared__ __attribute__((aligned(16))) float meta[kWv][2][kCW]; // per column: bias (0 / -inf), scale
@@ -142,6 +151,24 @@ void attn_dec_kernel(AttnParams p)
             vb[mm] = r * kD * 2 + 16 * ((d >> 3) ^ vs) + 2 * (d & 7);
         }
     }
+    // e4m3 tiles: read u of column half c is chunk 4u + g (dims 16(4u + g)
+    // .. +15, the K fragments of k-steps 2u and 2u + 1) of row 16c + l16, at
+    // slot (4u + g) ^ eswz(row) = 16(u / 4) + (4(u % 4) ^ g ^ l16 ^ 8c).
+    // V^T (ds_read_b64_tr_b8): lane l16 of block g addresses row R = 4g +
+    // l16/2 (l16 < 8) or 16 + 4g + l16/2 - 4, bytes 8(l16 % 2) .. +7 of chunk
+    // 8w + m at slot vy ^ m; result byte k is column R(2k) at head_dim 128w +
+    // 16m + l16, the columns of the weights' B-operand layout
+    int kbe[2][4], vrow = 0, vy = 0;
+    if constexpr (E4) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) kbe[c][u] = (16 * c + l16) * kRB + 16 * ((4 * u) ^ g ^ l16 ^ (8 * c));
+        const int k = l16 >> 1;
+        const int R = k < 4 ? 4 * g + k : 16 + 4 * g + (k - 4);
+        vrow = R * kRB + 8 * (l16 & 1);
+        vy = (8 * w) ^ eswz(R);
+    }
 
     f32x4 acc[kPM];
 #pragma unroll
@@ -161,77 +188,112 @@ void attn_dec_kernel(AttnParams p)
         const int e = e_next;
         const bool win = cw + lane < p.n_win;
         if (!first) __syncthreads();   // every wave has finished PV of the previous round
-        float scl = 0.0f;
-        if (lane < kCW) {
-            if constexpr (KV == 2) {
-                if (e >= 0) scl = (win ? p.win_scale : p.cmp_scale)[e];
-            }
-            meta[w][0][lane] = e >= 0 ? 0.0f : -INFINITY;
-        }
+        if (lane < kCW) meta[w][0][lane] = e >= 0 ? 0.0f : -INFINITY;
         // gathers: row r of the tile is column cw + r.  Lane r forms the row's
         // address (a stand-in row for an unused column), and each row goes out
         // with that address as a scalar base; chunk j of the row goes to slot
-        // j ^ rswz(r)
-        const uint8_t *rsrc = safe_src;
+        // j ^ rswz(r).  e4m3: gather q moves rows 2q (lanes 0-31) and 2q + 1
+        // (lanes 32-63), lane L filling slot L % 32 of its row, i.e. loading
+        // chunk (L % 32) ^ eswz(row)
+        const uint8_t *rsrc = E4 ? g_dec_pad_row : safe_src;
         if (e >= 0) rsrc = (win ? p.win : p.cmp) + (int64_t)e * (win ? p.win_rs : p.cmp_rs);
         const uint32_t alo = (uint32_t)(uintptr_t)rsrc, ahi = (uint32_t)((uintptr_t)rsrc >> 32);
-        Raw raw[kCW];
+        if constexpr (!E4) {
 #pragma unroll
-        for (int r = 0; r < kCW; ++r) {
-            const uint64_t rb = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ahi, r) << 32) |
-                                (uint32_t)__builtin_amdgcn_readlane((int)alo, r);
-            if constexpr (KV == 0) {
+            for (int r = 0; r < kCW; ++r) {
+                const uint64_t rb = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)ahi, r) << 32) |
+                                    (uint32_t)__builtin_amdgcn_readlane((int)alo, r);
                 dma_row(rb, 16 * (lane ^ rswz(r)), lds_offset(mytile + r * kD * 2));
-            } else {
-                // unused columns keep zero codes (arbitrary bytes may be NaN encodings)
-                const uint2 v = *(const uint2 *)((const uint8_t *)(uintptr_t)rb + 8 * lane);
-                raw[r] = __builtin_amdgcn_readlane(e, r) >= 0 ? v : make_uint2(0u, 0u);
+            }
+        } else {
+            const bool hi_half = lane >= 32;
+            const int ez = (lane & 31) ^ (lane >> 5);
+#pragma unroll
+            for (int q = 0; q < kCW / 2; ++q) {
+                const uint32_t lo0 = (uint32_t)__builtin_amdgcn_readlane((int)alo, 2 * q);
+                const uint32_t hi0 = (uint32_t)__builtin_amdgcn_readlane((int)ahi, 2 * q);
+                const uint32_t lo1 = (uint32_t)__builtin_amdgcn_readlane((int)alo, 2 * q + 1);
+                const uint32_t hi1 = (uint32_t)__builtin_amdgcn_readlane((int)ahi, 2 * q + 1);
+                const uint64_t b = ((uint64_t)(hi_half ? hi1 : hi0) << 32) | (hi_half ? lo1 : lo0);
+                const int sw = eswz(2 * q) & ~1;   // eswz(2q + h) = sw ^ h
+                dma16((const void *)(b + 16u * (uint32_t)(ez ^ sw)), lds_offset(mytile + 2 * q * kRB));
             }
         }
-        if (lane < kCW) meta[w][1][lane] = scl;
+        // e4m3: the row scales (unused columns 0), loaded after the gathers
+        // so the wait for q below counts them out
+        float scl = 0.0f;
+        if constexpr (E4) {
+            if (lane < kCW && e >= 0) scl = (win ? p.win_scale : p.cmp_scale)[e];
+        }
         e_next = -1;
         if (lane < kCW && cw + kRows + lane < c_end) e_next = idx_row[cw + kRows + lane];
         if (first) {
             // q has landed in every wave (each waits for its own DMAs, the
-            // barrier publishes them); read the fragments while the rows fly
-            if constexpr (KV == 0) wait_vm<kCW>();
-            else wait_vm<0>();
+            // barrier publishes them); read the fragments while the rows fly.
+            // e4m3: step s = 2u + h takes dims 16(4u + g) + 8h .. +7 (the
+            // order of the K reads), chunk 8u + 2g + h of the q row
+            if constexpr (!E4) wait_vm<kCW>();
+            else wait_vm<kCW / 2>();
             __syncthreads();
             const uint8_t *qrow = qs + l16 * kD * 2;
 #pragma unroll
-            for (int s = 0; s < kD / 32; ++s) qf[s] = lds_b128(qrow + 16 * ((4 * s + g) ^ l16));
+            for (int s = 0; s < kD / 32; ++s) {
+                const int qc = E4 ? 8 * (s >> 1) + 2 * g + (s & 1) : 4 * s + g;
+                qf[s] = lds_b128(qrow + 16 * (qc ^ l16));
+            }
             first = false;
         }
-        if constexpr (KV == 0) {
-            wait_vm<0>();
-        } else {
-            wait_vm<0>();
-#pragma unroll
-            for (int r = 0; r < kCW; ++r)
-                *(uint4 *)(mytile + r * kD * 2 + 16 * (lane ^ rswz(r))) = e4m3x8_to_bf16x8(raw[r]);
+        wait_vm<0>();
+        if constexpr (E4) {
+            if (lane < kCW) meta[w][1][lane] = scl;
         }
 
         // S^T of the wave's columns 16c + 4g + i, heads hbase + l16
         f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        if constexpr (!E4) {
 #pragma unroll
-        for (int s = 0; s < kD / 32; ++s) {
-            const int off = 128 * (s >> 1) + ((s & 1) ? kb1 : kb0);
-            const uint4 k0 = lds_b128(mytile + off), k1 = lds_b128(mytile + 16 * kD * 2 + off);
-            sacc[0] = mfma16x16x32(k0, qf[s], sacc[0]);
-            sacc[1] = mfma16x16x32(k1, qf[s], sacc[1]);
+            for (int s = 0; s < kD / 32; ++s) {
+                const int off = 128 * (s >> 1) + ((s & 1) ? kb1 : kb0);
+                const uint4 k0 = lds_b128(mytile + off), k1 = lds_b128(mytile + 16 * kD * 2 + off);
+                sacc[0] = mfma16x16x32(k0, qf[s], sacc[0]);
+                sacc[1] = mfma16x16x32(k1, qf[s], sacc[1]);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kD / 64; ++u) {
+                const uint4 r0 = lds_b128(mytile + kbe[0][u & 3] + 256 * (u >> 2));
+                const uint4 r1 = lds_b128(mytile + kbe[1][u & 3] + 256 * (u >> 2));
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint4 k0 = e4m3x8_to_bf16x8(h ? make_uint2(r0.z, r0.w) : make_uint2(r0.x, r0.y));
+                    const uint4 k1 = e4m3x8_to_bf16x8(h ? make_uint2(r1.z, r1.w) : make_uint2(r1.x, r1.y));
+                    sacc[0] = mfma16x16x32(k0, qf[2 * u + h], sacc[0]);
+                    sacc[1] = mfma16x16x32(k1, qf[2 * u + h], sacc[1]);
+                }
+            }
         }
-        float x[2][4], csc[2][4];
+        // scores (log2 domain; e4m3: + e of the column's scale s = mu * 2^e)
+        float x[2][4], cmu[2][4];
+        int cne[2][4];
         float mx = -INFINITY;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const float4 b4 = *(const float4 *)&meta[w][0][16 * c + 4 * g];
-            const float4 s4 = *(const float4 *)&meta[w][1][16 * c + 4 * g];
-            const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, ss[4] = {s4.x, s4.y, s4.z, s4.w};
+            const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+            float ss[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+            if constexpr (E4) {
+                const float4 s4 = *(const float4 *)&meta[w][1][16 * c + 4 * g];
+                ss[0] = s4.x; ss[1] = s4.y; ss[2] = s4.z; ss[3] = s4.w;
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float v = sacc[c][i] * sl2;
-                if constexpr (KV == 2) v *= ss[i];
-                csc[c][i] = ss[i];
+                if constexpr (E4) {
+                    const int ex = __builtin_amdgcn_frexp_expf(ss[i]);
+                    cmu[c][i] = __builtin_amdgcn_frexp_mantf(ss[i]);
+                    cne[c][i] = -ex;
+                    v = __builtin_fmaf(sacc[c][i], ss[i] * sl2, (float)ex);
+                }
                 x[c][i] = v + bb[i];
                 mx = fmaxf(mx, x[c][i]);
             }
@@ -250,7 +312,7 @@ void attn_dec_kernel(AttnParams p)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 pr[c][i] = fast_exp2(x[c][i] - msub);
-                psum += pr[c][i];
+                psum += E4 ? __builtin_amdgcn_ldexpf(pr[c][i], cne[c][i]) : pr[c][i];
             }
         l_run = l_run * alpha + psum;
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
@@ -258,23 +320,21 @@ void attn_dec_kernel(AttnParams p)
             for (int m = 0; m < kPM; ++m) acc[m] *= alpha;
         }
         // this wave's weights in the B-operand layout: element 4c + i of lane
-        // (g, l16) is column 16c + 4g + i (e4m3: times the row scale, as NP
-        // bf16 terms, each the rounding of what the previous ones left)
-        {
-            float r8[8];
+        // (g, l16) is column 16c + 4g + i (e4m3: mu exp2(x - m) = p * s as
+        // two f16 terms)
+        if constexpr (!E4) {
+            xp[0][w][lane] = make_uint4(pack_bf16x2(pr[0][0], pr[0][1]), pack_bf16x2(pr[0][2], pr[0][3]),
+                                        pack_bf16x2(pr[1][0], pr[1][1]), pack_bf16x2(pr[1][2], pr[1][3]));
+        } else {
+            uint32_t hi[4], lo[4];
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) r8[4 * c + i] = KV == 2 ? pr[c][i] * csc[c][i] : pr[c][i];
-#pragma unroll
-            for (int ep = 0; ep < NP; ++ep) {
-                xp[ep][w][lane] = make_uint4(pack_bf16x2(r8[0], r8[1]), pack_bf16x2(r8[2], r8[3]),
-                                             pack_bf16x2(r8[4], r8[5]), pack_bf16x2(r8[6], r8[7]));
-                if (ep + 1 < NP) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) r8[i] -= __uint_as_float(bf16_bits(r8[i]) << 16);
-                }
-            }
+                for (int h = 0; h < 2; ++h)
+                    split_f16x2(pr[c][2 * h] * cmu[c][2 * h], pr[c][2 * h + 1] * cmu[c][2 * h + 1], hi[2 * c + h],
+                                lo[2 * c + h]);
+            xp[0][w][lane] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            xp[1][w][lane] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         }
         __syncthreads();   // every wave's weights published
         // O^T[128w + 16m + 4g + i][head l16] += sum over the round's 128 columns
@@ -286,11 +346,17 @@ void attn_dec_kernel(AttnParams p)
             const uint8_t *bt = tiles[wb];
 #pragma unroll
             for (int m = 0; m < kPM; ++m) {
-                const uint2 v0 = lds_tr16(bt + vb[m & 3] + 128 * (m >> 2));
-                const uint2 v1 = lds_tr16(bt + vb[m & 3] + 16 * kD * 2 + 128 * (m >> 2));
-                const uint4 a = make_uint4(v0.x, v0.y, v1.x, v1.y);
-#pragma unroll
-                for (int ep = 0; ep < NP; ++ep) acc[m] = mfma16x16x32(a, pb[ep], acc[m]);
+                if constexpr (!E4) {
+                    const uint2 v0 = lds_tr16(bt + vb[m & 3] + 128 * (m >> 2));
+                    const uint2 v1 = lds_tr16(bt + vb[m & 3] + 16 * kD * 2 + 128 * (m >> 2));
+                    const uint4 a = make_uint4(v0.x, v0.y, v1.x, v1.y);
+                    acc[m] = mfma16x16x32(a, pb[0], acc[m]);
+                } else {
+                    const uint4 a = e4m3x8_to_f16x8(lds_tr8(bt + vrow + 16 * (vy ^ m)));
+                    const f16x8 av = __builtin_bit_cast(f16x8, a);
+                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, pb[0]), acc[m], 0, 0, 0);
+                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, pb[1]), acc[m], 0, 0, 0);
+                }
             }
         }
     }

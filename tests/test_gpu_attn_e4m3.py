@@ -151,3 +151,49 @@ def test_e4m3_bf16_output_and_determinism():
         h.add(hashlib.sha256(o.cpu().numpy().tobytes()).hexdigest())
     assert len(h) == 1
     assert sap.sparse_attn_num_splits(case.T, 64, 512, gidx.shape[1], 1) == 1
+
+
+# ------------------------------------------------- split-K decode, e4m3 rows
+
+@pytest.mark.parametrize("B", [1, 8])
+@pytest.mark.parametrize("ratio", [4, 128, 0])
+def test_e4m3_decode_splits(B, ratio):
+    """The decode kernel with e4m3 rows (raw codes gathered two rows per
+    DMA, K widened to bf16 in registers, V^T by ds_read_b64_tr_b8 widened to
+    f16, the weights as two f16 terms) over the automatic split count and
+    forced ones; the merge combines the splits' (max, sum) in the same
+    shifted log2 units."""
+    need_gpu()
+    case = W.decode_case(B=B, ratio=ratio, kv_dtype="e4m3", seed=W.SEED_BASE + 180 + 10 * B + ratio)
+    idx = oracle.case_idx(case)
+    ref = oracle.case_attn(case, idx=idx)
+    gidx = gpu_idx(case)
+    for splits in (0, 2, 5):
+        runs = sap.sparse_attn_num_splits(case.T, 64, 512, idx.shape[1], splits)
+        assert_attn_close(gpu_attn(case, idx=gidx, num_splits=splits), ref, f"e4m3 B{B} r{ratio} splits={splits} ({runs})")
+
+
+def test_e4m3_decode_holes_and_scales():
+    # unused columns (a token without any, window only, compressed only with
+    # a hole) and zero / negative scales, through the split-K decode path
+    need_gpu()
+    base = W.decode_case(B=4, pos=2000, ratio=4, topk=300, kv_dtype="e4m3", seed=W.SEED_BASE + 190)
+    g = torch.Generator().manual_seed(191)
+
+    def mix(s):
+        r = torch.rand(s.shape, generator=g)
+        s[r < 0.2] = 0.0
+        s[(r >= 0.2) & (r < 0.5)] *= -1.0
+        return s
+
+    case = _with_scales(base, mix, mix)
+    idx = oracle.case_idx(case)
+    idx[1, :] = -1
+    idx[2, case.n_win:] = -1
+    idx[3, :case.n_win] = -1
+    idx[3, case.n_win + 5:case.n_win + 40] = -1
+    ref = oracle.case_attn(case, idx=idx)
+    for splits in (0, 3):
+        out = gpu_attn(case, idx=dev(idx), num_splits=splits)
+        assert (out[1] == 0).all()
+        assert_attn_close(out, ref, f"e4m3 decode holes splits={splits}")
