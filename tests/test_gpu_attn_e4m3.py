@@ -173,6 +173,15 @@ def test_e4m3_decode_splits(B, ratio):
         assert_attn_close(gpu_attn(case, idx=gidx, num_splits=splits), ref, f"e4m3 B{B} r{ratio} splits={splits} ({runs})")
 
 
+@pytest.mark.parametrize("H", [20, 1])
+def test_e4m3_decode_head_counts(H):
+    # partial head groups through the split-K decode kernel (rows past H
+    # read a stand-in q row and write nothing)
+    need_gpu()
+    case = W.decode_case(B=2, pos=4000, ratio=4, H=H, kv_dtype="e4m3", seed=W.SEED_BASE + 195 + H)
+    assert_attn_close(gpu_attn(case), oracle.case_attn(case), f"e4m3 H={H} auto splits")
+
+
 def test_e4m3_decode_holes_and_scales():
     # unused columns (a token without any, window only, compressed only with
     # a hole) and zero / negative scales, through the split-K decode path

@@ -11,11 +11,12 @@ from gpu_helpers import dev, need_gpu, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_decode_step_graph_replays_match_eager(fused):
-    """fused: the selection runs as one top-k + index build launch."""
+@pytest.mark.parametrize("fused,kv", [(False, "bf16"), (True, "bf16"), (True, "e4m3")])
+def test_decode_step_graph_replays_match_eager(fused, kv):
+    """fused: the selection runs as one top-k + index build launch; kv: the
+    attention pools' row format (e4m3 with per-row scales)."""
     need_gpu()
-    c = W.decode_case(B=2, pos=4095, ratio=4, seed=W.SEED_BASE + 900)
+    c = W.decode_case(B=2, pos=4095, ratio=4, kv_dtype=kv, seed=W.SEED_BASE + 900)
     g = W.make_generator(W.SEED_BASE + 901)
     n_c = (4095 + 1 + 3) // 4
     keys = dev(W.fp4_key_rows(c.cmp_pool.shape[0], g))
@@ -29,6 +30,7 @@ def test_decode_step_graph_replays_match_eager(fused):
     ws = torch.empty(max(sap.sparse_attn_workspace_bytes(2, 64, 512, c.n_win + c.n_cmp, 0), 1),
                      dtype=torch.uint8, device="cuda")
     q, win, cmp = dev(c.q), dev(c.win_pool), dev(c.cmp_pool)
+    wsc, csc = dev(c.win_scale), dev(c.cmp_scale)
     pos, seq, win_pt, cmp_pt = dev(c.pos), dev(c.seq), dev(c.win_pt), dev(c.cmp_pt)
 
     def step():
@@ -38,7 +40,8 @@ def test_decode_step_graph_replays_match_eager(fused):
         else:
             sap.topk_select(logits, c.n_cmp, out=sel)
             sap.build_sparse_idx(pos, seq, c.n_win, win_pt, c.page, sel, cmp_pt, out=idx)
-        sap.sparse_attn_paged(q, win, cmp, idx, c.n_win, c.sm_scale, out=out, workspace=ws)
+        sap.sparse_attn_paged(q, win, cmp, idx, c.n_win, c.sm_scale, out=out, win_scale=wsc, cmp_scale=csc,
+                              workspace=ws)
 
     step()
     torch.cuda.synchronize()
