@@ -196,9 +196,12 @@ __device__ void find_bin(Shared &s, int rem, int k)
 // and_or_publish).  Passes start below the bits every candidate shares and
 // take 11 bits each, until the bin of the k-th key is taken whole.  The
 // histogram bins are cleared by the caller before the first pass (and by
-// find_bin after each).
+// find_bin after each).  With max_passes the select may stop early: then P
+// (under M) is the prefix of the bin that holds the k-th key, so keys whose
+// prefix is at least P include the k largest (a lower bound, not the cut).
 template <class ForEach>
-__device__ Sel radix_select(ForEach for_each, int k, uint32_t a, uint32_t o, Shared &s, bool nozero = false)
+__device__ Sel radix_select(ForEach for_each, int k, uint32_t a, uint32_t o, Shared &s, bool nozero = false,
+                           int max_passes = 32)
 {
     const int tid = threadIdx.x;
     const uint32_t diff = a ^ o;
@@ -234,7 +237,7 @@ __device__ Sel radix_select(ForEach for_each, int k, uint32_t a, uint32_t o, Sha
         rem -= m4.y;
         P |= (uint32_t)m4.x << lo;
         M |= dm << lo;
-        if (m4.z == rem || lo == 0) {
+        if (m4.z == rem || lo == 0 || --max_passes == 0) {
             ceq = m4.z;
             break;
         }
@@ -759,7 +762,10 @@ __global__ __launch_bounds__(kT) void topk_filter_kernel(TopkParams p, int nch)
         if (ns >= want) {
             uint32_t a, o;
             and_or_read(s, a, o);
-            tau = radix_select(for_each, want, a, o, s).P;   // low bits zero: key >= tau <=> prefix >= P
+            // one pass: the bin of the want-th sample key bounds the cut from
+            // below (the select launch is exact whatever tau admits, and
+            // falls back to a streamed select when fewer than k pass)
+            tau = radix_select(for_each, want, a, o, s, false, 1).P;   // low bits zero: key >= tau <=> prefix >= P
             if (tau == 0u) tau = 1u;
         }
     }
