@@ -71,9 +71,11 @@ template <int KV> struct RawRow;
 template <> struct RawRow<0> { using T = uint4; };   // 8 bf16
 template <> struct RawRow<2> { using T = uint2; };   // 8 e4m3 codes
 
-// NW = 4: one wave per SIMD (the roles below); NW = 8: two head groups of
-// four waves for S and the softmax, each wave holding half the Q operand and
-// half the O accumulators, so two waves share each SIMD (D >= 128).
+// NW = 4: one wave per SIMD (the roles below), the shape the launches use;
+// the code also covers NW = 8 (two head groups of four waves for S and the
+// softmax, each wave holding half the Q operand and half the O accumulators,
+// two waves per SIMD, D >= 128), which served head_dim 512 before the
+// dedicated one-pass and decode kernels of attn_d512.hip and attn_dec.hip.
 template <int D, int KV, int OUT, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void attn_kernel(AttnParams p)
@@ -845,7 +847,7 @@ __global__ __launch_bounds__(64 * WPB) void attn_merge_kernel(AttnParams p)
 template <int D, int KV, int OUT>
 hipError_t launch_attn_t(const AttnParams &p, hipStream_t s)
 {
-    constexpr int NW = attn_waves(D, KV);
+    constexpr int NW = kAttnWaves;
     const dim3 grid((unsigned)(p.T * p.num_splits), (unsigned)((p.H + kAttnHeadsPerBlock - 1) / kAttnHeadsPerBlock));
     hipLaunchKernelGGL((attn_kernel<D, KV, OUT, NW>), grid, dim3(64 * NW), 0, s, p);
     return hipGetLastError();
@@ -854,12 +856,15 @@ hipError_t launch_attn_t(const AttnParams &p, hipStream_t s)
 template <int D>
 hipError_t launch_attn_d(const AttnParams &p, int kv, int out, hipStream_t s)
 {
-    // bf16 rows at head_dim 512, one split per token (prefill): the
-    // one-barrier kernel of attn_d512.hip; split-K (decode) stays here, where
-    // eight waves share the q staging and partial stores of the few workgroups
-    if (D == 512 && p.num_splits == 1) return launch_attn_d512(p, kv, out, s);
-    if (kv == 0) return out == 1 ? launch_attn_t<D, 0, 1>(p, s) : launch_attn_t<D, 0, 0>(p, s);
-    return out == 1 ? launch_attn_t<D, 2, 1>(p, s) : launch_attn_t<D, 2, 0>(p, s);
+    // head_dim 512: one split per token runs the one-barrier kernel of
+    // attn_d512.hip; its split plans run attn_dec.hip (the plan never sends
+    // head_dim 512 splits here)
+    if constexpr (D == 512) {
+        return p.num_splits == 1 ? launch_attn_d512(p, kv, out, s) : hipErrorInvalidValue;
+    } else {
+        if (kv == 0) return out == 1 ? launch_attn_t<D, 0, 1>(p, s) : launch_attn_t<D, 0, 0>(p, s);
+        return out == 1 ? launch_attn_t<D, 2, 1>(p, s) : launch_attn_t<D, 2, 0>(p, s);
+    }
 }
 
 template <int D, int NW>
@@ -895,9 +900,11 @@ hipError_t launch_merge_t(const AttnParams &p, int out, hipStream_t s)
 }
 
 template <int D>
-hipError_t launch_merge_d(const AttnParams &p, int kv, int out, hipStream_t s)
+hipError_t launch_merge_d(const AttnParams &p, int, int out, hipStream_t s)
 {
-    return attn_waves(D, kv) == 8 ? launch_merge_t<D, 8>(p, out, s) : launch_merge_t<D, 4>(p, out, s);
+    // head_dim 512 splits are merged by attn_dec.hip's merge kernel
+    if constexpr (D == 512) return hipErrorInvalidValue;
+    else return launch_merge_t<D, kAttnWaves>(p, out, s);
 }
 
 }  // namespace

@@ -49,10 +49,9 @@ hipError_t launch_attn_d512(const AttnParams &p, int kv, int out_dtype, hipStrea
 // split-K decode at head_dim 512 (attn_dec.hip) and its merge
 hipError_t launch_attn_dec(const AttnParams &p, int kv, int out_dtype, hipStream_t s);
 hipError_t launch_attn_dec_merge(const AttnParams &p, int out_dtype, hipStream_t s);
-// waves per workgroup of the split-K attention kernel, whose layout the split
-// partials follow: 8 (two head groups, two waves per SIMD) at head_dim 512,
-// else 4
-constexpr int attn_waves(int D, int kv) { return D == 512 ? 8 : 4; }
+// waves per workgroup of the tiled attention kernel (head_dims below 512),
+// whose layout its split partials follow
+constexpr int kAttnWaves = 4;
 
 struct IndexerParams {
     const uint16_t *q;               // bf16 [B, Hi, 128]
