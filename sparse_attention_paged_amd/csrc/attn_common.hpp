@@ -58,6 +58,17 @@ __device__ __forceinline__ void split_f16x2(float a, float b, uint32_t &hi, uint
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
+// a, b -> an f16 pair (round to nearest, a in bits 0-15)
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), f16x2));
+}
+// the f16 in bits 0-15 / 16-31 of a word, widened (exactly)
+__device__ __forceinline__ float f16_lo(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu)); }
+__device__ __forceinline__ float f16_hi(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16)); }
+
 // max over the four lanes l, l^16, l^32, l^48 with the gfx950 row-swap
 // permutes (VALU, no LDS round trip)
 __device__ __forceinline__ float group4_max(float x)

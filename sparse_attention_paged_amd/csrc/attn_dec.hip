@@ -13,8 +13,8 @@
 // workgroups, and what they write for the merge should not outweigh the rows
 // they read.  One workgroup = 4 waves = 16 heads of one token over a range of
 // its columns taken in rounds of 128 (32 per wave); a split's partial output
-// is then 16 heads x 512 fp32 = 32 KiB, the size of 32 rows, for the 128
-// rows (and more) it summarises:
+// is then 16 heads x 512 f16 = 16 KiB (bf16 rows; e4m3 rows: fp32, 32 KiB),
+// the size of 16 (32) rows, for the 128 rows (and more) it summarises:
 //  - gather: wave w moves its 32 rows from HBM straight into its own LDS tile
 //    (global_load_lds_dwordx4: one 1 KiB row per wave instruction, 16-byte
 //    loads; e4m3 rows: the raw codes, two 512-byte rows per instruction);
@@ -37,7 +37,8 @@
 // enter PV as two f16 terms; the sums take p = 2^-e exp2(x + e - m).
 // One split per token stores the normalised output; several splits store
 // (unnormalised O, running max, sum) and attn_dec_merge_kernel combines them
-// in split order.  All workgroups of one token -- its splits and head groups
+// in split order; for bf16 rows O is stored in f16, each head's three values
+// scaled by one power of two so that its O fits f16.  All workgroups of one token -- its splits and head groups
 // -- are placed on one XCD, so a gathered row and the q rows come from HBM
 // once and the other head groups find them in that XCD's L2.
 #include "common.hpp"
@@ -110,6 +111,7 @@ void attn_dec_kernel(AttnParams p)
     __shared__ __attribute__((aligned(16))) float meta[kWv][2][kCW]; // per column: bias (0 / -inf), scale
     __shared__ float xm[kWv][kDecHeads];                            // tile maxima
     __shared__ float xl[kWv][kDecHeads];                            // softmax sums
+    __shared__ float xa[kWv][kDecHeads];                            // largest |O| per head_dim quarter
 
     const int G = p.hgroups;
     const DecSlot sl = dec_slot((int)blockIdx.x, G, p.num_splits, p.T);
@@ -366,6 +368,16 @@ void attn_dec_kernel(AttnParams p)
         const float ls = group4_sum(l_run);
         if (g == 0) xl[w][l16] = ls;
     }
+    if (!E4 && p.num_splits > 1) {
+        // a split's partial goes out in f16 scaled by a power of two: the
+        // largest |O| of each head (over the waves' head_dim quarters)
+        float mx = 0.0f;
+#pragma unroll
+        for (int m = 0; m < kPM; ++m)
+            mx = fmaxf(fmaxf(mx, fmaxf(fabsf(acc[m][0]), fabsf(acc[m][1]))), fmaxf(fabsf(acc[m][2]), fabsf(acc[m][3])));
+        mx = group4_max(mx);
+        if (g == 0) xa[w][l16] = mx;
+    }
     __syncthreads();
     const float l_tot = (xl[0][l16] + xl[1][l16]) + (xl[2][l16] + xl[3][l16]);
     const int head = hbase + l16;
@@ -388,10 +400,33 @@ void attn_dec_kernel(AttnParams p)
                 *(uint2 *)(o + 16 * m) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
             }
         }
+    } else if constexpr (!E4) {
+        // bf16 rows: partial outputs in f16, in the accumulators' own layout
+        // [unit][head group][w][m][lane] x 4 halves (each store instruction
+        // writes 512 consecutive bytes).  The head's O and sum are scaled by
+        // 2^sh and its max lowered by sh, which leaves every merge weight
+        // 2^(m - M) O and 2^(m - M) l unchanged: sh puts the largest |O| in
+        // [2^14, 2^15) (f16 keeps 11 significant bits of it, normal down to
+        // 2^-28 of it) unless the scaled sum would pass 2^120 or sh would
+        // pass 100 (O that small is below anything its f16 terms could
+        // matter for).  The f16 rounding, 2^-12 of the head's largest |O|,
+        // is below that of the bf16 weights (2^-9 of each).
+        const float mx = fmaxf(fmaxf(xa[0][l16], xa[1][l16]), fmaxf(xa[2][l16], xa[3][l16]));
+        const int sh = min(min(15 - __builtin_amdgcn_frexp_expf(mx), 120 - __builtin_amdgcn_frexp_expf(l_tot)), 100);
+        const int64_t pb = ((int64_t)sl.u * G + sl.g) * kWv + w;
+        uint16_t *po = (uint16_t *)p.part_o;
+#pragma unroll
+        for (int m = 0; m < kPM; ++m)
+            *(uint2 *)(po + ((pb * kPM + m) * 64 + lane) * 4) =
+                make_uint2(pack_f16x2(__builtin_amdgcn_ldexpf(acc[m][0], sh), __builtin_amdgcn_ldexpf(acc[m][1], sh)),
+                           pack_f16x2(__builtin_amdgcn_ldexpf(acc[m][2], sh), __builtin_amdgcn_ldexpf(acc[m][3], sh)));
+        if (w == 0 && g == 0)
+            *(float2 *)(p.part_ml + ((int64_t)sl.u * p.H + head) * 2) =
+                make_float2(m_run - (float)sh, __builtin_amdgcn_ldexpf(l_tot, sh));
     } else {
-        // partial outputs in the accumulators' own layout
-        // [unit][head group][w][m][lane] x 4 floats: each store instruction
-        // writes 1 KiB of consecutive bytes
+        // e4m3 rows: partial outputs in fp32 (their values reach 448 times
+        // the largest scale, where f16's 11 bits would not meet an absolute
+        // bound), same layout with 4 floats per lane (1 KiB per store)
         const int64_t pb = ((int64_t)sl.u * G + sl.g) * kWv + w;
 #pragma unroll
         for (int m = 0; m < kPM; ++m)
@@ -404,9 +439,10 @@ void attn_dec_kernel(AttnParams p)
 // out[t, h, :] = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j over the splits
 // j in order; zero when every split was empty.  One wave takes one (token,
 // head group, w, m) group of the partial layout: lane l owns head 16g + l%16
-// and head_dim 128w + 16m + 4(l/16) .. +3, so its partial loads are 1 KiB
-// contiguous per split; the loads of U splits go out before any is used.
-template <int OUT, int U, int WPB>   // WPB waves per workgroup
+// and head_dim 128w + 16m + 4(l/16) .. +3, so its partial loads are 512
+// bytes (f16) or 1 KiB (fp32) contiguous per split; the loads of U splits go
+// out before any is used.
+template <int OUT, int U, int WPB, bool H16>   // WPB waves per workgroup; H16: f16 partials (bf16 rows)
 __global__ __launch_bounds__(64 * WPB) void attn_dec_merge_kernel(AttnParams p, int nb)
 {
     // block b -> (token t, block y of the token's nb): token t on XCD t % 8,
@@ -422,8 +458,8 @@ __global__ __launch_bounds__(64 * WPB) void attn_dec_merge_kernel(AttnParams p, 
     if (head >= p.H) return;
     const int d = 128 * w + 16 * m + 4 * (lane >> 4);
     const int S = p.num_splits;
-    const int64_t pstride = (int64_t)G * kWv * kPM * 64;   // float4 slots per unit
-    const float4 *po = (const float4 *)p.part_o + ((int64_t)t * S) * pstride + (int64_t)grp * 64 + lane;
+    const int64_t pstride = (int64_t)G * kWv * kPM * 64;   // 4-value slots per unit
+    const int64_t po0 = ((int64_t)t * S) * pstride + (int64_t)grp * 64 + lane;
     const float2 *pml = (const float2 *)p.part_ml + ((int64_t)t * S) * p.H + head;
     float M = -INFINITY, L = 0.0f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -434,7 +470,12 @@ __global__ __launch_bounds__(64 * WPB) void attn_dec_merge_kernel(AttnParams p, 
         for (int u = 0; u < U; ++u) {
             const int js = min(j0 + u, S - 1);
             ml[u] = pml[(int64_t)js * p.H];
-            v[u] = po[(int64_t)js * pstride];
+            if constexpr (H16) {
+                const uint2 h = ((const uint2 *)p.part_o)[po0 + (int64_t)js * pstride];
+                v[u] = make_float4(f16_lo(h.x), f16_hi(h.x), f16_lo(h.y), f16_hi(h.y));
+            } else {
+                v[u] = ((const float4 *)p.part_o)[po0 + (int64_t)js * pstride];
+            }
         }
         float Mb = M;
 #pragma unroll
@@ -471,7 +512,7 @@ hipError_t launch_dec_t(const AttnParams &p, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int OUT>
+template <int OUT, bool H16>
 hipError_t launch_dec_merge_t(const AttnParams &p, hipStream_t s)
 {
     const int groups = p.hgroups * kWv * kPM;
@@ -482,8 +523,8 @@ hipError_t launch_dec_merge_t(const AttnParams &p, hipStream_t s)
     const dim3 grid((unsigned)(8 * (int64_t)nb * ((p.T + 7) / 8)));
     auto go = [&](auto u_tag) {
         constexpr int U = decltype(u_tag)::value;
-        if (one) hipLaunchKernelGGL((attn_dec_merge_kernel<OUT, U, 1>), grid, dim3(64), 0, s, p, nb);
-        else hipLaunchKernelGGL((attn_dec_merge_kernel<OUT, U, 4>), grid, dim3(256), 0, s, p, nb);
+        if (one) hipLaunchKernelGGL((attn_dec_merge_kernel<OUT, U, 1, H16>), grid, dim3(64), 0, s, p, nb);
+        else hipLaunchKernelGGL((attn_dec_merge_kernel<OUT, U, 4, H16>), grid, dim3(256), 0, s, p, nb);
     };
     const int S = p.num_splits;
     if (S <= 2) go(std::integral_constant<int, 2>{});
@@ -501,9 +542,10 @@ hipError_t launch_attn_dec(const AttnParams &p, int kv, int out, hipStream_t s)
     return out == 1 ? launch_dec_t<2, 1>(p, s) : launch_dec_t<2, 0>(p, s);
 }
 
-hipError_t launch_attn_dec_merge(const AttnParams &p, int out, hipStream_t s)
+hipError_t launch_attn_dec_merge(const AttnParams &p, int kv, int out, hipStream_t s)
 {
-    return out == 1 ? launch_dec_merge_t<1>(p, s) : launch_dec_merge_t<0>(p, s);
+    if (kv == 0) return out == 1 ? launch_dec_merge_t<1, true>(p, s) : launch_dec_merge_t<0, true>(p, s);
+    return out == 1 ? launch_dec_merge_t<1, false>(p, s) : launch_dec_merge_t<0, false>(p, s);
 }
 
 }  // namespace sap

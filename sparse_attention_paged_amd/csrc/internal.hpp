@@ -26,7 +26,7 @@ struct AttnParams {
     int T, H;
     float sm_scale_log2;             // sm_scale * log2(e)
     int num_splits, cols_per_split;  // cols_per_split: multiple of kAttnTile (decode kernel: of kDecRound)
-    float *part_o;                   // [T, S, H, D] unnormalised partial outputs
+    float *part_o;                   // [T, S, H, D] unnormalised partial outputs (decode kernel: its own layout, f16 for bf16 rows)
     float *part_ml;                  // [T, S, H, 2] running max (log2 domain), sum
     int hgroups;                     // decode kernel: head groups of kDecHeads
 };
@@ -48,7 +48,7 @@ hipError_t launch_attn_merge(const AttnParams &p, int D, int kv, int out_dtype, 
 hipError_t launch_attn_d512(const AttnParams &p, int kv, int out_dtype, hipStream_t s);
 // split-K decode at head_dim 512 (attn_dec.hip) and its merge
 hipError_t launch_attn_dec(const AttnParams &p, int kv, int out_dtype, hipStream_t s);
-hipError_t launch_attn_dec_merge(const AttnParams &p, int out_dtype, hipStream_t s);
+hipError_t launch_attn_dec_merge(const AttnParams &p, int kv, int out_dtype, hipStream_t s);
 // waves per workgroup of the tiled attention kernel (head_dims below 512),
 // whose layout its split partials follow
 constexpr int kAttnWaves = 4;

@@ -304,7 +304,7 @@ int attn_call(const void *q, sap_dtype q_dtype, int64_t q_stride_t, int64_t q_st
     hipError_t e;
     if (sp.kind == PLAN_DEC) {
         e = sap::launch_attn_dec(p, kv, od, (hipStream_t)stream);
-        if (e == hipSuccess && sp.splits > 1) e = sap::launch_attn_dec_merge(p, od, (hipStream_t)stream);
+        if (e == hipSuccess && sp.splits > 1) e = sap::launch_attn_dec_merge(p, kv, od, (hipStream_t)stream);
     } else {
         e = sap::launch_attn(p, D, kv, od, (hipStream_t)stream);
         if (e == hipSuccess && sp.splits > 1) e = sap::launch_attn_merge(p, D, kv, od, (hipStream_t)stream);
