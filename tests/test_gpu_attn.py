@@ -10,6 +10,7 @@ and 50, top-k widths that are not tile multiples, zero counts, the ratio-0
 alias and pool views with a row offset).  The fp8 case follows 'Perf/kv fp8
 read path' (What this changes).
 """
+import dataclasses
 import hashlib
 import math
 
@@ -356,3 +357,30 @@ def test_decode_merge_batches(B):
         say(f"  B{B} {idx.shape[1]} columns: {splits} splits requested, {runs} run")
         out = gpu_attn(case, idx=gidx, num_splits=splits)
         assert_attn_close(out, ref, f"B{B} splits={splits} (runs {runs})")
+
+
+@pytest.mark.parametrize("k", [60, -60])
+def test_decode_f16_partials_row_magnitudes(k):
+    """bf16 rows: a split's partial O is stored in f16 after one power-of-two
+    shift per head that brings its largest |O| to [2^14, 2^15), and the
+    head's max is lowered by the shift.  Rows scaled by 2^k with q scaled by
+    2^-k keep every score and scale every O by 2^k: against the oracle the
+    bar scales with the rows, and the output is 2^k times the unscaled one
+    up to the rounding of the shifted maxima in fp32 (a few ulps of the
+    log2 max, far below the bar)."""
+    need_gpu()
+    case = W.decode_case(B=2, pos=4000, ratio=4, seed=W.SEED_BASE + 140)
+    f = 2.0 ** k
+    sc = dataclasses.replace(case, q=(case.q.float() / f).to(torch.bfloat16),
+                             win_pool=(case.win_pool.float() * f).to(torch.bfloat16),
+                             cmp_pool=(case.cmp_pool.float() * f).to(torch.bfloat16))
+    gidx = gpu_idx(case)
+    assert sap.sparse_attn_num_splits(case.T, 64, 512, gidx.shape[1], 5) == 5
+    base = gpu_attn(case, idx=gidx, num_splits=5)
+    out = gpu_attn(sc, idx=gidx, num_splits=5)
+    assert torch.isfinite(out).all()
+    rel = ((out / f - base).abs().max() / base.abs().max()).item()
+    say(f"  rows x 2^{k}: largest deviation from 2^{k} x the unscaled output {rel:.2e} of max|out|")
+    assert rel <= 1e-5, rel
+    ref = oracle.case_attn(sc)
+    assert_attn_close(out / f, ref / f, f"rows x 2^{k}, 5 splits")
