@@ -118,7 +118,10 @@ int sap_build_sparse_idx(const int32_t *pos, const int32_t *seq, int T, int n_wi
  *           merge is exact algebra, but each split rounds its softmax weights
  *           to bf16 against its own running max, so split counts agree with
  *           the single pass to the same tolerance as with an exact result,
- *           not bit for bit.
+ *           not bit for bit.  (At head_dim 512 with bf16 rows a split's
+ *           partial output is kept in f16, scaled per head by a power of two
+ *           so that its largest value sits in [2^14, 2^15): a rounding of at
+ *           most 2^-12 of that value, below the bf16 weights' 2^-9.)
  * workspace: device scratch of at least sap_sparse_attn_workspace_bytes(T,
  *           H, D, n_win + n_cmp, num_splits) bytes, 256-byte aligned; may be
  *           NULL when that size is 0.
