@@ -121,7 +121,7 @@ int sap_build_sparse_idx(const int32_t *pos, const int32_t *seq, int T, int n_wi
  *           not bit for bit.  (At head_dim 512 with bf16 rows a split's
  *           partial output is kept in f16, scaled per head by a power of two
  *           so that its largest value sits in [2^14, 2^15): a rounding of at
- *           most 2^-12 of that value, below the bf16 weights' 2^-9.)
+ *           most 2^-11 of that value, below the bf16 weights' 2^-9.)
  * workspace: device scratch of at least sap_sparse_attn_workspace_bytes(T,
  *           H, D, n_win + n_cmp, num_splits) bytes, 256-byte aligned; may be
  *           NULL when that size is 0.

@@ -38,9 +38,10 @@
 // One split per token stores the normalised output; several splits store
 // (unnormalised O, running max, sum) and attn_dec_merge_kernel combines them
 // in split order; for bf16 rows O is stored in f16, each head's three values
-// scaled by one power of two so that its O fits f16.  All workgroups of one token -- its splits and head groups
-// -- are placed on one XCD, so a gathered row and the q rows come from HBM
-// once and the other head groups find them in that XCD's L2.
+// scaled by one power of two so that its O fits f16.  All workgroups of one
+// token -- its splits and head groups -- are placed on one XCD, so a
+// gathered row and the q rows come from HBM once and the other head groups
+// find them in that XCD's L2.
 #include "common.hpp"
 #include "formats.hpp"
 #include "internal.hpp"
@@ -409,8 +410,9 @@ void attn_dec_kernel(AttnParams p)
         // [2^14, 2^15) (f16 keeps 11 significant bits of it, normal down to
         // 2^-28 of it) unless the scaled sum would pass 2^120 or sh would
         // pass 100 (O that small is below anything its f16 terms could
-        // matter for).  The f16 rounding, 2^-12 of the head's largest |O|,
-        // is below that of the bf16 weights (2^-9 of each).
+        // matter for).  The f16 rounding, at most 8 in those units (2^-11 of
+        // the head's largest |O|), is below that of the bf16 weights (2^-9
+        // of each).
         const float mx = fmaxf(fmaxf(xa[0][l16], xa[1][l16]), fmaxf(xa[2][l16], xa[3][l16]));
         const int sh = min(min(15 - __builtin_amdgcn_frexp_expf(mx), 120 - __builtin_amdgcn_frexp_expf(l_tot)), 100);
         const int64_t pb = ((int64_t)sl.u * G + sl.g) * kWv + w;
